@@ -1,0 +1,230 @@
+"""numpy float64 oracle of paged softmax attention (test infrastructure only).
+
+The method computes exact softmax attention; the kernels on the pages only
+change where the keys come from (pages reached through a block table) and in
+what order partial sums are formed.  So this oracle is the definition written
+out in float64:
+
+  for sequence b with L = seq_lens[b] keys and Q = cu_seqlens_q[b+1] -
+  cu_seqlens_q[b] query tokens, query token i (0 <= i < Q) of query head h
+  attends to keys j < n_i = L - Q + i + 1 of kv head h // (Hq / Hkv)
+  (bottom-right causal alignment: InferMatrixLab/vllm-rlt PR #128, "Purpose",
+  Prefill; the chunk sits at the end of the context as in 1CatAI/1Cat-vLLM
+  PR #1279, commit 1 and its kernel microbenchmarks).  Key j of sequence b
+  lives at page block_tables[b, j // P], slot j % P.
+  s_j = scale * <q, K_j>;  m = max_j s_j;  w_j = exp(s_j - m);
+  o = sum_j w_j V_j / sum_j w_j;  lse = m + log(sum_j w_j)  (natural log).
+  A row with n_i <= 0 has no visible key: o = 0 and lse = -inf (the zero
+  output for empty rows of PR #128, "Test Plan").
+
+Split-KV (PR #128, "Purpose", Decode): the context of a row is cut into
+S equal parts aligned to a tile of T keys, a function of the row's own length
+only; every part yields an FP32 partial state (o_s normalised, lse_s) and a
+second pass merges them by log-sum-exp.  The exact tile is not stated; the
+reading used here is T = 32 and per = ceil(ceil(L/T)/S) tiles per part, part s
+covering keys [s*per*T, min((s+1)*per*T, L)).
+
+Rows are processed in blocks so that no score matrix of a long context exists
+whole in memory.  Everything is float64; inputs are upcast exactly.
+"""
+
+import numpy as np
+
+from .fp8 import e5m2_to_float64
+
+# Decode split tile (keys); see the module docstring for the reading.
+SPLIT_TILE = 32
+
+
+def dequantize_pool(pool, kind, scale=1.0):
+    """Exact float64 values of a KV page pool.
+
+    ``kind`` is 'float' for any IEEE float storage (fp32, fp16, or bf16 already
+    widened by the caller) or 'e5m2' for a uint8 array of fp8_e5m2 bytes, whose
+    values are decode(byte) * scale (per-tensor scale; 1CatAI/1Cat-vLLM PR #616,
+    fp8_e5m2 KV paragraph of "Test Result").
+    """
+    if kind == "float":
+        return np.asarray(pool, dtype=np.float64)
+    if kind == "e5m2":
+        return e5m2_to_float64(np.asarray(pool)) * float(scale)
+    raise ValueError(f"unknown pool kind {kind!r}")
+
+
+def gather_dense_kv(pool, block_table_row, seq_len, kv_head):
+    """Dense [seq_len, D] keys (or values) of one sequence and one kv head.
+
+    ``pool`` is [num_pages, page_size, Hkv, D]; key j is read from page
+    block_table_row[j // page_size], slot j % page_size.  Only the first
+    ceil(seq_len / page_size) table entries are read.
+    """
+    page_size = pool.shape[1]
+    j = np.arange(int(seq_len))
+    pages = np.asarray(block_table_row, dtype=np.int64)[j // page_size]
+    return np.asarray(pool[pages, j % page_size, kv_head, :], dtype=np.float64)
+
+
+def visible_key_count(seq_len, q_len, i):
+    """n_i = L - Q + i + 1: keys visible to query token i under bottom-right alignment."""
+    return seq_len - q_len + i + 1
+
+
+def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128):
+    """Softmax attention of query rows over a key range.
+
+    Row r attends to keys j with key_lo <= j < min(counts[r], key_hi, len(K)).
+    Returns (o [n, D], lse [n]); a row with no key in range gets o = 0 and
+    lse = -inf.
+    """
+    qrows = np.asarray(qrows, dtype=np.float64)
+    counts = np.asarray(counts, dtype=np.int64)
+    n, D = qrows.shape
+    L = K.shape[0]
+    hi = L if key_hi is None else min(int(key_hi), L)
+    o = np.zeros((n, D), dtype=np.float64)
+    lse = np.full(n, -np.inf, dtype=np.float64)
+    for r0 in range(0, n, block):
+        qb = qrows[r0:r0 + block]
+        end = np.minimum(counts[r0:r0 + block], hi)
+        emax = int(end.max()) if end.size else 0
+        if emax <= key_lo:
+            continue
+        Kb = K[key_lo:emax]
+        Vb = V[key_lo:emax]
+        s = scale * (qb @ Kb.T)
+        j = np.arange(key_lo, emax)
+        vis = j[None, :] < end[:, None]
+        s = np.where(vis, s, -np.inf)
+        m = s.max(axis=1)
+        has = np.isfinite(m)
+        w = np.where(vis, np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
+        den = w.sum(axis=1)
+        ob = (w @ Vb) / np.where(has, den, 1.0)[:, None]
+        o[r0:r0 + block] = np.where(has[:, None], ob, 0.0)
+        with np.errstate(divide="ignore"):
+            lse[r0:r0 + block] = np.where(has, m + np.log(np.where(has, den, 1.0)), -np.inf)
+    return o, lse
+
+
+def _token_to_seq(cu):
+    total = int(cu[-1])
+    return np.searchsorted(cu, np.arange(total), side="right") - 1
+
+
+def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, rows=None):
+    """Varlen paged attention in float64.
+
+    q            [total_q, Hq, D]
+    k_pool/v_pool [num_pages, page_size, Hkv, D] (float64 values; see dequantize_pool)
+    cu_seqlens_q [B + 1], seq_lens [B], block_tables [B, max_pages]
+    rows         optional [n, 2] array of (token, q head) pairs to compute.
+
+    Returns (out [total_q, Hq, D], lse [total_q, Hq]) or, with ``rows``,
+    (out [n, D], lse [n]) in the order given.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total_q, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bt = np.asarray(block_tables)
+    if cu[-1] != total_q:
+        raise ValueError("cu_seqlens_q[-1] must equal total_q")
+
+    if rows is None:
+        out = np.zeros((total_q, Hq, D))
+        lse = np.full((total_q, Hq), -np.inf)
+        want = None
+    else:
+        want = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+        out = np.zeros((len(want), D))
+        lse = np.full(len(want), -np.inf)
+        seq_of = _token_to_seq(cu)[want[:, 0]]
+
+    for b in range(len(L)):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        Qb, Lb = t1 - t0, int(L[b])
+        if Qb == 0:
+            continue
+        for h in range(Hkv):
+            heads = range(h * g, (h + 1) * g)
+            if want is not None:
+                sel = np.nonzero((seq_of == b) & (want[:, 1] // g == h))[0]
+                if sel.size == 0:
+                    continue
+            K = gather_dense_kv(k_pool, bt[b], Lb, h)
+            V = gather_dense_kv(v_pool, bt[b], Lb, h)
+            if want is None:
+                i = np.arange(Qb)
+                counts = visible_key_count(Lb, Qb, i)
+                for qh in heads:
+                    o, s = attention_rows(q[t0:t1, qh, :], K, V, counts, scale)
+                    out[t0:t1, qh, :] = o
+                    lse[t0:t1, qh] = s
+            else:
+                toks = want[sel, 0]
+                qrows = q[toks, want[sel, 1], :]
+                counts = visible_key_count(Lb, Qb, toks - t0)
+                o, s = attention_rows(qrows, K, V, counts, scale)
+                out[sel] = o
+                lse[sel] = s
+    return out, lse
+
+
+def split_ranges(seq_len, num_splits, tile=SPLIT_TILE):
+    """Key ranges of the S tile-aligned parts of a row of length seq_len."""
+    L = int(seq_len)
+    tiles = -(-L // tile)
+    per = -(-tiles // num_splits)
+    return [(min(s * per * tile, L), min((s + 1) * per * tile, L)) for s in range(num_splits)]
+
+
+def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE):
+    """Per-part partial states of rows over one sequence: (o_s [S, n, D], lse_s [S, n])."""
+    ranges = split_ranges(K.shape[0], num_splits, tile)
+    os_, ls_ = [], []
+    for lo, hi in ranges:
+        o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi)
+        os_.append(o)
+        ls_.append(s)
+    return np.stack(os_), np.stack(ls_)
+
+
+def merge_partials(o_s, lse_s):
+    """Log-sum-exp merge over axis 0 of partial states (o_s normalised per part).
+
+    M = max_s lse_s; w_s = exp(lse_s - M); o = sum_s w_s o_s / sum_s w_s;
+    lse = M + log sum_s w_s.  All parts empty: o = 0, lse = -inf.
+    """
+    o_s = np.asarray(o_s, dtype=np.float64)
+    lse_s = np.asarray(lse_s, dtype=np.float64)
+    M = lse_s.max(axis=0)
+    has = np.isfinite(M)
+    w = np.exp(lse_s - np.where(has, M, 0.0))
+    den = w.sum(axis=0)
+    o = (w[..., None] * o_s).sum(axis=0) / np.where(has, den, 1.0)[..., None]
+    o = np.where(has[..., None], o, 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(has, M + np.log(np.where(has, den, 1.0)), -np.inf)
+    return o, lse
+
+
+def attended_pairs(cu_seqlens_q, seq_lens):
+    """Sum over query tokens of their visible key count (per query head)."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    total = 0
+    for b in range(len(L)):
+        Qb = int(cu[b + 1] - cu[b])
+        for i in range(Qb):
+            total += max(0, int(L[b]) - Qb + i + 1)
+    return total
+
+
+def attention_flops(cu_seqlens_q, seq_lens, num_q_heads, head_dim):
+    """Causal-exact work: 2*D multiply-adds for QK^T and 2*D for PV per attended pair and head."""
+    return 4 * head_dim * num_q_heads * attended_pairs(cu_seqlens_q, seq_lens)
+

@@ -1,0 +1,368 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+* brute force: a pure-Python triple loop (oracle/brute.py) on tiny inputs;
+* closed forms: zero query / zero scale -> uniform weights, constant V,
+  a single visible key, two visible keys (logistic weights), empty rows;
+* a library routine: torch float64 scaled_dot_product_attention with a causal
+  mask equals a whole-sequence prefill on an identity block table, and a chunk
+  equals the last rows of the whole-sequence attention (bottom-right alignment);
+* invariants: page permutation, page size, GQA == MHA with repeated kv heads,
+  verify row (q = K+1) == K+1 decode rows, split + merge == unsplit;
+* the E5M2 decoder against torch's float8_e5m2 for all 256 bytes;
+* planted mistakes in the oracle are caught by at least one of the pins above.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oa
+from paged_attention_prefill_amd import inputs as gen
+
+
+def assert_same(a, b):
+    """Equal up to the rounding of a different BLAS blocking (row counts differ)."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert (np.isfinite(a) == np.isfinite(b)).all()
+    fin = np.isfinite(a)
+    np.testing.assert_allclose(a[fin], b[fin], rtol=0, atol=1e-14)
+    assert (a[~fin] == b[~fin]).all()
+
+
+def run_oracle(case, rows=None):
+    kvk = "e5m2" if case.kv_kind == "e5m2" else "float"
+    k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kvk, case.k_scale)
+    v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kvk, case.v_scale)
+    return oracle.paged_attention(gen.to_numpy64(case.q), k, v, case.cu_seqlens_q,
+                                  case.seq_lens, case.block_tables, case.scale, rows=rows)
+
+
+def brute(case):
+    q = gen.to_numpy64(case.q).tolist()
+    k = gen.to_numpy64(case.k_pool).tolist()
+    v = gen.to_numpy64(case.v_pool).tolist()
+    o, l = oracle.brute_paged_attention(q, k, v, case.cu_seqlens_q.tolist(), case.seq_lens.tolist(),
+                                        case.block_tables.tolist(), case.scale)
+    return np.array(o), np.array(l)
+
+
+def small_gqa_case(seed=11, **kw):
+    args = dict(q_lens=[5, 1, 3, 4], seq_lens=[9, 7, 2, 20], num_q_heads=6, num_kv_heads=2,
+                head_dim=16, page_size=4, q_kind="f32", seed=seed)
+    args.update(kw)
+    return gen.make_case("small_gqa", **args)
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("maker", [lambda: gen.tiny_fp32(), lambda: small_gqa_case()])
+def test_numpy_oracle_matches_brute_force(maker):
+    case = maker()
+    o, l = run_oracle(case)
+    bo, bl = brute(case)
+    assert np.isfinite(o).all()
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert (fin == np.isfinite(l)).all()
+    np.testing.assert_allclose(l[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_equal_full_output():
+    case = small_gqa_case(seed=12)
+    o, l = run_oracle(case)
+    rows = np.array([[0, 5], [4, 0], [5, 3], [12, 1], [8, 2]])
+    so, sl = run_oracle(case, rows=rows)
+    # same arithmetic, possibly another BLAS blocking: equal up to rounding
+    np.testing.assert_allclose(so, o[rows[:, 0], rows[:, 1]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(sl, l[rows[:, 0], rows[:, 1]], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def _dense_v(case, b, kvh):
+    v = gen.to_numpy64(case.v_pool)
+    return oracle.gather_dense_kv(v, case.block_tables[b], int(case.seq_lens[b]), kvh)
+
+
+def test_zero_query_gives_uniform_mean():
+    case = small_gqa_case(seed=13)
+    case.q.zero_()
+    o, l = run_oracle(case)
+    g = case.num_q_heads // case.num_kv_heads
+    for b in range(case.num_seqs):
+        t0, t1 = case.cu_seqlens_q[b], case.cu_seqlens_q[b + 1]
+        Q, L = t1 - t0, int(case.seq_lens[b])
+        for i in range(Q):
+            n = L - Q + i + 1
+            for h in range(case.num_q_heads):
+                if n <= 0:
+                    assert not o[t0 + i, h].any() and l[t0 + i, h] == -np.inf
+                    continue
+                V = _dense_v(case, b, h // g)
+                np.testing.assert_allclose(o[t0 + i, h], V[:n].mean(0), atol=1e-14)
+                assert abs(l[t0 + i, h] - math.log(n)) < 1e-14
+
+
+def test_zero_scale_gives_uniform_mean():
+    a = small_gqa_case(seed=14)
+    a.scale = 0.0
+    o, l = run_oracle(a)
+    b2 = small_gqa_case(seed=14)
+    b2.q.zero_()
+    o2, l2 = run_oracle(b2)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    np.testing.assert_allclose(l[np.isfinite(l)], l2[np.isfinite(l2)], atol=1e-14)
+
+
+def test_constant_values_pass_through():
+    case = small_gqa_case(seed=15)
+    c = torch.linspace(-3, 3, case.head_dim)
+    case.v_pool[:] = c  # every slot of every page, poison included
+    o, _ = run_oracle(case)
+    vis = np.abs(o).sum(-1) > 0
+    np.testing.assert_allclose(o[vis], np.broadcast_to(c.double().numpy(), o[vis].shape), atol=1e-13)
+
+
+def test_single_and_two_visible_keys():
+    # prefix 0: token 0 sees key 0 only, token 1 sees keys 0 and 1
+    case = gen.make_case("first_tokens", q_lens=[3], seq_lens=[3], num_q_heads=2, num_kv_heads=1,
+                         head_dim=8, page_size=16, q_kind="f32", seed=16)
+    o, l = run_oracle(case)
+    q = gen.to_numpy64(case.q)
+    K = oracle.gather_dense_kv(gen.to_numpy64(case.k_pool), case.block_tables[0], 3, 0)
+    V = _dense_v(case, 0, 0)
+    for h in range(2):
+        s0 = case.scale * q[0, h] @ K[0]
+        np.testing.assert_allclose(o[0, h], V[0], atol=0)
+        assert abs(l[0, h] - s0) < 1e-14
+        s = case.scale * np.array([q[1, h] @ K[0], q[1, h] @ K[1]])
+        w0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+        np.testing.assert_allclose(o[1, h], w0 * V[0] + (1 - w0) * V[1], atol=1e-14)
+        assert abs(l[1, h] - (max(s) + math.log(math.exp(s[0] - max(s)) + math.exp(s[1] - max(s))))) < 1e-14
+
+
+def test_rows_without_visible_keys_are_zero():
+    # q_len 6 > seq_len 3: tokens 0..2 see no key (n_i = 3 - 6 + i + 1 <= 0)
+    case = gen.make_case("empty_rows", q_lens=[6, 2], seq_lens=[3, 0], num_q_heads=2,
+                         num_kv_heads=2, head_dim=8, page_size=16, q_kind="f32", seed=17)
+    o, l = run_oracle(case)
+    assert not o[:3].any() and np.all(l[:3] == -np.inf)
+    assert not o[6:].any() and np.all(l[6:] == -np.inf)
+    assert np.isfinite(l[3:6]).all()
+
+
+# ---------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2)])
+def test_matches_torch_causal_sdpa(Hq, Hkv):
+    L, D = 37, 24
+    case = gen.make_case("sdpa", q_lens=[L], seq_lens=[L], num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, page_size=L, q_kind="f32", seed=18, shuffle=False)
+    o, l = run_oracle(case)
+    g = Hq // Hkv
+    qt = case.q.double().permute(1, 0, 2)                       # [Hq, L, D]
+    kt = case.k_pool[0].double().permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+    vt = case.v_pool[0].double().permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                           scale=case.scale)
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), atol=1e-13)
+    # logsumexp from the same library: logsumexp of the masked scores
+    sc = (qt @ kt.transpose(1, 2)) * case.scale
+    mask = torch.ones(L, L, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(sc.masked_fill(~mask, -math.inf), dim=-1)
+    np.testing.assert_allclose(l, ref_lse.T.numpy(), atol=1e-13)
+
+
+def test_chunk_equals_last_rows_of_full_causal_attention():
+    L, Q = 50, 13
+    full = gen.make_case("full", q_lens=[L], seq_lens=[L], num_q_heads=3, num_kv_heads=1,
+                         head_dim=16, page_size=16, q_kind="f32", seed=19)
+    chunk = gen.select_seqs(full, [0])
+    chunk.q = full.q[L - Q:].clone()
+    chunk.cu_seqlens_q = np.array([0, Q], dtype=np.int32)
+    o_full, l_full = run_oracle(full)
+    o_chunk, l_chunk = run_oracle(chunk)
+    assert_same(o_chunk, o_full[L - Q:])
+    assert_same(l_chunk, l_full[L - Q:])
+
+
+# ---------------------------------------------------------------- invariants
+
+def _repage(case, new_page_size, seed):
+    """Same dense K/V, laid out again with another page size and a fresh permutation."""
+    P2 = new_page_size
+    rng = np.random.default_rng(seed)
+    k = case.k_pool
+    v = case.v_pool
+    B = case.num_seqs
+    need = [-(-int(L) // P2) for L in case.seq_lens]
+    n_pages = sum(need) + 1
+    perm = rng.permutation(n_pages)
+    shape = (n_pages, P2) + tuple(k.shape[2:])
+    k2 = torch.full(shape, float("nan"), dtype=k.dtype)
+    v2 = torch.full(shape, float("nan"), dtype=v.dtype)
+    bt2 = np.full((B, max(need)), perm[-1], dtype=np.int32)
+    off = 0
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        for j in range(L):
+            src_p, src_s = case.block_tables[b, j // case.page_size], j % case.page_size
+            dst_p = perm[off + j // P2]
+            k2[dst_p, j % P2] = k[src_p, src_s]
+            v2[dst_p, j % P2] = v[src_p, src_s]
+        bt2[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    from dataclasses import replace
+    return replace(case, k_pool=k2, v_pool=v2, block_tables=bt2, page_size=P2)
+
+
+@pytest.mark.parametrize("P2", [4, 16, 48])
+def test_page_size_and_permutation_leave_output_unchanged(P2):
+    case = small_gqa_case(seed=20, page_size=16)
+    o, l = run_oracle(case)
+    o2, l2 = run_oracle(_repage(case, P2, seed=P2))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    case = small_gqa_case(seed=21)
+    g = case.num_q_heads // case.num_kv_heads
+    from dataclasses import replace
+    mha = replace(case, k_pool=case.k_pool.repeat_interleave(g, 2),
+                  v_pool=case.v_pool.repeat_interleave(g, 2), num_kv_heads=case.num_q_heads)
+    o, l = run_oracle(case)
+    o2, l2 = run_oracle(mha)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+
+
+def test_verify_row_equals_token_wise_decode_rows():
+    K1 = 5  # MTP verify row q = K + 1 with K = 4
+    L = 70
+    ver = gen.make_case("verify", q_lens=[K1], seq_lens=[L], num_q_heads=4, num_kv_heads=2,
+                        head_dim=16, page_size=16, q_kind="f32", seed=22)
+    o, l = run_oracle(ver)
+    from dataclasses import replace
+    dec = replace(ver, cu_seqlens_q=np.arange(K1 + 1, dtype=np.int32),
+                  seq_lens=np.array([L - K1 + 1 + i for i in range(K1)], dtype=np.int32),
+                  block_tables=np.repeat(ver.block_tables, K1, axis=0))
+    o2, l2 = run_oracle(dec)
+    assert_same(o, o2)
+    assert_same(l, l2)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 16, 40])
+def test_split_merge_equals_unsplit(S):
+    case = gen.make_case("split", q_lens=[4], seq_lens=[300], num_q_heads=2, num_kv_heads=1,
+                         head_dim=16, page_size=16, q_kind="f32", seed=23)
+    q = gen.to_numpy64(case.q)[:, 0, :]
+    K = oracle.gather_dense_kv(gen.to_numpy64(case.k_pool), case.block_tables[0], 300, 0)
+    V = oracle.gather_dense_kv(gen.to_numpy64(case.v_pool), case.block_tables[0], 300, 0)
+    counts = oracle.visible_key_count(300, 4, np.arange(4))
+    o, l = oracle.attention_rows(q, K, V, counts, case.scale)
+    os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S)
+    om, lm = oracle.merge_partials(os_, ls_)
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, l, atol=1e-13)
+    # an empty partial merges as the identity
+    oe = np.concatenate([os_, np.zeros((1,) + os_.shape[1:])])
+    le = np.concatenate([ls_, np.full((1,) + ls_.shape[1:], -np.inf)])
+    om2, lm2 = oracle.merge_partials(oe, le)
+    np.testing.assert_array_equal(om2, om)
+    np.testing.assert_array_equal(lm2, lm)
+
+
+def test_split_ranges_partition_properties():
+    for L in [0, 1, 31, 32, 33, 511, 512, 513, 4097, 10000]:
+        for S in [1, 2, 16]:
+            r = oracle.split_ranges(L, S)
+            assert len(r) == S
+            assert r[0][0] == 0 and r[-1][1] == L
+            for (a, b), (c, d) in zip(r, r[1:]):
+                assert b == c and a <= b
+            for a, b in r:
+                assert a % 32 == 0 or a == L
+            sizes = [b - a for a, b in r]
+            # equal parts of whole tiles, the last one possibly shorter or empty
+            full = [s for s in sizes if s > 0][:-1]
+            assert len(set(full)) <= 1
+    assert oracle.split_ranges(0, 4) == [(0, 0)] * 4
+    assert oracle.split_ranges(100, 16)[:4] == [(0, 32), (32, 64), (64, 96), (96, 100)]
+
+
+# ---------------------------------------------------------------- fp8
+
+def test_e5m2_decoder_matches_torch_on_all_bytes():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e5m2_to_float64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert (np.isnan(mine) == np.isnan(ref)).all()
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(mine[ok], ref[ok])
+    # a few values fixed by the bit layout alone
+    assert oracle.e5m2_to_float64(np.array([0x3C]))[0] == 1.0
+    assert oracle.e5m2_to_float64(np.array([0x01]))[0] == 2.0 ** -16
+    assert oracle.e5m2_to_float64(np.array([0x7B]))[0] == 57344.0
+    assert oracle.e5m2_to_float64(np.array([0xC0]))[0] == -2.0
+    assert np.isinf(oracle.e5m2_to_float64(np.array([0x7C]))[0])
+
+
+def test_e5m2_pool_dequantizes_with_scale():
+    case = gen.make_case("fp8", q_lens=[3], seq_lens=[20], num_q_heads=2, num_kv_heads=1,
+                         head_dim=16, page_size=16, q_kind="f16", kv_kind="e5m2", seed=24,
+                         k_scale=0.5, v_scale=2.0)
+    raw = case.k_pool.numpy()
+    k = oracle.dequantize_pool(raw, "e5m2", 0.5)
+    ref = torch.from_numpy(raw.copy()).view(torch.float8_e5m2).to(torch.float64).numpy() * 0.5
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(k[fin], ref[fin])
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _pin_suite_passes():
+    """Runs the pins that planted mistakes must trip; True if all hold."""
+    try:
+        test_numpy_oracle_matches_brute_force(lambda: small_gqa_case())
+        test_matches_torch_causal_sdpa(6, 2)
+        test_chunk_equals_last_rows_of_full_causal_attention()
+        test_zero_query_gives_uniform_mean()
+        test_rows_without_visible_keys_are_zero()
+        for S in (2, 3):
+            test_split_merge_equals_unsplit(S)
+    except AssertionError:
+        return False
+    return True
+
+
+MUTATIONS = {
+    "top_left_causal": ("visible_key_count", lambda L, Q, i: i + 1),
+    "off_by_one_visible": ("visible_key_count", lambda L, Q, i: L - Q + i),
+    "wrong_kv_head": ("gather_dense_kv",
+                      lambda pool, bt, L, h, _f=oa.gather_dense_kv: _f(pool, bt, L, (h + 1) % pool.shape[2])),
+    "page_slot_swapped": ("gather_dense_kv",
+                          lambda pool, bt, L, h: np.asarray(pool[np.asarray(bt)[np.arange(L) % pool.shape[1] % len(bt)],
+                                                                 np.arange(L) // pool.shape[1] % pool.shape[1], h, :], np.float64)),
+    "scale_dropped": ("attention_rows",
+                      lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, _f=oa.attention_rows:
+                      _f(q, K, V, c, 1.0, key_lo, key_hi, block)),
+    "lse_base2": ("attention_rows",
+                  lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, _f=oa.attention_rows:
+                  (lambda r: (r[0], r[1] / math.log(2)))(_f(q, K, V, c, scale, key_lo, key_hi, block))),
+    "merge_unweighted": ("merge_partials",
+                         lambda o, l: (np.asarray(o).mean(0), np.asarray(l).max(0))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    assert _pin_suite_passes()
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    assert not _pin_suite_passes(), f"mutation {name} survived every pin"
