@@ -1,0 +1,246 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input already
+resident in HBM: the varlen paged prefill of a 2048-token causal chunk after
+150,000 cached tokens (Hq 24, Hkv 4, D 256, page 64, fp16; the shape of the
+pages' D256 chunked-prefill measurement, at the full head count of the model),
+followed by the split-KV decode of a q=1 row over the same 152,048-token cache
+(pass 1 + merge).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_chunk|mixed_step|decode_batch|varlen]
+
+Prints ONE JSON line.  `value` is the step's algorithmic FLOPs (causal-exact:
+4 * D * Hq per attended pair) divided by the step time; the prefill TFLOPS and
+the decode GB/s are reported beside it, each from HIP events recorded on the
+stream the kernels run on.  `roofline` prices the dominant kernel (the prefill
+attention kernel) against the MFMA fp16 dense peak; `decode_roofline` prices
+the decode against the HBM peak.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from paged_attention_prefill_amd import inputs as gen  # noqa: E402
+from paged_attention_prefill_amd import ops, workload  # noqa: E402
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Call:
+    """One library call with preallocated outputs and workspace, timed by events."""
+
+    def __init__(self, kind, case, d, splits, max_q=None):
+        self.kind, self.case, self.d, self.splits = kind, case, d, splits
+        self.max_q = max_q or max(1, case.max_seqlen_q)
+        self.out = torch.empty_like(d["q"])
+        self.lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
+        D = case.head_dim
+        if kind == "prefill":
+            nb = ops.prefill_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
+        else:
+            nb = ops.decode_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
+        self.ws = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=d["q"].device)
+        self.times = []
+
+    def __call__(self, stream, record=False):
+        c, d = self.case, self.d
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        if self.kind == "prefill":
+            ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
+                              k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits, out=self.out,
+                              lse=self.lse, workspace=self.ws, stream=stream)
+        else:
+            ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], self.max_q, c.scale,
+                                num_splits=self.splits, k_scale=c.k_scale, v_scale=c.v_scale, out=self.out,
+                                lse=self.lse, workspace=self.ws, stream=stream)
+        if record:
+            e1.record(stream)
+            self.times.append((e0, e1))
+
+    def ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.times])) if self.times else float("nan")
+
+
+def build_workload(name):
+    """Returns (description, [Call specs]) for one step."""
+    if name == "long_chunk":
+        c = gen.long_chunk()
+        pre = gen.select_seqs(c, [0], name="prefill 2048 after 150000")
+        dec = gen.select_seqs(c, [1], name="decode q=1 at 152048")
+        desc = {"workload": "paged prefill of a 2048-token causal chunk after 150,000 cached tokens + split-KV "
+                            "decode of a q=1 row over the same cache",
+                "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
+                "seq_len": 152048, "kv_dtype": "f16"}
+        return desc, [("prefill", pre, "auto"), ("decode", dec, 128)]
+    if name == "mixed_step":
+        c = gen.mixed_step(kv_kind="f16")
+        ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
+        chunk = gen.select_seqs(c, [1], name="prefill 784 after 104000")
+        desc = {"workload": "mixed step: 784-token chunk after 104,000 cached tokens (prefill) + MTP verify row "
+                            "q=5 at 240,000 (split-KV decode)", "num_q_heads": 24, "num_kv_heads": 4,
+                "head_dim": 256, "page_size": 816, "kv_dtype": "f16"}
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 256)]
+    if name == "mixed_step_fp8":
+        c = gen.mixed_step(kv_kind="e5m2")
+        ver = gen.select_seqs(c, [0], name="verify q=5 at 240000 (fp8)")
+        chunk = gen.select_seqs(c, [1], name="prefill 784 after 104000 (fp8)")
+        desc = {"workload": "mixed step, fp8_e5m2 KV", "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256,
+                "page_size": 816, "kv_dtype": "e5m2"}
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 256)]
+    if name == "decode_batch":
+        c = gen.decode_batch(kind="bf16")
+        desc = {"workload": "split-KV decode batch: 32 rows q=1, lengths 0..10000, MHA 16 heads, D 128, page 16",
+                "num_q_heads": 16, "num_kv_heads": 16, "head_dim": 128, "page_size": 16, "kv_dtype": "bf16"}
+        return desc, [("decode", c, 16)]
+    if name == "varlen":
+        c = gen.varlen_prefill(kind="bf16")
+        desc = {"workload": "varlen paged prefill: q 64/300/1024/2048 after 0/777/4096/8192, Hq 32, Hkv 8, D 128, "
+                            "page 32", "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 32,
+                "kv_dtype": "bf16"}
+        return desc, [("prefill", c, "auto")]
+    raise SystemExit(f"unknown workload {name}")
+
+
+def call_flops(kind, case):
+    return workload.prefill_flops(case.cu_seqlens_q, case.seq_lens, case.num_q_heads, case.head_dim)
+
+
+def call_bytes(kind, case, splits):
+    return workload.decode_bytes(case.cu_seqlens_q, case.seq_lens, case.num_q_heads, case.num_kv_heads,
+                                 case.head_dim, case.page_size, case.q_kind, case.kv_kind, splits)
+
+
+def cpu_baseline(case, budget_rows, seed=0):
+    """Time the fp64 oracle on a sample of the prefill rows; returns the baseline dict."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(case.total_q, size=min(budget_rows, case.total_q), replace=False))
+    rows = np.array([(t, h) for t in toks for h in range(case.num_q_heads)], dtype=np.int64)
+    kind = "e5m2" if case.kv_kind == "e5m2" else "float"
+    k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, case.k_scale)
+    v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
+    q64 = gen.to_numpy64(case.q)
+    t0 = time.perf_counter()
+    oracle.paged_attention(q64, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    # attended pairs of the sampled rows
+    L = int(case.seq_lens[0])
+    Q = case.total_q
+    pairs = int(sum(max(0, L - Q + int(t) + 1) for t in toks)) * case.num_q_heads
+    flops = 4 * case.head_dim * pairs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} of {Q} query tokens x {case.num_q_heads} heads of the prefill "
+                      f"({pairs} attended pairs, {dt:.1f} s, numpy fp64)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_chunk")
+    ap.add_argument("--prefill-splits", default=None, help="override: 0 = auto, or a count")
+    ap.add_argument("--decode-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query tokens in the oracle sample")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding is a design note, not built)"}))
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ops.lib()
+
+    log(f"building workload {a.workload} ...")
+    desc, specs = build_workload(a.workload)
+    calls = []
+    for kind, case, splits in specs:
+        if kind == "prefill":
+            s = a.prefill_splits if a.prefill_splits is not None else splits
+            s = 0 if s == "auto" else int(s)
+            if s == 0:
+                s = ops.auto_splits(case.total_q, case.num_seqs, case.max_seqlen_q, case.num_q_heads,
+                                    case.num_kv_heads, case.head_dim, ops._TORCH_TO_PA[case.q.dtype],
+                                    ops.PA_FP8_E5M2 if case.kv_kind == "e5m2" else ops._TORCH_TO_PA[case.q.dtype])
+        else:
+            s = a.decode_splits or splits
+        log(f"  {kind}: {case.name}, splits {s}")
+        calls.append(Call(kind, case, gen.to_device(case), s))
+    stream = torch.cuda.current_stream()
+
+    for _ in range(a.warmup):
+        for c in calls:
+            c(stream)
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {a.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for c in calls:
+            c(stream, record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / a.steps * 1e3
+
+    step_flops = 0
+    parts = {}
+    for c in calls:
+        ms = c.ms()
+        if c.kind == "prefill":
+            f = call_flops(c.kind, c.case)
+            step_flops += f
+            parts["prefill"] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "flops": f, "splits": c.splits,
+                                "name": c.case.name}
+        else:
+            b = call_bytes(c.kind, c.case, c.splits)
+            f = call_flops(c.kind, c.case)
+            step_flops += f
+            parts["decode"] = {"ms": ms, "gbs": b / (ms * 1e-3) / 1e9, "bytes": b, "splits": c.splits,
+                               "name": c.case.name}
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    res = {"metric": "paged-prefill TFLOPS (2K chunk @150K ctx, D256); split-KV decode HBM GB/s",
+           "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": specs[0][1].q_kind, "data": "synthetic", "config": desc}
+    res.update(parts)
+    if "prefill" in parts:
+        pf = parts["prefill"]
+        res["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                           "kernel": "attn_mfma_kernel (+ merge when split)"}
+    if "decode" in parts:
+        dc = parts["decode"]
+        res["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": dc["gbs"] / HBM_PEAK_GBS, "traffic": None}
+    if not a.no_cpu_baseline and "prefill" in parts:
+        pre = [c for c in calls if c.kind == "prefill"][0].case
+        if pre.num_seqs == 1:
+            log("timing the oracle on a sample ...")
+            res["cpu_baseline"] = cpu_baseline(pre, a.cpu_rows)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

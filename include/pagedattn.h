@@ -1,0 +1,197 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: paged softmax attention over a
+ * block-table KV cache, hand-written HIP kernels for AMD gfx950 (MI355X).
+ *
+ * What the calls compute (the pages this library follows):
+ *  - pa_paged_prefill: the varlen paged prefill of InferMatrixLab/vllm-rlt
+ *    PR #128 ("Purpose", Prefill): packed queries addressed by cu_seqlens_q,
+ *    one block table per sequence, causal mask aligned bottom-right (query
+ *    token i of a sequence with Q query tokens and L keys sees keys
+ *    j < L - Q + i + 1), GQA, exact products for FP32 inputs; optionally the
+ *    key range of every query tile is split in whole tiles and merged by
+ *    log-sum-exp (1CatAI/1Cat-vLLM PR #1279, commit 5, split-KV by waves).
+ *  - pa_split_kv_decode: the split-KV decode of PR #128 ("Purpose", Decode)
+ *    for small-q rows (q = 1, or an MTP verify row q = K+1 as in
+ *    1CatAI/1Cat-vLLM PR #616, "Purpose"): each row's keys are cut into
+ *    num_splits equal parts of whole 32-key tiles, a function of the row's own
+ *    length only, each part writes an FP32 partial softmax state, and a second
+ *    launch merges them.  A row's output is bitwise independent of the other
+ *    rows in the call for fixed (num_splits, max_q_per_row, dtypes, head_dim).
+ *  - pa_merge_states: that second pass on its own (also used by prefill
+ *    splits).
+ *  - fp8_e5m2 KV (1CatAI/1Cat-vLLM PR #616, fp8_e5m2 paragraph of "Test
+ *    Result"): bytes are dequantized inside the kernels, value = e5m2(byte) *
+ *    k_scale (or v_scale).
+ *
+ * Conventions shared by all calls
+ *  - Every data pointer is DEVICE memory owned by the caller; the library
+ *    allocates nothing, keeps no state besides a per-device cache of the
+ *    compute-unit count, and is safe to call from several threads.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *    stream).  The launch grid depends only on the host scalars, so the calls
+ *    can be captured in a HIP graph.
+ *  - Device-side metadata (cu_seqlens_q, seq_lens, block_tables) is trusted:
+ *    checking it would need a device-to-host copy.  pa_validate_metadata
+ *    checks host copies of it.
+ *  - Layouts: q and out are [total_q, num_q_heads, head_dim], contiguous.
+ *    lse is [total_q, num_q_heads] float32, natural log, -inf for a row that
+ *    sees no key (its output is 0).  cu_seqlens_q is int32 [num_seqs + 1]
+ *    with cu_seqlens_q[0] = 0 and cu_seqlens_q[num_seqs] = total_q;
+ *    seq_lens is int32 [num_seqs] (keys of the sequence, the chunk's own keys
+ *    included: the caller writes the chunk's K/V into the pages first);
+ *    block_tables is int32 [num_seqs, max_pages_per_seq], row-major.
+ *  - KV pages: element (page p, slot s, kv head h, dim d) of K is at
+ *    k_pages + p*stride_page + s*stride_token + h*stride_head + d (in
+ *    elements of the KV dtype); V uses the same geometry.  The layouts
+ *    [pages, page_size, Hkv, D] and [pages, Hkv, page_size, D] are both
+ *    expressible.  page_size is any multiple of 16 (1CatAI/1Cat-vLLM PR #616,
+ *    the any-page gate).  Strides and base pointers must be 16-byte aligned.
+ *  - Query head hq reads kv head hq / (num_q_heads / num_kv_heads).
+ *  - Supported dtypes: (q, KV) = (F32, F32), (F16, F16), (BF16, BF16),
+ *    (F16, FP8_E5M2); out has q's dtype.  head_dim is a multiple of 16 in
+ *    [16, 256].
+ *
+ * Errors: every call returns PA_OK (0) or a negative pa_status; nothing is
+ * launched when an argument is rejected.  pa_last_error() gives a message
+ * for the last failure on the calling thread.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_VERSION 1
+#define PA_DECODE_MAX_Q 16       /* largest q of a decode / verify row */
+#define PA_DECODE_SPLIT_TILE 32  /* keys per tile of the split partition */
+#define PA_PREFILL_MAX_AUTO_SPLITS 4
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad stride */
+  PA_ERR_UNSUPPORTED = -2,      /* dtype pair, head_dim, page_size, GQA ratio, q > 16 */
+  PA_ERR_WORKSPACE = -3,        /* workspace missing or too small */
+  PA_ERR_HIP = -4,              /* HIP runtime / launch failure */
+  PA_ERR_METADATA = -5          /* pa_validate_metadata found an inconsistency */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E5M2 = 3
+} pa_dtype;
+
+/* One paged KV cache (K and V share the geometry). Host struct, device pointers. */
+typedef struct pa_kv_cache {
+  const void *k_pages;   /* device, caller-owned */
+  const void *v_pages;   /* device, caller-owned */
+  int64_t stride_page;   /* elements between pages */
+  int64_t stride_token;  /* elements between slots of a page */
+  int64_t stride_head;   /* elements between kv heads */
+  int32_t num_pages;
+  int32_t page_size;     /* multiple of 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* multiple of 16 in [16, 256]; contiguous */
+  int32_t dtype;         /* pa_dtype */
+  float k_scale;         /* FP8_E5M2 only (must be 1 otherwise) */
+  float v_scale;
+} pa_kv_cache;
+
+/*
+ * Varlen paged prefill (InferMatrixLab/vllm-rlt PR #128, "Purpose", Prefill).
+ *   q [total_q, num_q_heads, head_dim] (q_dtype); out same shape and dtype;
+ *   lse nullable; scale multiplies q.k (k_scale folded in for fp8).
+ *   max_seqlen_q bounds every cu_seqlens_q[b+1] - cu_seqlens_q[b] (it sizes the
+ *   static grid).  num_kv_splits: 1 = no key split; 2..64 = split every query
+ *   tile's keys into that many whole-tile parts and merge; 0 = choose 1..4 by
+ *   how many full waves of work groups fill the device (1CatAI/1Cat-vLLM
+ *   PR #1279, commit 5), which depends on the device, not on the batch.
+ *   With num_kv_splits != 1 the workspace must hold
+ *   pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits)
+ *   bytes of device memory (float-aligned); otherwise it may be NULL.
+ */
+int pa_paged_prefill(const void *q, int32_t q_dtype, void *out, float *lse,
+                     const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                     const int32_t *block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
+                     int32_t total_q, int32_t max_seqlen_q, int32_t num_q_heads,
+                     const pa_kv_cache *kv, float scale, int32_t num_kv_splits,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Split-KV decode / verify (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode).
+ *   Rows are the sequences of the call; row b has q_len = cu_seqlens_q[b+1] -
+ *   cu_seqlens_q[b] <= max_q_per_row <= PA_DECODE_MAX_Q query tokens (q_len 0
+ *   is allowed).  Row b's keys [0, L) are cut with T = PA_DECODE_SPLIT_TILE and
+ *   per = ceil(ceil(L / T) / num_splits) tiles per part; part s covers
+ *   [s*per*T, min((s+1)*per*T, L)).  Pass 1 writes, for every (token, q head,
+ *   part), an FP32 record of head_dim + 2 floats -- the part's normalised
+ *   output, its lse, one pad -- into the workspace laid out
+ *   [total_q, num_q_heads, num_splits, head_dim + 2]; pass 2 (the merge)
+ *   writes out and lse.  workspace_bytes >= pa_decode_workspace_bytes(...).
+ */
+int pa_split_kv_decode(const void *q, int32_t q_dtype, void *out, float *lse,
+                       const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                       const int32_t *block_tables, int32_t num_rows, int32_t max_pages_per_seq,
+                       int32_t total_q, int32_t max_q_per_row, int32_t num_q_heads,
+                       const pa_kv_cache *kv, float scale, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Merge of FP32 partial softmax states (InferMatrixLab/vllm-rlt PR #128,
+ * "Purpose", Decode: the second kernel).
+ *   partials [num_tokens, num_heads, num_splits, head_dim + 2] float32, record =
+ *   (o_s normalised, lse_s, pad).  For every (token, head): M = max_s lse_s,
+ *   w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s (ascending s),
+ *   lse = M + log(sum_s w_s); all parts empty (lse = -inf) gives o = 0,
+ *   lse = -inf.  out [num_tokens, num_heads, head_dim] in out_dtype (F32, F16,
+ *   BF16); out_lse nullable.  o_s of an empty part is ignored.
+ */
+int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_tokens,
+                    int32_t num_heads, int32_t head_dim, void *out, int32_t out_dtype,
+                    float *out_lse, void *stream);
+
+/* Workspace sizes in bytes (host-only, no HIP call). */
+size_t pa_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_kv_splits);
+size_t pa_decode_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t num_splits);
+
+/*
+ * Capability check without launching (host-only): returns PA_OK or the status
+ * a call with these scalars would return, and a static rejection reason.
+ */
+int pa_check_supported(int32_t q_dtype, int32_t kv_dtype, int32_t head_dim, int32_t page_size,
+                       int32_t num_q_heads, int32_t num_kv_heads, const char **reason);
+
+/*
+ * Host-side metadata check (debugging and tests; host pointers).  Checks that
+ * cu_seqlens_q starts at 0, is non-decreasing and ends at total_q; that every
+ * q length is <= max_q (when max_q > 0) and every seq_len is >= 0 and fits
+ * max_pages_per_seq pages; and that every block-table entry a sequence reads
+ * lies in [0, num_pages).  Returns PA_OK or PA_ERR_METADATA.
+ */
+int pa_validate_metadata(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                         const int32_t *block_tables, int32_t num_seqs,
+                         int32_t max_pages_per_seq, int32_t total_q, int32_t max_q,
+                         int32_t page_size, int32_t num_pages);
+
+/* Number of key splits pa_paged_prefill picks for num_kv_splits = 0 (uses the
+ * current device's compute-unit count); negative pa_status on failure. */
+int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen_q,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t q_dtype, int32_t kv_dtype);
+
+const char *pa_status_string(int status);
+const char *pa_last_error(void);
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

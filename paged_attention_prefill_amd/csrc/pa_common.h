@@ -1,0 +1,70 @@
+// Shared device-side definitions of the paged-attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+enum KvKind : int { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_E5M2 = 3 };
+
+// Keys per tile of the split partition (the decode parts and the prefill parts
+// are both cut on this grid).
+constexpr int kSplitTile = 32;
+
+// Everything a pass-1 kernel needs; passed by value.
+struct AttnParams {
+  const void* q;           // [total_q, Hq, D]
+  void* out;               // [total_q, Hq, D] (written when num_splits == 1 and !force_partial)
+  float* lse;              // [total_q, Hq] nullable
+  float* partial;          // [total_q, Hq, S, D + 2] when writing partial records
+  const int* cu_seqlens_q; // [B + 1]
+  const int* seq_lens;     // [B]
+  const int* block_tables; // [B, max_pages]
+  const void* k_pages;
+  const void* v_pages;
+  int64_t stride_page, stride_token, stride_head;  // elements
+  int num_seqs, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size;
+  int num_splits;
+  int write_partial;       // 1: records to `partial`; 0: final out/lse
+  int qtiles;              // q tiles per (sequence, kv head) in the grid
+  float scale_log2;        // scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// Block index -> work index so that consecutive work items run on the same XCD.
+// Work groups are handed to the 8 XCDs round robin; this is a bijection on
+// [0, n) whatever the real placement is, so it only affects locality.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = n / 8, rem = n % 8;
+  const int xcd = bid % 8, local = bid / 8;
+  const int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + local;
+}
+
+// Key range [lo, hi) of part `s` of a row with L keys cut into S parts of
+// whole kSplitTile-key tiles: per = ceil(ceil(L / T) / S).
+__device__ __forceinline__ void split_range(int L, int S, int s, int& lo, int& hi) {
+  const int tiles = (L + kSplitTile - 1) / kSplitTile;
+  const int per = (tiles + S - 1) / S;
+  const long long a = (long long)s * per * kSplitTile;
+  const long long b = a + (long long)per * kSplitTile;
+  lo = (int)(a < L ? a : L);
+  hi = (int)(b < L ? b : L);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp8 E5M2 byte -> fp16 bits: E5M2 is the high byte of an fp16 with the same
+// sign/exponent/mantissa layout, so the conversion is exact.
+__device__ __forceinline__ void e5m2x4_to_f16x4(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  lo = ((x & 0x000000FFu) << 8) | ((x & 0x0000FF00u) << 16);
+  hi = ((x & 0x00FF0000u) >> 8) | (x & 0xFF000000u);
+}
+
+}  // namespace pa

@@ -1,0 +1,375 @@
+// C ABI of libpagedattn.so: argument checks, launch plans and dispatch.
+// The operations are described in include/pagedattn.h.  Every check here runs
+// on host scalars before any HIP call, so a rejected call launches nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pa_common.h"
+#include "../../include/pagedattn.h"
+
+namespace pa {
+hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                            hipStream_t stream);
+hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                            hipStream_t stream);
+hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
+                        float* out_lse, hipStream_t stream);
+hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
+int mfma_rows_per_group();
+int valu_rows_per_group();
+}  // namespace pa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+size_t dtype_size(int dt) {
+  switch (dt) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_FP8_E5M2: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Supported (q, kv) pairs, head dims and page sizes; returns status + reason.
+int check_supported(int q_dtype, int kv_dtype, int head_dim, int page_size, int hq, int hkv,
+                    const char** reason) {
+  const char* r = nullptr;
+  int st = PA_OK;
+  if (dtype_size(q_dtype) == 0 || q_dtype == PA_FP8_E5M2) {
+    st = PA_ERR_UNSUPPORTED, r = "q dtype must be F32, F16 or BF16";
+  } else if (dtype_size(kv_dtype) == 0) {
+    st = PA_ERR_UNSUPPORTED, r = "unknown KV dtype";
+  } else if (!(kv_dtype == q_dtype || (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_F16))) {
+    st = PA_ERR_UNSUPPORTED, r = "KV dtype must equal q dtype, or be FP8_E5M2 with F16 q";
+  } else if (head_dim < 16 || head_dim > 256 || head_dim % 16 != 0) {
+    st = PA_ERR_UNSUPPORTED, r = "head_dim must be a multiple of 16 in [16, 256]";
+  } else if (page_size < 16 || page_size % 16 != 0) {
+    st = PA_ERR_UNSUPPORTED, r = "page_size must be a positive multiple of 16";
+  } else if (hq < 1 || hkv < 1) {
+    st = PA_ERR_INVALID_ARGUMENT, r = "head counts must be positive";
+  } else if (hq % hkv != 0) {
+    st = PA_ERR_UNSUPPORTED, r = "num_q_heads must be a multiple of num_kv_heads";
+  }
+  if (reason) *reason = r ? r : "supported";
+  return st;
+}
+
+int dpad_of(int head_dim) { return head_dim <= 64 ? 64 : head_dim <= 128 ? 128 : 256; }
+
+int kind_of(int dt) {
+  switch (dt) {
+    case PA_F32: return pa::KV_F32;
+    case PA_F16: return pa::KV_F16;
+    case PA_BF16: return pa::KV_BF16;
+    default: return pa::KV_E5M2;
+  }
+}
+
+int check_kv(const pa_kv_cache* kv, int q_dtype, int hq) {
+  if (kv == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  const char* reason = nullptr;
+  int st = check_supported(q_dtype, kv->dtype, kv->head_dim, kv->page_size, hq, kv->num_kv_heads, &reason);
+  if (st != PA_OK) return fail(st, "%s", reason);
+  if (kv->num_pages < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  if (kv->k_pages == nullptr || kv->v_pages == nullptr)
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_pages / v_pages is NULL");
+  if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_pages / v_pages must be 16-byte aligned");
+  const int64_t es = (int64_t)dtype_size(kv->dtype);
+  const int64_t st3[3] = {kv->stride_page, kv->stride_token, kv->stride_head};
+  for (int i = 0; i < 3; ++i)
+    if (st3[i] <= 0 || (st3[i] * es) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "KV strides must be positive and 16-byte multiples");
+  if (!std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be finite");
+  if (kv->dtype != PA_FP8_E5M2 && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
+    return fail(PA_ERR_UNSUPPORTED, "k_scale / v_scale apply to FP8_E5M2 KV only (must be 1)");
+  return PA_OK;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (dev >= 0 && dev < 64) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return PA_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return fail(PA_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return PA_OK;
+}
+
+// Split count in 1..4 that finishes the work groups in the fewest full waves on
+// this device (1CatAI/1Cat-vLLM PR #1279, commit 5); ties go to fewer splits.
+int auto_splits(int64_t active_groups, int slots) {
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= PA_PREFILL_MAX_AUTO_SPLITS; ++s) {
+    const int64_t waves = (active_groups * s + slots - 1) / slots;
+    const double cost = (double)waves / s;
+    if (cost < best_cost - 1e-9) best_cost = cost, best = s;
+  }
+  return best;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return PA_VERSION; }
+
+const char* pa_last_error(void) { return g_err; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_METADATA: return "inconsistent metadata";
+    default: return "unknown status";
+  }
+}
+
+int pa_check_supported(int32_t q_dtype, int32_t kv_dtype, int32_t head_dim, int32_t page_size,
+                       int32_t num_q_heads, int32_t num_kv_heads, const char** reason) {
+  return check_supported(q_dtype, kv_dtype, head_dim, page_size, num_q_heads, num_kv_heads, reason);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_kv_splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int s = num_kv_splits == 0 ? PA_PREFILL_MAX_AUTO_SPLITS : num_kv_splits;
+  if (s <= 1) return 0;
+  return (size_t)total_q * num_q_heads * s * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+size_t pa_decode_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t num_splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return (size_t)total_q * num_q_heads * num_splits * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int pa_validate_metadata(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt,
+                         int32_t num_seqs, int32_t max_pages, int32_t total_q, int32_t max_q,
+                         int32_t page_size, int32_t num_pages) {
+  if (num_seqs < 0 || max_pages < 1 || page_size < 1 || num_pages < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad scalar");
+  if (num_seqs == 0) return ok();
+  if (!cu || !seq_lens || !bt) return fail(PA_ERR_INVALID_ARGUMENT, "NULL metadata pointer");
+  if (cu[0] != 0) return fail(PA_ERR_METADATA, "cu_seqlens_q[0] = %d, expected 0", cu[0]);
+  for (int b = 0; b < num_seqs; ++b) {
+    const int ql = cu[b + 1] - cu[b];
+    if (ql < 0) return fail(PA_ERR_METADATA, "cu_seqlens_q decreases at %d", b);
+    if (max_q > 0 && ql > max_q) return fail(PA_ERR_METADATA, "sequence %d has q_len %d > %d", b, ql, max_q);
+    const int L = seq_lens[b];
+    if (L < 0) return fail(PA_ERR_METADATA, "seq_lens[%d] = %d < 0", b, L);
+    const int64_t need = ((int64_t)L + page_size - 1) / page_size;
+    if (need > max_pages)
+      return fail(PA_ERR_METADATA, "sequence %d needs %lld pages > max_pages_per_seq %d", b,
+                  (long long)need, max_pages);
+    for (int64_t i = 0; i < need; ++i) {
+      const int pg = bt[(int64_t)b * max_pages + i];
+      if (pg < 0 || pg >= num_pages)
+        return fail(PA_ERR_METADATA, "block_tables[%d][%lld] = %d out of [0, %d)", b, (long long)i, pg,
+                    num_pages);
+    }
+  }
+  if (cu[num_seqs] != total_q)
+    return fail(PA_ERR_METADATA, "cu_seqlens_q[%d] = %d != total_q %d", num_seqs, cu[num_seqs], total_q);
+  return ok();
+}
+
+int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen_q,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t q_dtype, int32_t kv_dtype) {
+  const char* reason;
+  int st = check_supported(q_dtype, kv_dtype, head_dim, 16, num_q_heads, num_kv_heads, &reason);
+  if (st != PA_OK) return fail(st, "%s", reason);
+  if (total_q <= 0 || num_seqs <= 0) return 1;
+  const int g = num_q_heads / num_kv_heads;
+  const bool valu = q_dtype == PA_F32;
+  const int rows = valu ? pa::valu_rows_per_group() : pa::mfma_rows_per_group();
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != PA_OK) return st;
+  int occ = 1;
+  if (!valu) {
+    if (pa::mfma_occupancy(kind_of(q_dtype), kind_of(kv_dtype), dpad_of(head_dim), &occ) != hipSuccess || occ < 1)
+      occ = 1;
+  }
+  const int64_t tiles_grid = ceil_div((int64_t)max_seqlen_q * g, rows) * num_seqs;
+  const int64_t tiles_est = ceil_div((int64_t)total_q * g, rows) + num_seqs - 1;
+  const int64_t active = (tiles_grid < tiles_est ? tiles_grid : tiles_est) * num_kv_heads;
+  return auto_splits(active, cus * occ);
+}
+
+static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
+                         const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
+                         int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
+                         int splits, bool always_partial, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  const int g = hq / kv->num_kv_heads;
+  const bool valu = q_dtype == PA_F32;
+  const int rows = valu ? pa::valu_rows_per_group() : pa::mfma_rows_per_group();
+  const int qtiles = (int)ceil_div((int64_t)max_q * g, rows);
+  const int64_t nblocks = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
+  if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nblocks);
+  if (nblocks == 0 || total_q == 0) return ok();
+  const bool partial = always_partial || splits > 1;
+
+  pa::AttnParams p;
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.partial = (float*)workspace;
+  p.cu_seqlens_q = cu;
+  p.seq_lens = seq_lens;
+  p.block_tables = bt;
+  p.k_pages = kv->k_pages;
+  p.v_pages = kv->v_pages;
+  p.stride_page = kv->stride_page;
+  p.stride_token = kv->stride_token;
+  p.stride_head = kv->stride_head;
+  p.num_seqs = num_seqs;
+  p.max_pages = max_pages;
+  p.num_q_heads = hq;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.group = g;
+  p.head_dim = kv->head_dim;
+  p.page_size = kv->page_size;
+  p.num_splits = splits;
+  p.write_partial = partial ? 1 : 0;
+  p.qtiles = qtiles;
+  p.scale_log2 = scale * (kv->dtype == PA_FP8_E5M2 ? kv->k_scale : 1.0f) * 1.4426950408889634f;
+  p.v_scale = kv->dtype == PA_FP8_E5M2 ? kv->v_scale : 1.0f;
+
+  const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
+  hipError_t e = valu ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
+                      : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (partial) {
+    e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  (void)ws_bytes;
+  return ok();
+}
+
+static int check_common(const void* q, int q_dtype, void* out, const int32_t* cu, const int32_t* seq_lens,
+                        const int32_t* bt, int num_seqs, int max_pages, int total_q, int max_q, int hq,
+                        const pa_kv_cache* kv) {
+  if (num_seqs < 0 || total_q < 0 || max_q < 0 || max_pages < 1 || hq < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative size or max_pages_per_seq < 1 or num_q_heads < 1");
+  int st = check_kv(kv, q_dtype, hq);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!q || !out || !cu || !seq_lens || !bt) return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARGUMENT, "q / out must be 16-byte aligned");
+  if (max_q < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max q length must be >= 1 when total_q > 0");
+  return PA_OK;
+}
+
+int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                     const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs,
+                     int32_t max_pages_per_seq, int32_t total_q, int32_t max_seqlen_q,
+                     int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_kv_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq,
+                        total_q, max_seqlen_q, num_q_heads, kv);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (num_kv_splits < 0 || num_kv_splits > 64) return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_splits must be in [0, 64]");
+  if (num_seqs == 0 || total_q == 0) return ok();
+  int splits = num_kv_splits;
+  if (splits != 1) {
+    const size_t need = pa_prefill_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_kv_splits);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u))
+      return fail(PA_ERR_WORKSPACE, "prefill with %d splits needs %zu bytes of 8-byte aligned workspace (got %zu)",
+                  num_kv_splits, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+  }
+  if (splits == 0) {
+    splits = pa_prefill_auto_splits(total_q, num_seqs, max_seqlen_q, num_q_heads, kv->num_kv_heads,
+                                    kv->head_dim, q_dtype, kv->dtype);
+    if (splits < 0) return splits;
+  }
+  return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_seqs,
+                       max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, false,
+                       workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                       const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
+                       int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
+                       int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                        total_q, max_q_per_row, num_q_heads, kv);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (max_q_per_row > PA_DECODE_MAX_Q)
+    return fail(PA_ERR_UNSUPPORTED, "max_q_per_row %d > %d (longer rows go to pa_paged_prefill)", max_q_per_row,
+                PA_DECODE_MAX_Q);
+  if (num_splits < 1 || num_splits > 4096) return fail(PA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 4096]");
+  if (num_rows == 0 || total_q == 0) return ok();
+  const size_t need = pa_decode_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_splits);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u))
+    return fail(PA_ERR_WORKSPACE, "decode needs %zu bytes of 8-byte aligned workspace (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                       total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, true, workspace,
+                       workspace_bytes, (hipStream_t)stream);
+}
+
+int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, void* out, int32_t out_dtype, float* out_lse, void* stream) {
+  if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 1 || head_dim > 256)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad merge sizes");
+  if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "merge output dtype must be F32, F16 or BF16");
+  if (num_tokens == 0) return ok();
+  if (!partials || !out) return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31) * 4)
+    return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  hipError_t e = pa::launch_merge(partials, num_splits, num_tokens, num_heads, head_dim, out, kind_of(out_dtype),
+                                  out_lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

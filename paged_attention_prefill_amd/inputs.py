@@ -240,3 +240,21 @@ def to_numpy64(t: torch.Tensor, kv_kind: Optional[str] = None):
     if kv_kind == "e5m2":
         return t.numpy()
     return t.to(torch.float64).numpy()
+
+
+def to_device(case, device="cuda"):
+    """Copies of a case's tensors on the GPU (the pools keep their logical strides)."""
+    def dev(t):
+        return t.to(device)
+    k = case.k_pool
+    v = case.v_pool
+    if case.layout != "NHD":
+        # move the physical storage, then rebuild the same logical view
+        k = k.permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
+    else:
+        k, v = dev(k.contiguous()), dev(v.contiguous())
+    return dict(q=dev(case.q.contiguous()), k=k, v=v,
+                cu=torch.from_numpy(case.cu_seqlens_q.astype(np.int32)).to(device),
+                seq_lens=torch.from_numpy(case.seq_lens.astype(np.int32)).to(device),
+                bt=torch.from_numpy(np.ascontiguousarray(case.block_tables, dtype=np.int32)).to(device))

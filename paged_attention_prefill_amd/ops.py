@@ -1,0 +1,234 @@
+"""Thin ctypes binding over libpagedattn.so (argument marshalling only).
+
+Every step of the attention runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, sizes and the current HIP stream,
+and turns status codes into exceptions.  It raises if the library has not been
+built: there is no fallback path.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
+
+PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA = \
+    0, -1, -2, -3, -4, -5
+PA_F32, PA_F16, PA_BF16, PA_FP8_E5M2 = 0, 1, 2, 3
+DECODE_MAX_Q = 16
+SPLIT_TILE = 32
+
+_TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+                torch.uint8: PA_FP8_E5M2, torch.float8_e5m2: PA_FP8_E5M2}
+_PA_TO_TORCH = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"pagedattn status {status}: {message}")
+        self.status = status
+
+
+class KvCache(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("stride_page", ctypes.c_int64), ("stride_token", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def lib():
+    """The loaded library; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_attention_prefill_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pa_paged_prefill.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                       ctypes.POINTER(KvCache), ctypes.c_float, _I, _P, _SZ, _P]
+        L.pa_split_kv_decode.argtypes = L.pa_paged_prefill.argtypes
+        L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
+        L.pa_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.pa_prefill_workspace_bytes.restype = _SZ
+        L.pa_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.pa_decode_workspace_bytes.restype = _SZ
+        L.pa_check_supported.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_char_p)]
+        L.pa_validate_metadata.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I]
+        L.pa_prefill_auto_splits.argtypes = [_I] * 8
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_last_error.restype = ctypes.c_char_p
+        for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_merge_states", "pa_check_supported",
+                     "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
+            if name != "pa_status_string":
+                getattr(L, name).restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def header_symbols():
+    """Function names declared in include/pagedattn.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status):
+    if status != PA_OK:
+        L = lib()
+        raise PagedAttentionError(status, (L.pa_last_error() or b"").decode() or
+                                  L.pa_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype(t):
+    try:
+        return _TORCH_TO_PA[t.dtype]
+    except KeyError:
+        raise PagedAttentionError(PA_ERR_UNSUPPORTED, f"unsupported dtype {t.dtype}") from None
+
+
+def kv_cache(k_pages, v_pages, k_scale=1.0, v_scale=1.0):
+    """Describe logical [num_pages, page_size, Hkv, D] K/V page tensors (D contiguous)."""
+    if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "K and V pages must share shape and strides")
+    if k_pages.dtype != v_pages.dtype:
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "K and V pages must share the dtype")
+    if k_pages.dim() != 4 or k_pages.stride(3) != 1:
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "pages must be 4-D with a contiguous head dim")
+    n, P, H, D = k_pages.shape
+    s = k_pages.stride()
+    return KvCache(k_pages.data_ptr(), v_pages.data_ptr(), s[0], s[1], s[2], n, P, H, D,
+                   _dtype(k_pages), float(k_scale), float(v_scale))
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits):
+    return int(lib().pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits))
+
+
+def decode_workspace_bytes(total_q, num_q_heads, head_dim, num_splits):
+    return int(lib().pa_decode_workspace_bytes(total_q, num_q_heads, head_dim, num_splits))
+
+
+def _workspace(workspace, nbytes, device):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+    return workspace
+
+
+def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_seqlen_q, scale,
+                  *, k_scale=1.0, v_scale=1.0, num_kv_splits=1, out=None, lse=None,
+                  return_lse=False, workspace=None, stream=None):
+    """pa_paged_prefill on torch tensors; returns out (and lse)."""
+    total_q, Hq, D = q.shape
+    if not q.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    B = int(seq_lens.numel())
+    ws_bytes = prefill_workspace_bytes(total_q, Hq, D, num_kv_splits)
+    workspace = _workspace(workspace, ws_bytes, q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_paged_prefill(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
+                                  _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
+                                  _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
+                                  total_q, int(max_seqlen_q), Hq, ctypes.byref(kv), float(scale),
+                                  int(num_kv_splits), _ptr(workspace), ws_have, _stream(stream)))
+    return (out, lse) if return_lse or lse is not None else out
+
+
+def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
+                    *, num_splits=16, k_scale=1.0, v_scale=1.0, out=None, lse=None,
+                    return_lse=False, workspace=None, stream=None):
+    """pa_split_kv_decode on torch tensors; returns out (and lse)."""
+    total_q, Hq, D = q.shape
+    if not q.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    B = int(seq_lens.numel())
+    ws_bytes = decode_workspace_bytes(total_q, Hq, D, num_splits)
+    workspace = _workspace(workspace, ws_bytes, q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_split_kv_decode(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
+                                    _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
+                                    _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
+                                    total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale),
+                                    int(num_splits), _ptr(workspace), ws_have, _stream(stream)))
+    return (out, lse) if return_lse or lse is not None else out
+
+
+def merge_states(partials, out_dtype=torch.float32, *, out=None, lse=None, return_lse=False, stream=None):
+    """pa_merge_states: partials [N, H, S, D + 2] float32 -> out [N, H, D]."""
+    N, H, S, R = partials.shape
+    D = R - 2
+    if partials.dtype != torch.float32 or not partials.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "partials must be contiguous float32")
+    out = torch.empty((N, H, D), dtype=out_dtype, device=partials.device) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=partials.device)
+    _check(lib().pa_merge_states(_ptr(partials), S, N, H, D, _ptr(out), _TORCH_TO_PA[out.dtype],
+                                 _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse or lse is not None else out
+
+
+def check_supported(q_dtype, kv_dtype, head_dim, page_size, num_q_heads, num_kv_heads):
+    """(status, reason) of pa_check_supported; dtypes as PA_* codes."""
+    r = ctypes.c_char_p()
+    st = lib().pa_check_supported(q_dtype, kv_dtype, head_dim, page_size, num_q_heads, num_kv_heads,
+                                  ctypes.byref(r))
+    return st, r.value.decode()
+
+
+def validate_metadata(cu_seqlens_q, seq_lens, block_tables, total_q, max_q, page_size, num_pages):
+    """pa_validate_metadata on host (numpy) copies; returns (status, message)."""
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    st = lib().pa_validate_metadata(cu.ctypes.data, sl.ctypes.data, bt.ctypes.data, len(sl),
+                                    bt.shape[-1], total_q, max_q, page_size, num_pages)
+    return st, (lib().pa_last_error() or b"").decode()
+
+
+def auto_splits(total_q, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype):
+    st = lib().pa_prefill_auto_splits(total_q, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads,
+                                      head_dim, q_dtype, kv_dtype)
+    if st < 0:
+        _check(st)
+    return st

@@ -1,0 +1,386 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI (needs an MI355X).
+
+Bars (max-abs error against the oracle): fp32 1e-5; fp16/bf16 2e-2; fp8_e5m2
+KV 5e-2 against the oracle fed the same dequantized values.  Besides the
+max-abs bar every comparison also reports max|err| / max|ref| and
+rms(err) / rms(ref), with a self-imposed bar of 1e-2 on the rms ratio for
+16-bit inputs (at long contexts the outputs are small and the absolute bar
+alone would be loose).  Bitwise checks: a decode row alone vs in a batch; page
+permutation, page size and KV layout leave outputs unchanged.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_prefill_amd import inputs as gen
+from paged_attention_prefill_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2}
+RMS_BAR = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e5m2": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ops.lib()  # raises if the library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def oracle_pools(case):
+    kind = "e5m2" if case.kv_kind == "e5m2" else "float"
+    k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, case.k_scale)
+    v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
+    return k, v
+
+
+def run_oracle(case, rows=None, pools=None):
+    k, v = pools if pools is not None else oracle_pools(case)
+    return oracle.paged_attention(gen.to_numpy64(case.q), k, v, case.cu_seqlens_q, case.seq_lens,
+                                  case.block_tables, case.scale, rows=rows)
+
+
+def gpu_prefill(case, d=None, splits=1):
+    d = d or gen.to_device(case)
+    say(f"  prefill {case.name}: total_q={case.total_q} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} P={case.page_size} splits={splits}")
+    out, lse = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], case.max_seqlen_q,
+                                 case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                                 num_kv_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def gpu_decode(case, d=None, splits=None, max_q=None):
+    d = d or gen.to_device(case)
+    splits = splits or case.num_splits
+    max_q = max_q or max(1, case.max_seqlen_q)
+    say(f"  decode {case.name}: rows={case.num_seqs} total_q={case.total_q} Hq={case.num_q_heads} "
+        f"Hkv={case.num_kv_heads} D={case.head_dim} P={case.page_size} S={splits} max_q={max_q}")
+    out, lse = ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], max_q, case.scale,
+                                   num_splits=splits, k_scale=case.k_scale, v_scale=case.v_scale,
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare(name, kind, got, ref, got_lse=None, ref_lse=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rel = mx / max(float(np.abs(ref).max()), 1e-30) if err.size else 0.0
+    rms = float(np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)) if err.size else 0.0
+    say(f"  {name}: max|err|={mx:.3e} max|err|/max|ref|={rel:.3e} rms ratio={rms:.3e} (bar {TOL[kind]})")
+    assert mx <= TOL[kind], f"{name}: max-abs error {mx} > {TOL[kind]}"
+    assert rms <= RMS_BAR[kind], f"{name}: rms ratio {rms} > {RMS_BAR[kind]}"
+    if got_lse is not None:
+        gl = np.asarray(got_lse, np.float64)
+        rl = np.asarray(ref_lse, np.float64)
+        assert (np.isfinite(gl) == np.isfinite(rl)).all(), f"{name}: lse -inf pattern differs"
+        fin = np.isfinite(rl)
+        if fin.any():
+            lerr = float(np.abs(gl[fin] - rl[fin]).max())
+            say(f"  {name}: lse max|err|={lerr:.3e}")
+            assert lerr <= max(TOL[kind], 1e-4), f"{name}: lse error {lerr}"
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+def test_tiny_fp32_prefill_all_rows():
+    c = gen.tiny_fp32()
+    ref, rl = run_oracle(c)
+    for splits in (1, 2, 16):
+        out, lse = gpu_prefill(c, splits=splits)
+        compare(f"tiny prefill S={splits}", "f32", out, ref, lse, rl)
+
+
+def test_tiny_fp32_decode_row_and_verify_row():
+    c = gen.tiny_fp32()
+    ref, rl = run_oracle(c)
+    out, lse = gpu_decode(c, splits=16, max_q=16)   # the 16-token chunk as a verify row + the q=1 row
+    compare("tiny decode (both rows)", "f32", out.cpu().numpy(), ref, lse.cpu().numpy(), rl)
+    b = gen.select_seqs(c, [1])
+    out1, lse1 = gpu_decode(b, splits=16, max_q=1)
+    compare("tiny decode row", "f32", out1.cpu().numpy(), ref[16:], lse1.cpu().numpy(), rl[16:])
+
+
+# ------------------------------------------------------------------ decode batch
+
+@pytest.fixture(scope="module")
+def decode_bf16():
+    c = gen.decode_batch(kind="bf16")
+    return c, gen.to_device(c), run_oracle(c)
+
+
+def test_decode_batch_bf16_matches_oracle(decode_bf16):
+    c, d, (ref, rl) = decode_bf16
+    out, lse = gpu_decode(c, d, splits=16)
+    compare("decode bf16 S=16", "bf16", out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
+    # the empty row (length 0) is exactly zero with lse -inf
+    z = int(np.nonzero(c.seq_lens == 0)[0][0])
+    assert not out[z].float().abs().sum().item() and torch.isinf(lse[z]).all()
+
+
+def test_decode_row_alone_equals_row_in_batch_bitwise(decode_bf16):
+    c, d, _ = decode_bf16
+    out_b, lse_b = gpu_decode(c, d, splits=16, max_q=1)
+    for b in [0, 1, 4, 5, 9, 13, 31]:
+        one = gen.select_seqs(c, [b])
+        out1, lse1 = gpu_decode(one, splits=16, max_q=1)
+        assert torch.equal(out1.view(torch.int16), out_b[b:b + 1].view(torch.int16)), f"row {b}"
+        assert torch.equal(lse1, lse_b[b:b + 1]), f"row {b} lse"
+    # and in another batch composition
+    sub = gen.select_seqs(c, [13, 5, 31])
+    out3, _ = gpu_decode(sub, splits=16, max_q=1)
+    for i, b in enumerate([13, 5, 31]):
+        assert torch.equal(out3[i].view(torch.int16), out_b[b].view(torch.int16))
+
+
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_decode_other_split_counts(decode_bf16, splits):
+    c, d, (ref, rl) = decode_bf16
+    out, lse = gpu_decode(c, d, splits=splits)
+    compare(f"decode bf16 S={splits}", "bf16", out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
+
+
+def test_decode_batch_fp32_matches_oracle():
+    c = gen.decode_batch(kind="f32")
+    ref, rl = run_oracle(c)
+    out, lse = gpu_decode(c, splits=16)
+    compare("decode f32 S=16", "f32", out.cpu().numpy(), ref, lse.cpu().numpy(), rl)
+
+
+# ------------------------------------------------------------------ varlen prefill
+
+@pytest.fixture(scope="module")
+def varlen_bf16():
+    c = gen.varlen_prefill(kind="bf16")
+    return c, gen.to_device(c), run_oracle(c)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 0])
+def test_varlen_prefill_bf16(varlen_bf16, splits):
+    c, d, (ref, rl) = varlen_bf16
+    out, lse = gpu_prefill(c, d, splits=splits)
+    compare(f"varlen bf16 S={splits}", "bf16", out, ref, lse, rl)
+
+
+def test_varlen_prefill_fp16_and_fp32():
+    for kind in ("f16", "f32"):
+        c = gen.varlen_prefill(kind=kind)
+        if kind == "f32":  # the exact-product path at a size the fp32 kernel finishes quickly
+            c = gen.select_seqs(c, [0, 1, 2])
+        ref, rl = run_oracle(c)
+        out, lse = gpu_prefill(c)
+        compare(f"varlen {kind}", kind, out, ref, lse, rl)
+
+
+def test_prefill_splits_agree_with_unsplit(varlen_bf16):
+    c, d, _ = varlen_bf16
+    o1, _ = gpu_prefill(c, d, splits=1)
+    o4, _ = gpu_prefill(c, d, splits=4)
+    assert np.abs(o1 - o4).max() < 1e-2
+
+
+# ------------------------------------------------------------------ invariants (bitwise)
+
+def _repage(case, P2, seed):
+    """Same dense K/V in another page size / permutation / layout (built on the CPU)."""
+    rng = np.random.default_rng(seed)
+    B = case.num_seqs
+    need = [-(-int(L) // P2) for L in case.seq_lens]
+    n_pages = sum(need) + 1
+    perm = rng.permutation(n_pages)
+    shape = (n_pages, P2) + tuple(case.k_pool.shape[2:])
+    k2 = torch.full(shape, float("nan"), dtype=case.k_pool.dtype)
+    v2 = torch.full(shape, float("nan"), dtype=case.v_pool.dtype)
+    bt2 = np.full((B, max(need)), perm[-1], dtype=np.int32)
+    off = 0
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        j = np.arange(L)
+        src_p = case.block_tables[b, j // case.page_size]
+        src_s = j % case.page_size
+        dst_p = perm[off + j // P2]
+        k2[torch.from_numpy(dst_p), torch.from_numpy(j % P2)] = case.k_pool[torch.from_numpy(src_p), torch.from_numpy(src_s)]
+        v2[torch.from_numpy(dst_p), torch.from_numpy(j % P2)] = case.v_pool[torch.from_numpy(src_p), torch.from_numpy(src_s)]
+        bt2[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    from dataclasses import replace
+    return replace(case, k_pool=k2, v_pool=v2, block_tables=bt2, page_size=P2)
+
+
+def test_page_size_permutation_and_layout_leave_output_bitwise_unchanged():
+    c = gen.make_case("inv", q_lens=[37, 1, 100], seq_lens=[300, 77, 700], num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, page_size=32, q_kind="f16", seed=31)
+    base, base_lse = gpu_prefill(c, splits=1)
+    dec, _ = gpu_decode(gen.select_seqs(c, [1]), splits=4, max_q=1)
+    for P2 in (16, 48, 816):
+        c2 = _repage(c, P2, seed=P2)
+        o2, l2 = gpu_prefill(c2, splits=1)
+        assert np.array_equal(o2, base) and np.array_equal(l2, base_lse), f"page {P2}"
+        d2, _ = gpu_decode(gen.select_seqs(c2, [1]), splits=4, max_q=1)
+        assert torch.equal(d2, dec)
+    # the same logical cache stored [pages, Hkv, page_size, D]
+    from dataclasses import replace
+    h = replace(c, layout="HND", k_pool=c.k_pool.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3),
+                v_pool=c.v_pool.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3))
+    assert h.k_pool.stride(2) == c.page_size * c.head_dim
+    oh, lh = gpu_prefill(h, splits=1)
+    assert np.array_equal(oh, base) and np.array_equal(lh, base_lse)
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+
+@pytest.mark.parametrize("D", [16, 64, 96, 128, 160, 256])
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_head_dims(D, kind):
+    c = gen.make_case(f"hd{D}", q_lens=[70, 3, 129], seq_lens=[70, 200, 1000], num_q_heads=6, num_kv_heads=2,
+                      head_dim=D, page_size=16, q_kind=kind, seed=D)
+    ref, rl = run_oracle(c)
+    out, lse = gpu_prefill(c)
+    compare(f"prefill {kind} D={D}", kind, out, ref, lse, rl)
+    out, lse = gpu_decode(gen.select_seqs(c, [1]), splits=5, max_q=3)
+    compare(f"decode {kind} D={D}", kind, out.float().cpu().numpy(), ref[70:73], lse.cpu().numpy(), rl[70:73])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (12, 2), (24, 4), (16, 2)])
+def test_gqa_ratios(Hq, Hkv):
+    c = gen.make_case(f"gqa{Hq}-{Hkv}", q_lens=[50, 16], seq_lens=[333, 16], num_q_heads=Hq,
+                      num_kv_heads=Hkv, head_dim=64, page_size=32, q_kind="f16", seed=Hq * 10 + Hkv)
+    ref, rl = run_oracle(c)
+    out, lse = gpu_prefill(c, splits=2)
+    compare(f"prefill gqa {Hq}/{Hkv}", "f16", out, ref, lse, rl)
+    one = gen.select_seqs(c, [1])
+    out, lse = gpu_decode(one, splits=3, max_q=16)
+    compare(f"decode gqa {Hq}/{Hkv}", "f16", out.float().cpu().numpy(), ref[50:], lse.cpu().numpy(), rl[50:])
+
+
+def test_edge_cases_empty_and_ragged():
+    # q_len > seq_len (leading rows see nothing), seq_len 0 with q > 0, q_len 0,
+    # single key, lengths just off tile and page boundaries
+    c = gen.make_case("edge", q_lens=[5, 3, 0, 1, 33, 1], seq_lens=[2, 0, 10, 1, 31, 33], num_q_heads=4,
+                      num_kv_heads=2, head_dim=64, page_size=16, q_kind="bf16", seed=41)
+    ref, rl = run_oracle(c)
+    for s in (1, 3):
+        out, lse = gpu_prefill(c, splits=s)
+        compare(f"edge prefill S={s}", "bf16", out, ref, lse, rl)
+        assert not out[:3].any() and np.isneginf(lse[:3]).all()
+        assert not out[5:8].any()
+    dec = gen.select_seqs(c, [1, 2, 3, 5])
+    out, lse = gpu_decode(dec, splits=16, max_q=3)
+    ref_d, rl_d = run_oracle(dec)
+    compare("edge decode", "bf16", out.float().cpu().numpy(), ref_d, lse.cpu().numpy(), rl_d)
+
+
+def test_peaked_scores():
+    # planted high-score keys (scale x 8): outputs are O(1), so the absolute bar is tight
+    c = gen.make_case("peaked", q_lens=[200], seq_lens=[3000], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      page_size=64, q_kind="f16", seed=51)
+    c.scale *= 8.0
+    ref, rl = run_oracle(c)
+    assert np.abs(ref).max() > 0.5
+    out, lse = gpu_prefill(c, splits=1)
+    compare("peaked prefill", "f16", out, ref, lse, rl)
+    dec = gen.select_seqs(c, [0])
+    dec.q = c.q[-4:].clone()
+    dec.cu_seqlens_q = np.array([0, 4], dtype=np.int32)
+    out, lse = gpu_decode(dec, splits=16, max_q=4)
+    compare("peaked decode", "f16", out.float().cpu().numpy(), ref[-4:], lse.cpu().numpy(), rl[-4:])
+
+
+def test_merge_states_matches_oracle_merge():
+    rng = np.random.default_rng(61)
+    N, H, S, D = 7, 3, 5, 128
+    o = rng.standard_normal((N, H, S, D))
+    l = rng.standard_normal((N, H, S)) * 3
+    l[0, 0, :] = -np.inf          # all parts empty
+    l[1, 1, 2] = -np.inf          # one empty part
+    o[1, 1, 2] = np.nan           # its output must be ignored
+    rec = np.concatenate([o, l[..., None], np.zeros((N, H, S, 1))], -1).astype(np.float32)
+    ro, rlse = oracle.merge_partials(np.moveaxis(rec[..., :D].astype(np.float64), 2, 0),
+                                     np.moveaxis(rec[..., D].astype(np.float64), 2, 0))
+    ro[1, 1] = oracle.merge_partials(np.delete(rec[1, 1, :, :D], 2, 0).astype(np.float64),
+                                     np.delete(rec[1, 1, :, D], 2, 0).astype(np.float64))[0]
+    out, lse = ops.merge_states(torch.from_numpy(rec).cuda(), torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    compare("merge f32", "f32", out.cpu().numpy(), ro)
+    assert np.isneginf(lse[0, 0].item()) and not out[0, 0].any()
+
+
+# ------------------------------------------------------------------ fp8 KV
+
+def test_fp8_prefill_and_decode_small():
+    c = gen.make_case("fp8", q_lens=[100, 5], seq_lens=[900, 2000], num_q_heads=12, num_kv_heads=2,
+                      head_dim=256, page_size=816, q_kind="f16", kv_kind="e5m2", seed=71,
+                      k_scale=0.5, v_scale=2.0)
+    ref, rl = run_oracle(c)
+    out, lse = gpu_prefill(c, splits=2)
+    compare("fp8 prefill", "e5m2", out, ref, lse, rl)
+    one = gen.select_seqs(c, [1])
+    out, lse = gpu_decode(one, splits=16, max_q=5)
+    compare("fp8 decode", "e5m2", out.float().cpu().numpy(), ref[100:], lse.cpu().numpy(), rl[100:])
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+
+def _sample_rows(case, n, seed, tokens=None):
+    rng = np.random.default_rng(seed)
+    toks = rng.integers(0, case.total_q, n) if tokens is None else np.asarray(tokens)
+    heads = rng.integers(0, case.num_q_heads, len(toks))
+    # always include the first and last rows of every sequence
+    extra = []
+    for b in range(case.num_seqs):
+        t0, t1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
+        if t1 > t0:
+            extra += [(t0, 0), (t1 - 1, case.num_q_heads - 1)]
+    rows = np.concatenate([np.stack([toks, heads], 1), np.array(extra, dtype=np.int64).reshape(-1, 2)])
+    return rows
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_long_chunk_prefill_sampled(splits):
+    c = gen.long_chunk()
+    pre = gen.select_seqs(c, [0])
+    d = gen.to_device(pre)
+    out, lse = gpu_prefill(pre, d, splits=splits)
+    rows = _sample_rows(pre, 48, seed=splits)
+    k, v = oracle_pools(pre)
+    ref, rl = run_oracle(pre, rows=rows, pools=(k, v))
+    compare(f"long chunk S={splits} (sampled {len(rows)})", "f16", out[rows[:, 0], rows[:, 1]], ref,
+            lse[rows[:, 0], rows[:, 1]], rl)
+    # the q=1 decode row over the same cache
+    dec = gen.select_seqs(c, [1])
+    od, ld = gpu_decode(dec, splits=64, max_q=1)
+    rd, rld = run_oracle(dec, pools=(k, v))
+    compare("long chunk decode row", "f16", od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
+
+
+@pytest.mark.parametrize("kv_kind", ["f16", "e5m2"])
+def test_mixed_step_sampled(kv_kind):
+    c = gen.mixed_step(kv_kind=kv_kind)
+    k, v = oracle_pools(c)
+    ver = gen.select_seqs(c, [0])
+    od, ld = gpu_decode(ver, splits=128, max_q=5)
+    rd, rld = run_oracle(ver, pools=(k, v))
+    compare(f"mixed verify row {kv_kind}", kv_kind, od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
+    chunk = gen.select_seqs(c, [1])
+    out, lse = gpu_prefill(chunk, splits=0)
+    rows = _sample_rows(chunk, 32, seed=5)
+    ref, rl = run_oracle(chunk, rows=rows, pools=(k, v))
+    compare(f"mixed chunk {kv_kind} (sampled {len(rows)})", kv_kind, out[rows[:, 0], rows[:, 1]], ref,
+            lse[rows[:, 0], rows[:, 1]], rl)
