@@ -146,10 +146,12 @@ int pa_split_kv_decode(const void *q, int32_t q_dtype, void *out, float *lse,
  * "Purpose", Decode: the second kernel).
  *   partials [num_tokens, num_heads, num_splits, head_dim + 2] float32, record =
  *   (o_s normalised, lse_s, pad).  For every (token, head): M = max_s lse_s,
- *   w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s (ascending s),
- *   lse = M + log(sum_s w_s); all parts empty (lse = -inf) gives o = 0,
- *   lse = -inf.  out [num_tokens, num_heads, head_dim] in out_dtype (F32, F16,
- *   BF16); out_lse nullable.  o_s of an empty part is ignored.
+ *   w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log(sum_s
+ *   w_s), summed in a fixed order that depends only on num_splits and
+ *   head_dim; all parts empty (lse = -inf) gives o = 0, lse = -inf.
+ *   out [num_tokens, num_heads, head_dim] in out_dtype (F32, F16, BF16);
+ *   out_lse nullable.  o_s of an empty part is ignored.  head_dim must be
+ *   even and <= 256; partials 8-byte aligned.
  */
 int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_tokens,
                     int32_t num_heads, int32_t head_dim, void *out, int32_t out_dtype,

@@ -109,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   const int lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, r32 = lane & 31;
 
-  int w = xcd_remap(blockIdx.x, gridDim.x);
+  int w = xcd_remap(blockIdx.x);
+  if (w >= p.num_work) return;
   const int qtile = w % p.qtiles;
   w /= p.qtiles;
   const int split = w % p.num_splits;

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  int w = xcd_remap(blockIdx.x, gridDim.x);
+  int w = xcd_remap(blockIdx.x);
+  if (w >= p.num_work) return;
   const int qtile = w % p.qtiles;
   w /= p.qtiles;
   const int split = w % p.num_splits;

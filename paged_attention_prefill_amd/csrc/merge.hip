@@ -2,81 +2,96 @@
 // (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode; also the log-sum-exp
 // merge of key-split prefill tiles, 1CatAI/1Cat-vLLM PR #1279, commit 5).
 //
-// One wave per (token, head).  Record s = (o_s[0..D), lse_s, pad) with o_s
-// normalised.  M = max_s lse_s; w_s = exp(lse_s - M); o = sum_s w_s o_s /
-// sum_s w_s, summed in ascending s for every output column, so a row's result
-// depends only on its own records (batch invariance).  All parts empty ->
-// o = 0, lse = -inf.
+// One work group of 256 threads per (token, head).  Record s = (o_s[0..D),
+// lse_s, pad) with o_s normalised.  M = max_s lse_s; w_s = exp(lse_s - M);
+// o = sum_s w_s o_s / sum_s w_s; lse = M + log sum_s w_s.  All parts empty ->
+// o = 0, lse = -inf; an empty part's o_s is never read into the sum.
+//
+// Thread t owns a pair of output columns (t % (D/2)) and a contiguous run of
+// parts (t / (D/2)); the runs are summed in ascending part order and then
+// combined in ascending run order.  The order depends only on S and D, so a
+// row's result does not depend on the other rows of the call (batch
+// invariance), and the many parts of a long decode row are read in parallel.
 
 #include "pa_common.h"
 
 namespace pa {
 
 namespace {
-constexpr int kMergeWaves = 4;
+constexpr int kMT = 256;
 constexpr float kNegInfM = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename OT> __device__ __forceinline__ void put(OT* p, float v) { *p = (OT)v; }
+template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, float b) {
+  p[0] = (OT)a;
+  p[1] = (OT)b;
+}
 }  // namespace
 
-template <typename OT, int NCOL>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials,
-                                                                 int S, int ntok, int H, int D,
-                                                                 OT* __restrict__ out,
-                                                                 float* __restrict__ out_lse) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (row >= (int64_t)ntok * H) return;
+template <typename OT>
+__global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ partials, int S, int D,
+                                                    OT* __restrict__ out, float* __restrict__ out_lse) {
+  __shared__ float red[kMT / 64];
+  __shared__ float2 part[kMT];
+  __shared__ float dpart[kMT];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t row = blockIdx.x;
   const int R = D + 2;
   const float* rec = partials + row * (int64_t)S * R;
 
+  // M = max_s lse_s
   float M = kNegInfM;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, rec[(int64_t)s * R + D]);
+  for (int s = t; s < S; s += kMT) M = fmaxf(M, rec[(int64_t)s * R + D]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-  float acc[NCOL];
-#pragma unroll
-  for (int c = 0; c < NCOL; ++c) acc[c] = 0.0f;
-  float den = 0.0f;
-  if (M != kNegInfM) {
-    for (int s = 0; s < S; ++s) {
+  const int DC = D >> 1;                 // float2 column pairs
+  const int SG = kMT / DC;               // runs of parts (>= 1 since D <= 256... D/2 <= 128)
+  const int dc = t % DC, sg = t / DC;
+  const int per = (S + SG - 1) / SG;
+  const int s0 = sg * per, s1 = min(S, s0 + per);
+  float ax = 0.0f, ay = 0.0f, den = 0.0f;
+  if (M != kNegInfM && sg < SG) {
+#pragma unroll 4
+    for (int s = s0; s < s1; ++s) {
       const float* r = rec + (int64_t)s * R;
       const float ls = r[D];
-      if (ls == kNegInfM) continue;  // empty part: contributes nothing
-      const float ws = exp2f((ls - M) * kLog2e);
+      const float2 v = *(const float2*)(r + 2 * dc);
+      const bool live = ls != kNegInfM;
+      const float ws = live ? exp2f((ls - M) * kLog2e) : 0.0f;
+      ax = live ? fmaf(ws, v.x, ax) : ax;
+      ay = live ? fmaf(ws, v.y, ay) : ay;
       den += ws;
-#pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        const int d = lane + 64 * c;
-        if (d < D) acc[c] = fmaf(ws, r[d], acc[c]);
-      }
     }
   }
-  const bool empty = M == kNegInfM || !(den > 0.0f);
-  const float inv = empty ? 0.0f : 1.0f / den;
-  OT* orow = out + row * D;
-#pragma unroll
-  for (int c = 0; c < NCOL; ++c) {
-    const int d = lane + 64 * c;
-    if (d < D) put<OT>(orow + d, acc[c] * inv);
+  part[t] = make_float2(ax, ay);
+  dpart[t] = den;
+  __syncthreads();
+  if (t < DC) {
+    float sx = 0.0f, sy = 0.0f, sd = 0.0f;
+    for (int gI = 0; gI < SG; ++gI) {
+      const float2 v = part[gI * DC + t];
+      sx += v.x;
+      sy += v.y;
+      sd += dpart[gI * DC];  // every thread of a run holds the same den
+    }
+    const bool empty = M == kNegInfM || !(sd > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / sd;
+    put2<OT>(out + row * D + 2 * t, sx * inv, sy * inv);
+    if (out_lse != nullptr && t == 0) out_lse[row] = empty ? kNegInfM : M + logf(sd);
   }
-  if (out_lse != nullptr && lane == 0) out_lse[row] = empty ? kNegInfM : M + logf(den);
 }
 
 template <typename OT>
-static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out,
-                           float* out_lse, hipStream_t stream) {
+static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out, float* out_lse,
+                           hipStream_t stream) {
   const int64_t rows = (int64_t)ntok * H;
-  const int nblk = (int)((rows + kMergeWaves - 1) / kMergeWaves);
-  if (nblk == 0) return hipSuccess;
-  if (D <= 64)
-    hipLaunchKernelGGL((merge_kernel<OT, 1>), dim3(nblk), dim3(64 * kMergeWaves), 0, stream, partials, S, ntok, H, D, (OT*)out, out_lse);
-  else if (D <= 128)
-    hipLaunchKernelGGL((merge_kernel<OT, 2>), dim3(nblk), dim3(64 * kMergeWaves), 0, stream, partials, S, ntok, H, D, (OT*)out, out_lse);
-  else
-    hipLaunchKernelGGL((merge_kernel<OT, 4>), dim3(nblk), dim3(64 * kMergeWaves), 0, stream, partials, S, ntok, H, D, (OT*)out, out_lse);
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((merge_kernel<OT>), dim3((unsigned)rows), dim3(kMT), 0, stream, partials, S, D, (OT*)out,
+                     out_lse);
   return hipGetLastError();
 }
 

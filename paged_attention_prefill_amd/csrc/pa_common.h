@@ -33,18 +33,22 @@ struct AttnParams {
   int num_splits;
   int write_partial;       // 1: records to `partial`; 0: final out/lse
   int qtiles;              // q tiles per (sequence, kv head) in the grid
+  int num_work;            // work items (the grid is padded beyond it)
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;
 };
 
-// Block index -> work index so that consecutive work items run on the same XCD.
-// Work groups are handed to the 8 XCDs round robin; this is a bijection on
-// [0, n) whatever the real placement is, so it only affects locality.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n / 8, rem = n % 8;
-  const int xcd = bid % 8, local = bid / 8;
-  const int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  return base + local;
+// Block index -> work index.  Work groups are handed to the 8 XCDs round
+// robin; runs of kXcdGroup consecutive work items (neighbouring query tiles of
+// one sequence, kv head and key part, which read the same K/V) are kept on one
+// XCD so that they share its L2, and successive runs go to successive XCDs so
+// that every XCD gets a share of every sequence.  The grid is padded to a
+// multiple of 8 * kXcdGroup; the mapping is a bijection on the padded range
+// whatever the real placement is, so it only affects locality.
+constexpr int kXcdGroup = 16;
+__device__ __forceinline__ int xcd_remap(int bid) {
+  const int xcd = bid & 7, k = bid >> 3;
+  return ((k / kXcdGroup) * 8 + xcd) * kXcdGroup + (k % kXcdGroup);
 }
 
 // Key range [lo, hi) of part `s` of a row with L keys cut into S parts of

@@ -21,6 +21,9 @@ hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dp
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
                         float* out_lse, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
+hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
+hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
+int mfma_dma_rows(int dpad);
 int mfma_rows_per_group();
 int valu_rows_per_group();
 }  // namespace pa
@@ -104,6 +107,8 @@ int check_kv(const pa_kv_cache* kv, int q_dtype, int hq) {
   for (int i = 0; i < 3; ++i)
     if (st3[i] <= 0 || (st3[i] * es) % 16 != 0)
       return fail(PA_ERR_INVALID_ARGUMENT, "KV strides must be positive and 16-byte multiples");
+  if (kv->stride_token * es * 32 >= ((int64_t)1 << 31))
+    return fail(PA_ERR_UNSUPPORTED, "stride_token too large (32 slots must span < 2 GiB)");
   if (!std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
     return fail(PA_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be finite");
   if (kv->dtype != PA_FP8_E5M2 && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
@@ -145,6 +150,19 @@ int auto_splits(int64_t active_groups, int slots) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Which pass-1 kernel serves a dtype pair: fp32 -> exact-product VALU kernel;
+// fp16/bf16 with same-dtype KV -> MFMA kernel with the LDS DMA pipeline;
+// fp16 q with fp8_e5m2 KV -> MFMA kernel with register-staged dequant.
+enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
+KernelKind kernel_for(int q_dtype, int kv_dtype) {
+  if (q_dtype == PA_F32) return K_VALU;
+  if (kv_dtype == PA_FP8_E5M2) return K_REGSTAGE;
+  return K_DMA;
+}
+int rows_for(KernelKind k, int dpad) {
+  return k == K_VALU ? pa::valu_rows_per_group() : k == K_DMA ? pa::mfma_dma_rows(dpad) : pa::mfma_rows_per_group();
+}
 
 }  // namespace
 
@@ -223,16 +241,16 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   if (st != PA_OK) return fail(st, "%s", reason);
   if (total_q <= 0 || num_seqs <= 0) return 1;
   const int g = num_q_heads / num_kv_heads;
-  const bool valu = q_dtype == PA_F32;
-  const int rows = valu ? pa::valu_rows_per_group() : pa::mfma_rows_per_group();
+  const KernelKind kk = kernel_for(q_dtype, kv_dtype);
+  const int rows = rows_for(kk, dpad_of(head_dim));
   int cus = 0;
   st = device_cus(&cus);
   if (st != PA_OK) return st;
   int occ = 1;
-  if (!valu) {
-    if (pa::mfma_occupancy(kind_of(q_dtype), kind_of(kv_dtype), dpad_of(head_dim), &occ) != hipSuccess || occ < 1)
-      occ = 1;
-  }
+  hipError_t oe = hipSuccess;
+  if (kk == K_DMA) oe = pa::mfma_dma_occupancy(kind_of(q_dtype), dpad_of(head_dim), &occ);
+  else if (kk == K_REGSTAGE) oe = pa::mfma_occupancy(kind_of(q_dtype), kind_of(kv_dtype), dpad_of(head_dim), &occ);
+  if (oe != hipSuccess || occ < 1) occ = 1;
   const int64_t tiles_grid = ceil_div((int64_t)max_seqlen_q * g, rows) * num_seqs;
   const int64_t tiles_est = ceil_div((int64_t)total_q * g, rows) + num_seqs - 1;
   const int64_t active = (tiles_grid < tiles_est ? tiles_grid : tiles_est) * num_kv_heads;
@@ -245,12 +263,14 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
                          int splits, bool always_partial, void* workspace, size_t ws_bytes,
                          hipStream_t stream) {
   const int g = hq / kv->num_kv_heads;
-  const bool valu = q_dtype == PA_F32;
-  const int rows = valu ? pa::valu_rows_per_group() : pa::mfma_rows_per_group();
+  const KernelKind kind = kernel_for(q_dtype, kv->dtype);
+  const int rows = rows_for(kind, dpad_of(kv->head_dim));
   const int qtiles = (int)ceil_div((int64_t)max_q * g, rows);
-  const int64_t nblocks = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
-  if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nblocks);
-  if (nblocks == 0 || total_q == 0) return ok();
+  const int64_t nwork = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
+  const int64_t pad = 8 * pa::kXcdGroup;
+  const int64_t nblocks = (nwork + pad - 1) / pad * pad;
+  if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nwork);
+  if (nwork == 0 || total_q == 0) return ok();
   const bool partial = always_partial || splits > 1;
 
   pa::AttnParams p;
@@ -276,12 +296,14 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.num_splits = splits;
   p.write_partial = partial ? 1 : 0;
   p.qtiles = qtiles;
+  p.num_work = (int)nwork;
   p.scale_log2 = scale * (kv->dtype == PA_FP8_E5M2 ? kv->k_scale : 1.0f) * 1.4426950408889634f;
   p.v_scale = kv->dtype == PA_FP8_E5M2 ? kv->v_scale : 1.0f;
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
-  hipError_t e = valu ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
-                      : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
+  hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
+                 : kind == K_DMA ? pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream)
+                                 : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial) {
     e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, stream);
@@ -358,13 +380,15 @@ int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, co
 
 int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,
                     int32_t head_dim, void* out, int32_t out_dtype, float* out_lse, void* stream) {
-  if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 1 || head_dim > 256)
-    return fail(PA_ERR_INVALID_ARGUMENT, "bad merge sizes");
+  if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 2 || head_dim > 256 || head_dim % 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad merge sizes (head_dim must be even, <= 256)");
   if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "merge output dtype must be F32, F16 or BF16");
   if (num_tokens == 0) return ok();
   if (!partials || !out) return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31) * 4)
+  if (((uintptr_t)partials & 7u) || ((uintptr_t)out & 3u))
+    return fail(PA_ERR_INVALID_ARGUMENT, "partials must be 8-byte and out 4-byte aligned");
+  if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
     return fail(PA_ERR_UNSUPPORTED, "too many rows");
   hipError_t e = pa::launch_merge(partials, num_splits, num_tokens, num_heads, head_dim, out, kind_of(out_dtype),
                                   out_lse, (hipStream_t)stream);
