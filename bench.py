@@ -154,6 +154,20 @@ def cpu_baseline(case, budget_rows, seed=0):
             "seconds": dt}
 
 
+def copy_reference(steps):
+    """A plain device copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                      "launches": steps}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +177,9 @@ def main():
     ap.add_argument("--prefill-splits", default=None, help="override: 0 = auto, or a count")
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="query tokens in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=400, help="query tokens in the oracle sample")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters")
     a = ap.parse_args()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -171,6 +187,8 @@ def main():
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if a.mode == "copy":
+        return copy_reference(a.steps)
     ops.lib()
 
     log(f"building workload {a.workload} ...")

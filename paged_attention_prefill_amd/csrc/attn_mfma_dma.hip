@@ -49,6 +49,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Work-group barrier for the LDS ring.  __syncthreads() also waits for every
+// outstanding vector-memory load (vmcnt(0)), which would drain the tile loads
+// still in flight; here each wave has already waited for its own loads of the
+// tile about to be read, so only LDS traffic has to settle before s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // XOR swizzles of the 16-byte chunks of a key row (chunk c of key `key` lives
 // in slot swz(key, c)); chosen so that the MFMA operand reads are free of LDS
 // bank conflicts.  Both are involutions.
@@ -89,9 +97,11 @@ template <> struct Mf<__bf16> {
 
 }  // namespace
 
-template <typename QT, int DPAD, int WAVES, int NST>
-__global__ __launch_bounds__(64 * WAVES, (DPAD <= 128 ? 2 : 1)) void attn_mfma_dma_kernel(const AttnParams p) {
-  constexpr int ROWS = 32 * WAVES;
+template <typename QT, int DPAD, int WAVES, int RB, int NST>
+__global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void attn_mfma_dma_kernel(
+    const AttnParams p) {
+  constexpr int WROWS = 32 * RB;                // query rows per wave (RB blocks of 32)
+  constexpr int ROWS = WROWS * WAVES;
   constexpr int CPK = DPAD / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = CPK * 16;                // bytes per key row in LDS
   constexpr int TILE_BYTES = kKT * ROWB;        // one K (or V) tile
@@ -100,9 +110,12 @@ __global__ __launch_bounds__(64 * WAVES, (DPAD <= 128 ? 2 : 1)) void attn_mfma_d
   static_assert(INSTR % WAVES == 0, "DMA instructions must split evenly over the waves");
   constexpr int LPW = INSTR / WAVES;            // DMA instructions per wave per tile
   constexpr int HALF = INSTR / 2;               // instructions per region (K or V)
+  constexpr int KPI = 64 / CPK;                 // keys per DMA instruction
   constexpr int NKK = DPAD / 16;
   constexpr int NDB = DPAD / 32;
   static_assert((NST - 2) * LPW <= 63, "vmcnt range");
+  static_assert(NST <= 5, "wait ladder covers up to 4 tiles ahead");
+  static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
 
@@ -130,139 +143,181 @@ __global__ __launch_bounds__(64 * WAVES, (DPAD <= 128 ? 2 : 1)) void attn_mfma_d
   int klo, khi;
   split_range(L, p.num_splits, split, klo, khi);
 
-  const int prow = row0 + wave * 32 + r32;
-  const bool valid = prow < nrows;
-  const int tok = valid ? prow / g : 0;
-  const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
-  const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
   const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
-  const int wrow_first = row0 + wave * 32;
-  const bool wave_active = wrow_first < nrows;
-  const int wave_kend = wave_active ? min(khi, L - qlen + (min(wrow_first + 32, nrows) - 1) / g + 1) : 0;
+  const int wrow0 = row0 + wave * WROWS;
+  const bool wave_active = wrow0 < nrows;
+  const int wave_kend = wave_active ? min(khi, L - qlen + (min(wrow0 + WROWS, nrows) - 1) / g + 1) : 0;
 
-  // ---- Q^T fragments (B operand): lane holds row r32, d = 16 kk + 8 hi .. +7
-  uint4 qf[NKK];
-  {
-    const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
+  // ---- this lane's rows (one per block) and their Q^T fragments (B operand):
+  // lane holds row r32 of each block, d = 16 kk + 8 hi .. +7
+  bool valid[RB], rb_on[RB];
+  int tok[RB], hq[RB], lim[RB];
+  uint4 qf[RB][NKK];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int prow = wrow0 + rb * 32 + r32;
+    valid[rb] = prow < nrows;
+    rb_on[rb] = wrow0 + rb * 32 < nrows;
+    tok[rb] = valid[rb] ? prow / g : 0;
+    hq[rb] = kvh * g + (valid[rb] ? prow - (prow / g) * g : 0);
+    lim[rb] = valid[rb] ? min(L - qlen + tok[rb] + 1, khi) : 0;
+    const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb]) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int d = kk * 16 + hi * 8;
-      qf[kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
+      qf[rb][kk] = (valid[rb] && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
     }
   }
 
-  f32x16_t oacc[NDB];
+  f32x16_t oacc[RB][NDB];
+  float m[RB], lsum[RB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = (f32x16_t)(0.0f);
-  float m = kNegInf, lsum = 0.0f;
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    lsum[rb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[rb][db] = (f32x16_t)(0.0f);
+  }
 
   const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
   const int P = p.page_size;
   const int* bt = p.block_tables + (int64_t)seq * p.max_pages;
-  const int64_t sp_b = p.stride_page * 2, st_b = p.stride_token * 2;
+  const int64_t sp_b = p.stride_page * 2;
+  const int st_b = (int)(p.stride_token * 2);  // 32 keys * stride fits in 32 bits (checked on the host)
   const char* kbase = (const char*)p.k_pages + (int64_t)kvh * p.stride_head * 2;
   const char* vbase = (const char*)p.v_pages + (int64_t)kvh * p.stride_head * 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(&smem[0]);
   const int dchunks = p.head_dim >> 3;
 
-  // ---- per-lane DMA roles (loop invariant): key, chunk offset, LDS slot
-  int dkey[LPW];
-  int doff[LPW];  // bytes; 32 keys * stride_token fits in 32 bits (checked on the host)
-  const char* dbase[LPW];
-  uint32_t dlds[LPW];
+  // ---- per-lane DMA roles (loop invariant): byte offset of (key, chunk) in a tile
+  const int lkey = lane / CPK, lpos = lane % CPK;
+  int doff[LPW];
 #pragma unroll
   for (int n = 0; n < LPW; ++n) {
     const int inst = wave * LPW + n;
     const int region = inst / HALF;  // 0: K, 1: V (wave-uniform)
     const int ri = inst - region * HALF;
-    const int slot = ri * 64 + lane;
-    const int key = slot / CPK, pos = slot % CPK;
-    int c = region == 0 ? swz_k<DPAD>(key, pos) : swz_v<DPAD>(key, pos);
+    const int key = ri * KPI + lkey;
+    int c = region == 0 ? swz_k<DPAD>(key, lpos) : swz_v<DPAD>(key, lpos);
     c = c < dchunks ? c : dchunks - 1;  // head_dim < DPAD: any finite data (multiplied by 0 / discarded)
-    dkey[n] = key;
-    doff[n] = key * (int)st_b + c * 16;
-    dbase[n] = region == 0 ? kbase : vbase;
-    dlds[n] = lds0 + region * TILE_BYTES + ri * 1024;
+    doff[n] = key * st_b + c * 16;
   }
 
+  // Page ids are read through the constant address space at a uniform index,
+  // i.e. with scalar loads: they are tracked by lgkmcnt, so waiting for one
+  // never drains the tile loads in flight (which a vector load's vmcnt wait
+  // would).
+  const int pg0 = klo / P;
+  const __attribute__((address_space(4))) int* btc = (const __attribute__((address_space(4))) int*)bt;
+  auto page_id = [&](int pg) -> int { return btc[__builtin_amdgcn_readfirstlane(pg)]; };
+
   // running page position of the next tile to issue
-  int nx_pg = klo / P, nx_off = klo - (klo / P) * P;
+  int nx_pg = pg0, nx_off = klo - pg0 * P;
   auto issue = [&](int it, int stage) {
     const int j0 = klo + it * kKT;
     const int pg = nx_pg, off = nx_off;
     nx_off += kKT;
     while (nx_off >= P) nx_off -= P, ++nx_pg;
     const int first_n = P - off;
-    const int page_a = bt[pg];
-    const int page_b = (first_n < kKT && (pg + 1) * P < kend) ? bt[pg + 1] : page_a;
+    const int page_a = page_id(pg);
+    const int page_b = (first_n < kKT && (pg + 1) * P < kend) ? page_id(pg + 1) : page_a;
     const int64_t A = (int64_t)page_a * sp_b + (int64_t)off * st_b;
     const int64_t B = (int64_t)page_b * sp_b - (int64_t)first_n * st_b;
     const int lastkey = kend - 1 - j0;
-    const uint32_t sbase = stage * STAGE_BYTES;
+    const uint32_t sbase = lds0 + stage * STAGE_BYTES;
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
-      int key = dkey[n];
+      const int inst = wave * LPW + n;
+      const int region = inst / HALF;
+      const int ri = inst - region * HALF;
+      int key = ri * KPI + lkey;
       int o = doff[n];
       if (key > lastkey) {  // past the work group's last key: reload a valid key (finite data, masked)
-        o += (lastkey - key) * (int)st_b;
+        o += (lastkey - key) * st_b;
         key = lastkey;
       }
-      dma16(dbase[n] + (key < first_n ? A : B) + o, dlds[n] + sbase);
+      dma16((region == 0 ? kbase : vbase) + (key < first_n ? A : B) + o,
+            sbase + region * TILE_BYTES + ri * 1024);
     }
   };
 
-  // ---- per-lane LDS read offsets (loop invariant)
+  // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
+  // is an XOR of a lane constant with the loop index on bits that do not
+  // overlap the row and stage parts of the address, so each read costs one XOR.
   const int sk = DPAD >= 128 ? (r32 & 15) : ((r32 >> 1) & 7);
-  const int krow = r32 * ROWB;
+  const uint32_t klane = r32 * ROWB + (((uint32_t)(hi ^ sk)) << 4);
   const int tg = lane >> 4, tk = lane & 15;
   const int vkey = 4 * hi + (tk >> 2);
   const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
   const int vcl = 2 * (tg & 1) + ((tk & 3) >> 1);
-  const int vrow = vkey * ROWB + 8 * (tk & 1);
+  const uint32_t vlane = TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
 
-  auto compute = [&](int stage, int j0) {
-    if (!wave_active || j0 >= wave_kend) return;
-    const char* kt = smem + stage * STAGE_BYTES;
-    const char* vt = kt + TILE_BYTES;
-    f32x16_t s = (f32x16_t)(0.0f);
+  uint4 pf[RB][2];  // P of the last tile whose softmax ran (kept across iterations by the late group)
+
+  // S^T = K Q^T for this wave's rows, scale + mask, online softmax -> pf
+  auto qk_softmax = [&](int stage, int j0) {
+    const uint32_t kls = stage * STAGE_BYTES + klane;
+    f32x16_t s[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb] = (f32x16_t)(0.0f);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 a = *(const uint4*)(kt + krow + (((2 * kk + hi) ^ sk) << 4));
-      s = Mf<QT>::run(a, qf[kk], s);
-    }
-    float tmax = kNegInf;
+      const uint4 a = *(const uint4*)(smem + (kls ^ (kk << 5)));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = key < lim ? s[r] * p.scale_log2 : kNegInf;
-      s[r] = v;
-      tmax = fmaxf(tmax, v);
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb]) s[rb] = Mf<QT>::run(a, qf[rb][kk], s[rb]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__any(tmax > m + kTau)) {
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
-      lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m = mnew;
-    }
-    const float mref = m == kNegInf ? 0.0f : m;
-    uint4 pf[2];
-    uint32_t* pw = (uint32_t*)pf;
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = kNegInf;
+      if (__any(j0 + kKT > lim[rb])) {  // causal diagonal / key-range end inside this tile
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float e0 = fast_exp2(s[r] - mref), e1 = fast_exp2(s[r + 1] - mref);
-      lsum += e0 + e1;
-      pw[r >> 1] = Mf<QT>::pack2(e0, e1);
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float v = key < lim[rb] ? s[rb][r] * p.scale_log2 : kNegInf;
+          s[rb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = s[rb][r] * p.scale_log2;
+          s[rb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (__any(tmax > m[rb] + kTau)) {
+        const float mnew = fmaxf(m[rb], tmax);
+        const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[rb] - mnew);
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[rb][db] *= alpha;
+        m[rb] = mnew;
+      }
+      const float mref = m[rb] == kNegInf ? 0.0f : m[rb];
+      uint32_t* pw = (uint32_t*)pf[rb];
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = fast_exp2(s[rb][r] - mref), e1 = fast_exp2(s[rb][r + 1] - mref);
+        ls += e0 + e1;
+        pw[r >> 1] = Mf<QT>::pack2(e0, e1);
+      }
+      lsum[rb] += ls;
     }
+  };
+
+  // O^T += V^T P^T with the P of the tile in `stage`
+  auto pv = [&](int stage) {
+    const uint32_t vls = stage * STAGE_BYTES + vlane;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int coff = ((((4 * db) ^ sv) + vcl) << 4);
+      const uint32_t va = vls ^ (db << 6);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const char* a0 = vt + vrow + ks * 16 * ROWB + coff;
+        const char* a0 = smem + va + ks * 16 * ROWB;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a0);
         const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a0 + 8 * ROWB));
         uint4 a;
@@ -270,19 +325,39 @@ __global__ __launch_bounds__(64 * WAVES, (DPAD <= 128 ? 2 : 1)) void attn_mfma_d
         a.y = __builtin_bit_cast(uint2, lo).y;
         a.z = __builtin_bit_cast(uint2, hi4).x;
         a.w = __builtin_bit_cast(uint2, hi4).y;
-        oacc[db] = Mf<QT>::run(a, pf[ks], oacc[db]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb_on[rb]) oacc[rb][db] = Mf<QT>::run(a, pf[rb][ks], oacc[rb][db]);
       }
     }
   };
 
+  // Ping-pong (two waves per SIMD): the late wave group runs each tile's PV
+  // one iteration after its softmax, so one group's softmax overlaps the
+  // other group's MFMAs.  Tiles are then read up to one iteration after their
+  // barrier, so the loads run DIST = NST - 2 tiles ahead instead of NST - 1.
+  constexpr bool PP = (WAVES == 8);
+  constexpr int DIST = PP ? NST - 2 : NST - 1;
+  const bool late = PP && wave >= WAVES / 2;
+
+  // Every load the compiler can see (Q fragments, metadata) completes here, so
+  // that it places no vmcnt wait inside the loop: such a wait would also drain
+  // the tile loads in flight, which the compiler does not track.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
   int issued = 0;
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i)
+  for (int i = 0; i < DIST; ++i)
     if (issued < ntiles) issue(issued, issued), ++issued;
 
   for (int it = 0; it < ntiles; ++it) {
     const int ahead = issued - it - 1;  // tiles issued after this one
-    if constexpr (NST >= 4) {
+    if constexpr (DIST >= 4) {
+      if (ahead >= 3) wait_vmcnt<3 * LPW>();
+      else if (ahead == 2) wait_vmcnt<2 * LPW>();
+      else if (ahead == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (DIST == 3) {
       if (ahead >= 2) wait_vmcnt<2 * LPW>();
       else if (ahead == 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
@@ -290,124 +365,140 @@ __global__ __launch_bounds__(64 * WAVES, (DPAD <= 128 ? 2 : 1)) void attn_mfma_d
       if (ahead >= 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
     }
-    __syncthreads();
+    lds_barrier();
     if (issued < ntiles) issue(issued, issued % NST), ++issued;
-    compute(it % NST, klo + it * kKT);
+    const int j0 = klo + it * kKT;
+    const bool live = wave_active && j0 < wave_kend;
+    if (late && it > 0 && wave_active && j0 - kKT < wave_kend) pv((it - 1) % NST);
+    if (live) qk_softmax(it % NST, j0);
+    if (!late && live) pv(it % NST);
   }
+  if (late && ntiles > 0 && wave_active && klo + (ntiles - 1) * kKT < wave_kend) pv((ntiles - 1) % NST);
 
   // ---- epilogue
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (!valid) return;
-  const bool empty = (m == kNegInf) || !(ltot > 0.0f);
-  const float inv = empty ? 0.0f : p.v_scale / ltot;
-  const float lse_nat = empty ? kNegInf : (m + __log2f(ltot)) * 0.69314718055994530942f;
-  const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
-  if (p.write_partial) {
-    float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+    if (!valid[rb]) continue;
+    const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
+    const float inv = empty ? 0.0f : p.v_scale / ltot;
+    const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
+    const int64_t rowidx = (int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb];
+    if (p.write_partial) {
+      float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = db * 32 + 8 * rr + 4 * hi;
-        if (d < p.head_dim) {
-          float2 a = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv};
-          float2 b = {oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
-          *(float2*)(rec + d) = a;
-          *(float2*)(rec + d + 2) = b;
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = db * 32 + 8 * rr + 4 * hi;
+          if (d < p.head_dim) {
+            float2 a = {oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv};
+            float2 b = {oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv};
+            *(float2*)(rec + d) = a;
+            *(float2*)(rec + d + 2) = b;
+          }
         }
       }
-    }
-    if (hi == 0) {
-      float2 t = {lse_nat, 0.0f};
-      *(float2*)(rec + p.head_dim) = t;
-    }
-  } else {
-    QT* orow = (QT*)p.out + rowidx * p.head_dim;
+      if (hi == 0) {
+        float2 t = {lse_nat, 0.0f};
+        *(float2*)(rec + p.head_dim) = t;
+      }
+    } else {
+      QT* orow = (QT*)p.out + rowidx * p.head_dim;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = db * 32 + 8 * rr + 4 * hi;
-        if (d < p.head_dim) {
-          uint2 v = {Mf<QT>::pack2(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
-                     Mf<QT>::pack2(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
-          *(uint2*)(orow + d) = v;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = db * 32 + 8 * rr + 4 * hi;
+          if (d < p.head_dim) {
+            uint2 v = {Mf<QT>::pack2(oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv),
+                       Mf<QT>::pack2(oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv)};
+            *(uint2*)(orow + d) = v;
+          }
         }
       }
+      if (p.lse != nullptr && hi == 0) p.lse[rowidx] = lse_nat;
     }
-    if (p.lse != nullptr && hi == 0) p.lse[rowidx] = lse_nat;
   }
 }
 
 // ---- host side -------------------------------------------------------------
 
 namespace {
-struct DmaCfg {
-  int waves, nst;
-};
-// Work-group shape per head-dim bucket (tuning knob while measuring).
-int d256_waves() {
-  static int w = [] {
-    const char* e = getenv("PA_TUNE_D256_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
+// Work-group shapes (waves, row blocks per wave, stages), by head-dim bucket.
+// A tuning knob picks among the compiled shapes while measuring.
+int tune_cfg() {
+  static int c = [] {
+    const char* e = getenv("PA_TUNE_CFG");
+    return e ? atoi(e) : 0;
   }();
-  return w;
+  return c;
 }
-DmaCfg dma_cfg(int dpad) {
-  switch (dpad) {
-    case 64: return {4, 4};
-    case 128: return {4, 4};
-    default: return {d256_waves(), 4};
+
+template <typename QT, int DPAD, int WAVES, int RB, int NST>
+struct Cfg {
+  static hipError_t launch(const AttnParams& p, int nblocks, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST>), dim3(nblocks), dim3(64 * WAVES), 0, stream,
+                       p);
+    return hipGetLastError();
   }
-}
-
-template <typename QT, int DPAD, int WAVES, int NST>
-hipError_t launch_cfg(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_mfma_dma_kernel<QT, DPAD, WAVES, NST>), dim3(nblocks), dim3(64 * WAVES), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <typename QT, int DPAD, int WAVES, int NST>
-hipError_t occ_cfg(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, attn_mfma_dma_kernel<QT, DPAD, WAVES, NST>, 64 * WAVES, 0);
-}
-
-template <typename QT>
-hipError_t launch_q(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
-  switch (dpad) {
-    case 64: return launch_cfg<QT, 64, 4, 4>(p, nblocks, stream);
-    case 128: return launch_cfg<QT, 128, 4, 4>(p, nblocks, stream);
-    case 256:
-      return d256_waves() == 4 ? launch_cfg<QT, 256, 4, 4>(p, nblocks, stream)
-                               : launch_cfg<QT, 256, 8, 4>(p, nblocks, stream);
-    default: return hipErrorInvalidValue;
+  static hipError_t occ(int* n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST>,
+                                                        64 * WAVES, 0);
   }
-}
+  static constexpr int rows = 32 * WAVES * RB;
+};
 
-template <typename QT>
-hipError_t occ_q(int dpad, int* n) {
+// Prefill (cfg 0, default): 8 waves x 32 rows, two waves per SIMD in
+// ping-pong.  Decode pass 1: 4 waves x 32 rows without ping-pong, so that the
+// loads run NST - 1 tiles ahead (HBM latency, not the MFMA, bounds it).
+// cfg 1 / 2 (prefill, D <= 128): 4 waves x 64 rows / 4 waves x 32 rows.
+template <typename QT, typename F>
+hipError_t with_cfg(int dpad, bool decode, F&& f) {
+  const int c = tune_cfg();
+  if (decode) {
+    switch (dpad) {
+      case 64: return f(Cfg<QT, 64, 4, 1, 4>());
+      case 128: return f(Cfg<QT, 128, 4, 1, 4>());
+      case 256: return c == 3 ? f(Cfg<QT, 256, 4, 1, 4>()) : f(Cfg<QT, 256, 4, 1, 5>());
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (dpad) {
-    case 64: return occ_cfg<QT, 64, 4, 4>(n);
-    case 128: return occ_cfg<QT, 128, 4, 4>(n);
-    case 256: return d256_waves() == 4 ? occ_cfg<QT, 256, 4, 4>(n) : occ_cfg<QT, 256, 8, 4>(n);
+    case 64:
+      return c == 1 ? f(Cfg<QT, 64, 4, 2, 4>()) : c == 2 ? f(Cfg<QT, 64, 4, 1, 4>()) : f(Cfg<QT, 64, 8, 1, 4>());
+    case 128:
+      return c == 1 ? f(Cfg<QT, 128, 4, 2, 4>()) : c == 2 ? f(Cfg<QT, 128, 4, 1, 4>()) : f(Cfg<QT, 128, 8, 1, 4>());
+    case 256: return f(Cfg<QT, 256, 8, 1, 4>());
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
-// fp16 or bf16 q with KV of the same dtype.
-hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
-  if (q_kind == KV_F16) return launch_q<_Float16>(p, dpad, nblocks, stream);
-  if (q_kind == KV_BF16) return launch_q<__bf16>(p, dpad, nblocks, stream);
+// fp16 or bf16 q with KV of the same dtype; `decode` selects the decode shape.
+hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool decode, int nblocks,
+                                hipStream_t stream) {
+  auto go = [&](auto cfg) { return decltype(cfg)::launch(p, nblocks, stream); };
+  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
+  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
-  if (q_kind == KV_F16) return occ_q<_Float16>(dpad, blocks_per_cu);
-  if (q_kind == KV_BF16) return occ_q<__bf16>(dpad, blocks_per_cu);
+hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu) {
+  auto go = [&](auto cfg) { return decltype(cfg)::occ(blocks_per_cu); };
+  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
+  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);
   return hipErrorInvalidValue;
 }
 
-int mfma_dma_rows(int dpad) { return 32 * dma_cfg(dpad).waves; }
+int mfma_dma_rows(int dpad, bool decode) {
+  int rows = 0;
+  auto go = [&](auto cfg) {
+    rows = decltype(cfg)::rows;
+    return hipSuccess;
+  };
+  (void)with_cfg<_Float16>(dpad, decode, go);
+  return rows;
+}
 
 }  // namespace pa

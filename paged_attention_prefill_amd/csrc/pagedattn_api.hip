@@ -21,9 +21,10 @@ hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dp
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
                         float* out_lse, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
-hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
-hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
-int mfma_dma_rows(int dpad);
+hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool decode, int nblocks,
+                                hipStream_t stream);
+hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu);
+int mfma_dma_rows(int dpad, bool decode);
 int mfma_rows_per_group();
 int valu_rows_per_group();
 }  // namespace pa
@@ -160,8 +161,10 @@ KernelKind kernel_for(int q_dtype, int kv_dtype) {
   if (kv_dtype == PA_FP8_E5M2) return K_REGSTAGE;
   return K_DMA;
 }
-int rows_for(KernelKind k, int dpad) {
-  return k == K_VALU ? pa::valu_rows_per_group() : k == K_DMA ? pa::mfma_dma_rows(dpad) : pa::mfma_rows_per_group();
+int rows_for(KernelKind k, int dpad, bool decode) {
+  return k == K_VALU  ? pa::valu_rows_per_group()
+         : k == K_DMA ? pa::mfma_dma_rows(dpad, decode)
+                      : pa::mfma_rows_per_group();
 }
 
 }  // namespace
@@ -242,13 +245,13 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   if (total_q <= 0 || num_seqs <= 0) return 1;
   const int g = num_q_heads / num_kv_heads;
   const KernelKind kk = kernel_for(q_dtype, kv_dtype);
-  const int rows = rows_for(kk, dpad_of(head_dim));
+  const int rows = rows_for(kk, dpad_of(head_dim), false);
   int cus = 0;
   st = device_cus(&cus);
   if (st != PA_OK) return st;
   int occ = 1;
   hipError_t oe = hipSuccess;
-  if (kk == K_DMA) oe = pa::mfma_dma_occupancy(kind_of(q_dtype), dpad_of(head_dim), &occ);
+  if (kk == K_DMA) oe = pa::mfma_dma_occupancy(kind_of(q_dtype), dpad_of(head_dim), false, &occ);
   else if (kk == K_REGSTAGE) oe = pa::mfma_occupancy(kind_of(q_dtype), kind_of(kv_dtype), dpad_of(head_dim), &occ);
   if (oe != hipSuccess || occ < 1) occ = 1;
   const int64_t tiles_grid = ceil_div((int64_t)max_seqlen_q * g, rows) * num_seqs;
@@ -260,18 +263,18 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
 static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
                          const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
                          int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
-                         int splits, bool always_partial, void* workspace, size_t ws_bytes,
+                         int splits, bool is_decode, void* workspace, size_t ws_bytes,
                          hipStream_t stream) {
   const int g = hq / kv->num_kv_heads;
   const KernelKind kind = kernel_for(q_dtype, kv->dtype);
-  const int rows = rows_for(kind, dpad_of(kv->head_dim));
+  const int rows = rows_for(kind, dpad_of(kv->head_dim), is_decode);
   const int qtiles = (int)ceil_div((int64_t)max_q * g, rows);
   const int64_t nwork = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
   const int64_t pad = 8 * pa::kXcdGroup;
   const int64_t nblocks = (nwork + pad - 1) / pad * pad;
   if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nwork);
   if (nwork == 0 || total_q == 0) return ok();
-  const bool partial = always_partial || splits > 1;
+  const bool partial = is_decode || splits > 1;
 
   pa::AttnParams p;
   p.q = q;
@@ -302,7 +305,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
-                 : kind == K_DMA ? pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream)
+                 : kind == K_DMA ? pa::launch_attn_mfma_dma(p, qk, dp, is_decode, (int)nblocks, stream)
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial) {
