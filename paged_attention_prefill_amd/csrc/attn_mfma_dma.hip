@@ -21,100 +21,26 @@
 // insert a wait for all of them before every LDS read; completion is tracked
 // by hand with s_waitcnt vmcnt(N) plus a work-group barrier.
 
-#include "pa_common.h"
-
 #include <cstdlib>
 
-#pragma clang diagnostic ignored "-Winline-asm"
+#include "pa_mfma.h"
 
 namespace pa {
 
-namespace {
-
-constexpr int kKT = 32;
-constexpr float kTau = 8.0f;
-constexpr float kNegInf = -__builtin_huge_valf();
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
-
-__device__ __forceinline__ void dma16(const char* g, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
-               "s"(__builtin_amdgcn_readfirstlane(lds_byte))
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Work-group barrier for the LDS ring.  __syncthreads() also waits for every
-// outstanding vector-memory load (vmcnt(0)), which would drain the tile loads
-// still in flight; here each wave has already waited for its own loads of the
-// tile about to be read, so only LDS traffic has to settle before s_barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// XOR swizzles of the 16-byte chunks of a key row (chunk c of key `key` lives
-// in slot swz(key, c)); chosen so that the MFMA operand reads are free of LDS
-// bank conflicts.  Both are involutions.
-template <int DPAD>
-__device__ __forceinline__ int swz_k(int key, int c) {
-  if constexpr (DPAD >= 128) return c ^ (key & 15);
-  else return c ^ ((key >> 1) & 7);
-}
-template <int DPAD>
-__device__ __forceinline__ int swz_v(int key, int c) {
-  if constexpr (DPAD >= 128) return c ^ ((key & 3) << 2);
-  else return c ^ (((key >> 1) & 1) << 2);
-}
-
-template <typename QT> struct Mf;
-template <> struct Mf<_Float16> {
-  static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
-                                                  0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 v = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-};
-template <> struct Mf<__bf16> {
-  static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    b2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-};
-
-}  // namespace
+using namespace mf;
 
 template <typename QT, int DPAD, int WAVES, int RB, int NST>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void attn_mfma_dma_kernel(
     const AttnParams p) {
   constexpr int WROWS = 32 * RB;                // query rows per wave (RB blocks of 32)
   constexpr int ROWS = WROWS * WAVES;
-  constexpr int CPK = DPAD / 8;                 // 16-byte chunks per key row
-  constexpr int ROWB = CPK * 16;                // bytes per key row in LDS
-  constexpr int TILE_BYTES = kKT * ROWB;        // one K (or V) tile
-  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  constexpr int INSTR = STAGE_BYTES / 1024;     // 1 KB DMA instructions per stage
-  static_assert(INSTR % WAVES == 0, "DMA instructions must split evenly over the waves");
-  constexpr int LPW = INSTR / WAVES;            // DMA instructions per wave per tile
-  constexpr int HALF = INSTR / 2;               // instructions per region (K or V)
-  constexpr int KPI = 64 / CPK;                 // keys per DMA instruction
+  typedef TileLoader<DPAD, WAVES> TL;
+  constexpr int ROWB = TL::ROWB;                // bytes per key row in LDS
+  constexpr int TILE_BYTES = TL::TILE_BYTES;    // one K (or V) tile
+  constexpr int STAGE_BYTES = TL::STAGE_BYTES;
+  constexpr int LPW = TL::LPW;                  // DMA instructions per wave per tile
   constexpr int NKK = DPAD / 16;
   constexpr int NDB = DPAD / 32;
-  static_assert((NST - 2) * LPW <= 63, "vmcnt range");
-  static_assert(NST <= 5, "wait ladder covers up to 4 tiles ahead");
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
@@ -181,66 +107,10 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   }
 
   const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
-  const int P = p.page_size;
-  const int* bt = p.block_tables + (int64_t)seq * p.max_pages;
-  const int64_t sp_b = p.stride_page * 2;
-  const int st_b = (int)(p.stride_token * 2);  // 32 keys * stride fits in 32 bits (checked on the host)
-  const char* kbase = (const char*)p.k_pages + (int64_t)kvh * p.stride_head * 2;
-  const char* vbase = (const char*)p.v_pages + (int64_t)kvh * p.stride_head * 2;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(&smem[0]);
-  const int dchunks = p.head_dim >> 3;
 
-  // ---- per-lane DMA roles (loop invariant): byte offset of (key, chunk) in a tile
-  const int lkey = lane / CPK, lpos = lane % CPK;
-  int doff[LPW];
-#pragma unroll
-  for (int n = 0; n < LPW; ++n) {
-    const int inst = wave * LPW + n;
-    const int region = inst / HALF;  // 0: K, 1: V (wave-uniform)
-    const int ri = inst - region * HALF;
-    const int key = ri * KPI + lkey;
-    int c = region == 0 ? swz_k<DPAD>(key, lpos) : swz_v<DPAD>(key, lpos);
-    c = c < dchunks ? c : dchunks - 1;  // head_dim < DPAD: any finite data (multiplied by 0 / discarded)
-    doff[n] = key * st_b + c * 16;
-  }
-
-  // Page ids are read through the constant address space at a uniform index,
-  // i.e. with scalar loads: they are tracked by lgkmcnt, so waiting for one
-  // never drains the tile loads in flight (which a vector load's vmcnt wait
-  // would).
-  const int pg0 = klo / P;
-  const __attribute__((address_space(4))) int* btc = (const __attribute__((address_space(4))) int*)bt;
-  auto page_id = [&](int pg) -> int { return btc[__builtin_amdgcn_readfirstlane(pg)]; };
-
-  // running page position of the next tile to issue
-  int nx_pg = pg0, nx_off = klo - pg0 * P;
-  auto issue = [&](int it, int stage) {
-    const int j0 = klo + it * kKT;
-    const int pg = nx_pg, off = nx_off;
-    nx_off += kKT;
-    while (nx_off >= P) nx_off -= P, ++nx_pg;
-    const int first_n = P - off;
-    const int page_a = page_id(pg);
-    const int page_b = (first_n < kKT && (pg + 1) * P < kend) ? page_id(pg + 1) : page_a;
-    const int64_t A = (int64_t)page_a * sp_b + (int64_t)off * st_b;
-    const int64_t B = (int64_t)page_b * sp_b - (int64_t)first_n * st_b;
-    const int lastkey = kend - 1 - j0;
-    const uint32_t sbase = lds0 + stage * STAGE_BYTES;
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      const int inst = wave * LPW + n;
-      const int region = inst / HALF;
-      const int ri = inst - region * HALF;
-      int key = ri * KPI + lkey;
-      int o = doff[n];
-      if (key > lastkey) {  // past the work group's last key: reload a valid key (finite data, masked)
-        o += (lastkey - key) * st_b;
-        key = lastkey;
-      }
-      dma16((region == 0 ? kbase : vbase) + (key < first_n ? A : B) + o,
-            sbase + region * TILE_BYTES + ri * 1024);
-    }
-  };
+  TileLoader<DPAD, WAVES> tl;
+  tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  auto issue = [&](int it, int stage) { tl.issue(it, stage); };
 
   // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
   // is an XOR of a lane constant with the loop index on bits that do not
@@ -340,10 +210,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   constexpr int DIST = PP ? NST - 2 : NST - 1;
   const bool late = PP && wave >= WAVES / 2;
 
-  // Every load the compiler can see (Q fragments, metadata) completes here, so
-  // that it places no vmcnt wait inside the loop: such a wait would also drain
-  // the tile loads in flight, which the compiler does not track.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  drain_visible_loads();
 
   int issued = 0;
 #pragma unroll
@@ -351,20 +218,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     if (issued < ntiles) issue(issued, issued), ++issued;
 
   for (int it = 0; it < ntiles; ++it) {
-    const int ahead = issued - it - 1;  // tiles issued after this one
-    if constexpr (DIST >= 4) {
-      if (ahead >= 3) wait_vmcnt<3 * LPW>();
-      else if (ahead == 2) wait_vmcnt<2 * LPW>();
-      else if (ahead == 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-    } else if constexpr (DIST == 3) {
-      if (ahead >= 2) wait_vmcnt<2 * LPW>();
-      else if (ahead == 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-    } else {
-      if (ahead >= 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-    }
+    wait_tiles<LPW, DIST - 1>(issued - it - 1);  // this tile's own loads have landed
     lds_barrier();
     if (issued < ntiles) issue(issued, issued % NST), ++issued;
     const int j0 = klo + it * kKT;
@@ -450,20 +304,11 @@ struct Cfg {
 };
 
 // Prefill (cfg 0, default): 8 waves x 32 rows, two waves per SIMD in
-// ping-pong.  Decode pass 1: 4 waves x 32 rows without ping-pong, so that the
-// loads run NST - 1 tiles ahead (HBM latency, not the MFMA, bounds it).
-// cfg 1 / 2 (prefill, D <= 128): 4 waves x 64 rows / 4 waves x 32 rows.
+// ping-pong.  cfg 1 / 2 (D <= 128): 4 waves x 64 rows / 4 waves x 32 rows.
 template <typename QT, typename F>
 hipError_t with_cfg(int dpad, bool decode, F&& f) {
   const int c = tune_cfg();
-  if (decode) {
-    switch (dpad) {
-      case 64: return f(Cfg<QT, 64, 4, 1, 4>());
-      case 128: return f(Cfg<QT, 128, 4, 1, 4>());
-      case 256: return c == 3 ? f(Cfg<QT, 256, 4, 1, 4>()) : f(Cfg<QT, 256, 4, 1, 5>());
-      default: return hipErrorInvalidValue;
-    }
-  }
+  (void)decode;  // decode pass 1 has its own kernel (attn_decode.hip)
   switch (dpad) {
     case 64:
       return c == 1 ? f(Cfg<QT, 64, 4, 2, 4>()) : c == 2 ? f(Cfg<QT, 64, 4, 1, 4>()) : f(Cfg<QT, 64, 8, 1, 4>());

@@ -25,6 +25,8 @@ hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool 
                                 hipStream_t stream);
 hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu);
 int mfma_dma_rows(int dpad, bool decode);
+hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
+int decode_rows_per_group();
 int mfma_rows_per_group();
 int valu_rows_per_group();
 }  // namespace pa
@@ -162,9 +164,9 @@ KernelKind kernel_for(int q_dtype, int kv_dtype) {
   return K_DMA;
 }
 int rows_for(KernelKind k, int dpad, bool decode) {
-  return k == K_VALU  ? pa::valu_rows_per_group()
-         : k == K_DMA ? pa::mfma_dma_rows(dpad, decode)
-                      : pa::mfma_rows_per_group();
+  if (k == K_VALU) return pa::valu_rows_per_group();
+  if (k == K_DMA) return decode ? pa::decode_rows_per_group() : pa::mfma_dma_rows(dpad, false);
+  return pa::mfma_rows_per_group();
 }
 
 }  // namespace
@@ -305,7 +307,8 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
-                 : kind == K_DMA ? pa::launch_attn_mfma_dma(p, qk, dp, is_decode, (int)nblocks, stream)
+                 : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, dp, (int)nblocks, stream)
+                                              : pa::launch_attn_mfma_dma(p, qk, dp, false, (int)nblocks, stream))
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial) {
