@@ -35,6 +35,30 @@ from paged_attention_prefill_amd import ops, workload  # noqa: E402
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sources_hash():
+    """sha256 over the HIP sources: counters taken on other sources no longer apply."""
+    import hashlib
+    d = os.path.join(ROOT, "paged_attention_prefill_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name, part):
+    """HBM bytes per launch from the rocprofv3 counter runs, if taken on these sources."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != kernel_sources_hash():
+        return None
+    e = t.get("workloads", {}).get(workload_name, {}).get(part)
+    return None if e is None else e.get("hbm_bytes_per_call")
 
 
 def log(*a):
@@ -89,7 +113,7 @@ def build_workload(name):
                             "decode of a q=1 row over the same cache",
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
                 "seq_len": 152048, "kv_dtype": "f16"}
-        return desc, [("prefill", pre, "auto"), ("decode", dec, 128)]
+        return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
     if name == "mixed_step":
         c = gen.mixed_step(kv_kind="f16")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
@@ -97,14 +121,14 @@ def build_workload(name):
         desc = {"workload": "mixed step: 784-token chunk after 104,000 cached tokens (prefill) + MTP verify row "
                             "q=5 at 240,000 (split-KV decode)", "num_q_heads": 24, "num_kv_heads": 4,
                 "head_dim": 256, "page_size": 816, "kv_dtype": "f16"}
-        return desc, [("prefill", chunk, "auto"), ("decode", ver, 256)]
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
     if name == "mixed_step_fp8":
         c = gen.mixed_step(kv_kind="e5m2")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000 (fp8)")
         chunk = gen.select_seqs(c, [1], name="prefill 784 after 104000 (fp8)")
         desc = {"workload": "mixed step, fp8_e5m2 KV", "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256,
                 "page_size": 816, "kv_dtype": "e5m2"}
-        return desc, [("prefill", chunk, "auto"), ("decode", ver, 256)]
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
     if name == "decode_batch":
         c = gen.decode_batch(kind="bf16")
         desc = {"workload": "split-KV decode batch: 32 rows q=1, lengths 0..10000, MHA 16 heads, D 128, page 16",
@@ -177,7 +201,7 @@ def main():
     ap.add_argument("--prefill-splits", default=None, help="override: 0 = auto, or a count")
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=400, help="query tokens in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters")
     a = ap.parse_args()
@@ -245,12 +269,15 @@ def main():
     if "prefill" in parts:
         pf = parts["prefill"]
         res["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS, "traffic": None,
-                           "kernel": "attn_mfma_kernel (+ merge when split)"}
+                           "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS,
+                           "traffic": measured_traffic(a.workload, "prefill"),
+                           "kernel": "attn_mfma_dma_kernel (+ merge_kernel when the keys are split)"}
     if "decode" in parts:
         dc = parts["decode"]
         res["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": dc["gbs"] / HBM_PEAK_GBS, "traffic": None}
+                                  "frac": dc["gbs"] / HBM_PEAK_GBS,
+                                  "traffic": measured_traffic(a.workload, "decode"),
+                                  "kernel": "attn_decode_kernel + merge_kernel"}
     if not a.no_cpu_baseline and "prefill" in parts:
         pre = [c for c in calls if c.kind == "prefill"][0].case
         if pre.num_seqs == 1:
