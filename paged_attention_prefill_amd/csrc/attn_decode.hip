@@ -90,8 +90,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   TL tl;
   tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
 
-  const int sk = DPAD >= 128 ? (r32 & 15) : ((r32 >> 1) & 7);
-  const uint32_t klane = r32 * ROWB + (((uint32_t)(hi ^ sk)) << 4);
+  const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
   const int vkey = 4 * hi + (tk >> 2);
   const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < KKW; ++i) {
       const int kk = wave * KKW + i;
-      const uint4 a = *(const uint4*)(smem + ((sb + klane) ^ (kk << 5)));
+      const uint4 a = *(const uint4*)(smem + sb + klane + kk * kKStep);
       s = Mf<QT>::run(a, qf[i], s);
     }
 #pragma unroll

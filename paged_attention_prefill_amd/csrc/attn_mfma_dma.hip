@@ -115,8 +115,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
   // is an XOR of a lane constant with the loop index on bits that do not
   // overlap the row and stage parts of the address, so each read costs one XOR.
-  const int sk = DPAD >= 128 ? (r32 & 15) : ((r32 >> 1) & 7);
-  const uint32_t klane = r32 * ROWB + (((uint32_t)(hi ^ sk)) << 4);
+  const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
   const int vkey = 4 * hi + (tk >> 2);
   const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
@@ -131,12 +130,17 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     f32x16_t s[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s[rb] = (f32x16_t)(0.0f);
+    // each K fragment read is issued one k-step ahead of the MFMA that uses it
+    uint4 a = *(const uint4*)(smem + kls);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 a = *(const uint4*)(smem + (kls ^ (kk << 5)));
+      uint4 an;
+      if (kk + 1 < NKK) an = *(const uint4*)(smem + kls + (kk + 1) * kKStep);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         if (rb_on[rb]) s[rb] = Mf<QT>::run(a, qf[rb][kk], s[rb]);
+      a = an;
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -182,23 +186,21 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   // O^T += V^T P^T with the P of the tile in `stage`
   auto pv = [&](int stage) {
     const uint32_t vls = stage * STAGE_BYTES + vlane;
+    // each V^T fragment (two transpose reads) is issued one step ahead of its MFMA
+    uint4 a = read_vt(smem + vls, 8 * ROWB);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint32_t va = vls ^ (db << 6);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const char* a0 = smem + va + ks * 16 * ROWB;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a0);
-        const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a0 + 8 * ROWB));
-        uint4 a;
-        a.x = __builtin_bit_cast(uint2, lo).x;
-        a.y = __builtin_bit_cast(uint2, lo).y;
-        a.z = __builtin_bit_cast(uint2, hi4).x;
-        a.w = __builtin_bit_cast(uint2, hi4).y;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          if (rb_on[rb]) oacc[rb][db] = Mf<QT>::run(a, pf[rb][ks], oacc[rb][db]);
+    for (int st = 0; st < 2 * NDB; ++st) {
+      const int db = st >> 1, ks = st & 1;
+      uint4 an;
+      if (st + 1 < 2 * NDB) {
+        const int db1 = (st + 1) >> 1, ks1 = (st + 1) & 1;
+        an = read_vt(smem + (vls ^ (db1 << 6)) + ks1 * 16 * ROWB, 8 * ROWB);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb]) oacc[rb][db] = Mf<QT>::run(a, pf[rb][ks], oacc[rb][db]);
+      a = an;
     }
   };
 

@@ -57,14 +57,15 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // would also drain the tile loads, which it does not track).
 __device__ __forceinline__ void drain_visible_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// XOR swizzles of the 16-byte chunks of a key row (chunk c of key `key` lives
-// in slot swz(key, c)); chosen so that the MFMA operand reads are free of LDS
-// bank conflicts.  Both are involutions.
-template <int DPAD>
-__device__ __forceinline__ int swz_k(int key, int c) {
-  if constexpr (DPAD >= 128) return c ^ (key & 15);
-  else return c ^ ((key >> 1) & 7);
-}
+// LDS layouts of a tile (32 keys, DPAD elements per key, 16-byte chunks):
+//  * K is chunk-major: chunk c of key k at byte (c * 32 + k) * 16.  The S^T
+//    operand read of lane (key k, half h) at k-step kk is chunk 2 kk + h, so
+//    the 16 lanes of one LDS cycle read 16 consecutive 16-byte slots (no bank
+//    conflict) and successive k-steps are immediate offsets of one address.
+//  * V is row-major with an XOR swizzle of the chunks (chunk c of key k lives
+//    in slot swz_v(k, c)), chosen so that the transpose reads of the PV
+//    operand are free of bank conflicts.  The swizzle is an involution.
+__device__ __forceinline__ int k_slot(int key, int c) { return c * kKT + key; }
 template <int DPAD>
 __device__ __forceinline__ int swz_v(int key, int c) {
   if constexpr (DPAD >= 128) return c ^ ((key & 3) << 2);
@@ -95,6 +96,11 @@ template <> struct Mf<__bf16> {
   }
 };
 
+// Byte offset of lane (key r32, half hi)'s S^T operand at k-step 0 inside a K
+// tile; k-step kk adds kk * 2 * kKT * 16 bytes.
+__device__ __forceinline__ uint32_t k_frag_lane(int r32, int hi) { return (uint32_t)k_slot(r32, hi) * 16; }
+constexpr int kKStep = 2 * kKT * 16;
+
 // V^T fragment of the PV product (A operand of 32x32x16): two transpose reads
 // of four keys each, d = 32 db + lane % 32.
 __device__ __forceinline__ uint4 read_vt(const char* a0, int eight_rows) {
@@ -109,8 +115,8 @@ __device__ __forceinline__ uint4 read_vt(const char* a0, int eight_rows) {
 }
 
 // Gathers 32-key K and V tiles of one kv head through the block table into an
-// LDS ring (16-bit KV).  Stage layout: K tile then V tile, each 32 key rows of
-// DPAD elements with swizzled 16-byte chunks.  Every lane owns LPW 1 KB DMA
+// LDS ring (16-bit KV).  Stage layout: K tile (chunk-major) then V tile
+// (row-major, swizzled chunks), see above.  Every lane owns LPW 1 KB DMA
 // instructions per tile; a tile may straddle two pages of any size that is a
 // multiple of 16.  Keys at or past `kend` reload the last valid key (finite
 // data that the softmax masks), so nothing past the sequence is ever read.
@@ -127,6 +133,7 @@ struct TileLoader {
   static constexpr int KPI = 64 / CPK;
 
   int doff[LPW];
+  int dkey[LPW];
   int wave, lkey, klo, kend, P, st_b, nx_pg, nx_off;
   int64_t sp_b;
   const char* kbase;
@@ -156,9 +163,17 @@ struct TileLoader {
     for (int n = 0; n < LPW; ++n) {
       const int inst = wave * LPW + n;
       const int region = inst / HALF;  // 0: K, 1: V (wave-uniform)
-      const int key = (inst - region * HALF) * KPI + lkey;
-      int c = region == 0 ? swz_k<DPAD>(key, lpos) : swz_v<DPAD>(key, lpos);
+      const int ri = inst - region * HALF;
+      int key, c;
+      if (region == 0) {  // K: the instruction's 64 slots are chunks 2 ri, 2 ri + 1 of keys 0..31
+        key = lane & (kKT - 1);
+        c = 2 * ri + (lane >> 5);
+      } else {
+        key = ri * KPI + lkey;
+        c = swz_v<DPAD>(key, lpos);
+      }
       c = c < dchunks ? c : dchunks - 1;  // head_dim < DPAD: any finite data (multiplied by 0 / discarded)
+      dkey[n] = key;
       doff[n] = key * st_b + c * 16;
     }
   }
@@ -182,7 +197,7 @@ struct TileLoader {
       const int inst = wave * LPW + n;
       const int region = inst / HALF;
       const int ri = inst - region * HALF;
-      int key = ri * KPI + lkey;
+      int key = dkey[n];
       int o = doff[n];
       if (key > lastkey) {  // past the work group's last key: reload a valid key (finite data, masked)
         o += (lastkey - key) * st_b;
