@@ -322,9 +322,14 @@ hipError_t with_cfg(int dpad, bool decode, F&& f) {
 }
 }  // namespace
 
+hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
+hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu);
+static bool use_w4(int dpad) { return tune_cfg() == 3 && (dpad == 128 || dpad == 256); }
+
 // fp16 or bf16 q with KV of the same dtype; `decode` selects the decode shape.
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool decode, int nblocks,
                                 hipStream_t stream) {
+  if (use_w4(dpad)) return launch_attn_prefill_w4(p, q_kind, dpad, nblocks, stream);
   auto go = [&](auto cfg) { return decltype(cfg)::launch(p, nblocks, stream); };
   if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
   if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);
@@ -332,6 +337,7 @@ hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool 
 }
 
 hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu) {
+  if (use_w4(dpad)) return prefill_w4_occupancy(q_kind, dpad, blocks_per_cu);
   auto go = [&](auto cfg) { return decltype(cfg)::occ(blocks_per_cu); };
   if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
   if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);

@@ -1,0 +1,481 @@
+// Paged attention pass 1, one wave per SIMD, 64 query rows per wave (fp16 / bf16).
+//
+// Same computation and work decomposition as attn_mfma_dma.hip (GQA-packed
+// query rows of one sequence and kv head over one key part, 32-key tiles from
+// the LDS DMA ring, S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16, lazy
+// online softmax), arranged for a higher MFMA share of the SIMD:
+//
+//   * every wave holds two blocks of 32 rows, so each K or V^T fragment read
+//     from LDS feeds two MFMAs; LDS read traffic per flop is half that of a
+//     32-row wave, which matters because at 32 rows per wave the LDS is nearly
+//     as busy as the matrix cores;
+//   * the 64 x DPAD output accumulators (256 registers at D = 256) live in the
+//     AGPR file, the scores S^T in VGPRs (their MFMAs are issued from inline
+//     assembly, so that the compiler does not place them in AGPRs too);
+//   * the PV product of tile i - 1 is issued in the same basic block as the
+//     softmax of tile i and the two are interleaved instruction by instruction
+//     (a few VALU instructions run in the shadow of every MFMA), so the softmax
+//     costs little beyond the MFMA time; the QK product of tile i runs alone;
+//   * the row max is exchanged between the two lane halves with
+//     v_permlane32_swap (one VALU instruction instead of an LDS permute), the
+//     softmax scale is folded into the exponent's FMA, and the causal mask is
+//     only applied on tiles that reach a row's last key.
+//
+// Inline-assembly MFMAs are not covered by the compiler's hazard recognizer,
+// so the required wait states are written out where their results are read.
+
+#include <type_traits>
+
+#include "pa_mfma.h"
+
+namespace pa {
+
+using namespace mf;
+
+namespace {
+
+// c = a * b (+ c unless `first`), accumulator in VGPRs.
+template <typename QT>
+__device__ __forceinline__ void mfma_s(f32x16_t& c, uint4 a, uint4 b, bool first) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 av = __builtin_bit_cast(i32x4, a), bv = __builtin_bit_cast(i32x4, b);
+  if constexpr (__is_same(QT, _Float16)) {
+    if (first) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
+    else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+  } else {
+    if (first) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+  }
+}
+
+// Wait states between the last score MFMA and the first VALU read of its
+// result (20 >= the 12 that an 8-pass XDL op needs); tying the scores to the
+// statement keeps every read after it.
+__device__ __forceinline__ void scores_ready(f32x16_t& s0, f32x16_t& s1) {
+  asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s0), "+v"(s1));
+}
+
+// max(x[lane], x[lane ^ 32]) in every lane, through v_permlane32_swap (lanes
+// 32..63 of the first operand trade places with lanes 0..31 of the second).
+__device__ __forceinline__ float max_halves(float x) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
+}
+
+// max(a, b, c) without the canonicalizing moves the compiler adds around
+// fmaxf of MFMA results (the scores are never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// In-place scale of an accumulator held in AGPRs (read, multiply, write back
+// into the same register), so that the conditional rescale does not make the
+// compiler keep a second copy of the accumulators.
+__device__ __forceinline__ void scale_acc_agpr(f32x16_t& x, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float e = x[i], t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(t)
+                 : "v"(s));
+    x[i] = e;
+  }
+}
+
+// Pins the accumulators to the AGPR file and orders everything that defines
+// them before everything that reads them next, with `N` + 1 wait states.
+template <int NDB>
+__device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) asm volatile("s_nop 7" : "+a"(o[db]));
+}
+
+}  // namespace
+
+template <typename QT, int DPAD, int NST>
+__global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParams p) {
+  constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
+  typedef TileLoader<DPAD, WAVES> TL;
+  constexpr int ROWB = TL::ROWB;
+  constexpr int TILE_BYTES = TL::TILE_BYTES;
+  constexpr int STAGE_BYTES = TL::STAGE_BYTES;
+  constexpr int LPW = TL::LPW;
+  constexpr int NKK = DPAD / 16, NDB = DPAD / 32, NST2 = 2 * NDB;
+  constexpr int DIST = NST - 2;  // tile i - 1 is still read in iteration i
+  constexpr int KPF = 3, VPF = 3;  // LDS operand reads issued ahead of their MFMA
+  static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(DIST >= 1 && DIST <= 3, "ring depth");
+
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5, r32 = lane & 31;
+
+  int w = xcd_remap(blockIdx.x);
+  if (w >= p.num_work) return;
+  const int qtile = w % p.qtiles;
+  w /= p.qtiles;
+  const int split = w % p.num_splits;
+  w /= p.num_splits;
+  const int kvh = w % p.num_kv_heads;
+  const int seq = w / p.num_kv_heads;
+
+  const int q0 = p.cu_seqlens_q[seq];
+  const int qlen = p.cu_seqlens_q[seq + 1] - q0;
+  const int g = p.group;
+  const int nrows = qlen * g;
+  const int row0 = qtile * ROWS;
+  if (row0 >= nrows) return;
+  const int L = p.seq_lens[seq];
+  int klo, khi;
+  split_range(L, p.num_splits, split, klo, khi);
+  const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
+  const int kend = min(khi, L - qlen + last_tok + 1);
+  const int wrow0 = row0 + wave * WROWS;
+
+  // this lane's rows (one per block) and their Q^T fragments (B operand)
+  int lim[RB];
+  uint4 qf[RB][NKK];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int prow = wrow0 + rb * 32 + r32;
+    const bool valid = prow < nrows;
+    const int tok = valid ? prow / g : 0;
+    const int hq = kvh * g + (valid ? prow - tok * g : 0);
+    lim[rb] = valid ? min(L - qlen + tok + 1, khi) : 0;
+    const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int d = kk * 16 + hi * 8;
+      qf[rb][kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  f32x16_t oacc[RB][NDB];
+  float m[RB], lsum[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    lsum[rb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[rb][db] = (f32x16_t)(0.0f);
+    acc_fence<NDB>(oacc[rb]);
+  }
+
+  const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
+  TL tl;
+  tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
+
+  const uint32_t klane = k_frag_lane(r32, hi);
+  const int tg = lane >> 4, tk = lane & 15;
+  const int vkey = 4 * hi + (tk >> 2);
+  const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
+  const int vcl = 2 * (tg & 1) + ((tk & 3) >> 1);
+  const uint32_t vlane = TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
+  const float c = p.scale_log2;
+
+  f32x16_t s[RB];
+  uint4 pcur[RB][2], pnew[RB][2];
+  bool need[RB];
+  float alpha[RB];
+
+  // S^T = K Q^T for both row blocks; each K fragment feeds two MFMAs.  The
+  // DMA instructions of the tile being refilled are spread over the k-steps
+  // (MODE 1: fast tile, 2: general tile, 0: nothing to load), so that the
+  // vector memory unit takes them while the matrix cores are busy.
+  auto qk = [&](int stage, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    const uint32_t kls = stage * STAGE_BYTES + klane;
+    uint4 kf[KPF];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) kf[i] = *(const uint4*)(smem + kls + i * kKStep);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint4 a = kf[kk % KPF];
+      if (kk + KPF < NKK) kf[kk % KPF] = *(const uint4*)(smem + kls + (kk + KPF) * kKStep);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mfma_s<QT>(s[rb], a, qf[rb][kk], kk == 0);
+      if constexpr (MODE != 0) {
+        constexpr int EVERY = NKK / LPW;
+        static_assert(NKK % LPW == 0, "DMA spread");
+        if (kk % EVERY == EVERY - 1) tl.template part<MODE == 1>(kk / EVERY);
+      }
+    }
+    scores_ready(s[0], s[1]);
+  };
+
+  // Causal / key-range mask on the scores of the tile starting at key j0;
+  // only tiles that reach some row's last key need it.
+  auto mask_scores = [&](int j0) {
+    if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1])) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
+        const int t = lim[rb] - j0 - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kNegInf;
+      }
+    }
+  };
+
+  // Online softmax of the (masked) scores in `s` -> pnew, cut into kSmSteps
+  // small steps (15 per row block, the two blocks alternating) so that they
+  // can be placed between MFMAs: per block, 4 steps of row max, the exchange
+  // between lane halves and the rescale decision, the new reference max, 8
+  // steps of two exponentials each, and the row-sum update.
+  constexpr int kSmSteps = 30;
+  float tmax[RB], nref[RB], ls[RB];
+  auto sm_step = [&](int j) {
+    const int rb = j & 1, k = j >> 1;
+    if (k == 0) {  // elements 0..4
+      tmax[rb] = max3f(max3f(s[rb][0], s[rb][1], s[rb][2]), s[rb][3], s[rb][4]);
+    } else if (k < 3) {  // elements 4k + 1 .. 4k + 4
+      tmax[rb] = max3f(max3f(tmax[rb], s[rb][4 * k + 1], s[rb][4 * k + 2]), s[rb][4 * k + 3], s[rb][4 * k + 4]);
+    } else if (k == 3) {  // elements 13..15
+      tmax[rb] = max3f(max3f(tmax[rb], s[rb][13], s[rb][14]), s[rb][15], s[rb][15]);
+    } else if (k == 4) {
+      tmax[rb] = max_halves(tmax[rb]) * c;
+      need[rb] = __any(tmax[rb] > m[rb] + kTau);
+    } else if (k == 5) {
+      const float mnew = need[rb] ? fmaxf(m[rb], tmax[rb]) : m[rb];
+      alpha[rb] = (need[rb] && mnew != kNegInf) ? fast_exp2(m[rb] - mnew) : 1.0f;
+      m[rb] = mnew;
+      nref[rb] = mnew == kNegInf ? 0.0f : -mnew;
+      ls[rb] = 0.0f;
+    } else if (k < 14) {
+      const int q = k - 6;  // elements 2q, 2q + 1 -> packed word q
+      const float e0 = fast_exp2(__builtin_fmaf(s[rb][2 * q], c, nref[rb]));
+      const float e1 = fast_exp2(__builtin_fmaf(s[rb][2 * q + 1], c, nref[rb]));
+      ls[rb] += e0 + e1;
+      ((uint32_t*)pnew[rb])[q] = Mf<QT>::pack2(e0, e1);
+    } else {
+      lsum[rb] = __builtin_fmaf(lsum[rb], alpha[rb], ls[rb]);
+    }
+  };
+  // Keeps the softmax results in the block that computed them (otherwise the
+  // compiler sinks the exponentials below the rescale branch).
+  auto pin_softmax = [&]() {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        i32x4 t = __builtin_bit_cast(i32x4, pnew[rb][ks]);
+        asm volatile("" : "+v"(t));
+        pnew[rb][ks] = __builtin_bit_cast(uint4, t);
+      }
+      asm volatile("" : "+v"(lsum[rb]));
+    }
+  };
+  auto softmax = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSmSteps; ++j) sm_step(j);
+    pin_softmax();
+  };
+
+  auto vt_read = [&](uint32_t vls, int n) {
+    return read_vt(smem + (vls ^ ((n >> 1) << 6)) + (n & 1) * 16 * ROWB, 8 * ROWB);
+  };
+
+  // O^T += V^T P^T for the tile in `stage` with the P in pcur.
+  auto pv = [&](int stage) {
+    const uint32_t vls = stage * STAGE_BYTES + vlane;
+    uint4 vf[VPF];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vf[i] = vt_read(vls, i);
+#pragma unroll
+    for (int st = 0; st < NST2; ++st) {
+      const int db = st >> 1, ks = st & 1;
+      const uint4 a = vf[st % VPF];
+      if (st + VPF < NST2) vf[st % VPF] = vt_read(vls, st + VPF);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = Mf<QT>::run(a, pcur[rb][ks], oacc[rb][db]);
+    }
+  };
+
+  // PV of the previous tile with the softmax of the current one placed between
+  // its MFMAs by hand (scheduling barriers keep every group where it is).
+  auto pv_softmax = [&](int pstage) {
+    constexpr int NMF = RB * NST2;
+    const uint32_t vls = pstage * STAGE_BYTES + vlane;
+    uint4 vf[VPF];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vf[i] = vt_read(vls, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NST2; ++st) {
+      const int db = st >> 1, ks = st & 1;
+      const uint4 a = vf[st % VPF];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        oacc[rb][db] = Mf<QT>::run(a, pcur[rb][ks], oacc[rb][db]);
+        const int i = st * RB + rb;
+#pragma unroll
+        for (int j = i * kSmSteps / NMF; j < (i + 1) * kSmSteps / NMF; ++j) sm_step(j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (st + VPF < NST2) vf[st % VPF] = vt_read(vls, st + VPF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pin_softmax();
+  };
+
+  auto rescale = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (need[rb]) {
+        // the accumulators were last written by MFMAs: wait states before the reads
+        asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) scale_acc_agpr(oacc[rb][db], alpha[rb]);
+        acc_fence<NDB>(oacc[rb]);
+      }
+    }
+  };
+
+  drain_visible_loads();
+
+  int issued = 0;
+#pragma unroll
+  for (int i = 0; i < DIST; ++i)
+    if (issued < ntiles) tl.issue(issued, issued), ++issued;
+  if (issued < ntiles) tl.fetch(issued);
+
+  // QK of the tile in `stage`, issuing the next tile's loads on the way.
+  auto qk_issue = [&](int stage) {
+    if (issued < ntiles) {
+      tl.begin(issued % NST);
+      if (tl.fast()) qk(stage, std::integral_constant<int, 1>());
+      else qk(stage, std::integral_constant<int, 2>());
+      ++issued;
+    } else {
+      qk(stage, std::integral_constant<int, 0>());
+    }
+  };
+
+  if (ntiles > 0) {
+    // tile 0: QK and softmax only (no earlier PV to overlap with)
+    wait_tiles<LPW, DIST - 1>(issued - 1);
+    lds_barrier();
+    qk_issue(0);
+    mask_scores(klo);
+    softmax();
+    if (issued < ntiles) tl.fetch(issued);
+    // alpha of the first tile multiplies zero accumulators: nothing to rescale
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      pcur[rb][0] = pnew[rb][0];
+      pcur[rb][1] = pnew[rb][1];
+    }
+
+    for (int it = 1; it < ntiles; ++it) {
+      wait_tiles<LPW, DIST - 1>(issued - it - 1);
+      lds_barrier();
+      const int j0 = klo + it * kKT;
+      qk_issue(it % NST);
+      mask_scores(j0);
+      pv_softmax((it - 1) % NST);
+      rescale();
+      if (issued < ntiles) tl.fetch(issued);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        pcur[rb][0] = pnew[rb][0];
+        pcur[rb][1] = pnew[rb][1];
+      }
+    }
+    pv((ntiles - 1) % NST);
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+    const int prow = wrow0 + rb * 32 + r32;
+    if (prow >= nrows) continue;
+    const int tok = prow / g;
+    const int hq = kvh * g + (prow - tok * g);
+    const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
+    const float inv = empty ? 0.0f : p.v_scale / ltot;
+    const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
+    const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
+    if (p.write_partial) {
+      float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = db * 32 + 8 * rr + 4 * hi;
+          if (d < p.head_dim) {
+            float2 a = {oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv};
+            float2 b = {oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv};
+            *(float2*)(rec + d) = a;
+            *(float2*)(rec + d + 2) = b;
+          }
+        }
+      }
+      if (hi == 0) {
+        float2 t = {lse_nat, 0.0f};
+        *(float2*)(rec + p.head_dim) = t;
+      }
+    } else {
+      QT* orow = (QT*)p.out + rowidx * p.head_dim;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = db * 32 + 8 * rr + 4 * hi;
+          if (d < p.head_dim) {
+            uint2 v = {Mf<QT>::pack2(oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv),
+                       Mf<QT>::pack2(oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv)};
+            *(uint2*)(orow + d) = v;
+          }
+        }
+      }
+      if (p.lse != nullptr && hi == 0) p.lse[rowidx] = lse_nat;
+    }
+  }
+}
+
+// ---- host side -------------------------------------------------------------
+
+namespace {
+template <typename QT, int DPAD, int NST>
+hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+template <typename QT>
+hipError_t launch_w4_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
+  switch (dpad) {
+    case 128: return launch_w4<QT, 128, 5>(p, nblocks, stream);
+    case 256: return launch_w4<QT, 256, 5>(p, nblocks, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+// Prefill pass 1 for fp16 / bf16 q with KV of the same dtype, head dims padded
+// to 128 or 256; 256 query rows per work group.
+hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
+  if (q_kind == KV_F16) return launch_w4_d<_Float16>(p, dpad, nblocks, stream);
+  if (q_kind == KV_BF16) return launch_w4_d<__bf16>(p, dpad, nblocks, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
+  (void)q_kind;
+  if (dpad == 128)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_prefill_w4_kernel<_Float16, 128, 5>, 256, 0);
+  if (dpad == 256)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_prefill_w4_kernel<_Float16, 256, 5>, 256, 0);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

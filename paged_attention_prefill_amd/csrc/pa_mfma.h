@@ -25,6 +25,20 @@ __device__ __forceinline__ void dma16(const char* g, uint32_t lds_byte) {
                : "memory", "m0");
 }
 
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset
+// (the saddr form: no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16_sb(const char* base, uint32_t voff, uint32_t lds_byte) {
+  // readfirstlane works on (signed) int: widen through uint32_t so that the
+  // low half is zero-extended, not sign-extended into the high half
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const char* sbase = (const char*)(uintptr_t)((hi << 32) | lo);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_byte))
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -120,6 +134,11 @@ __device__ __forceinline__ uint4 read_vt(const char* a0, int eight_rows) {
 // instructions per tile; a tile may straddle two pages of any size that is a
 // multiple of 16.  Keys at or past `kend` reload the last valid key (finite
 // data that the softmax masks), so nothing past the sequence is ever read.
+//
+// A tile is loaded in three steps so that callers can spread the work:
+// fetch(it) reads the tile's page ids (scalar loads), begin(stage) forms its
+// page bases, part<FAST>(n) issues DMA instruction n of this wave.  FAST may
+// be used when fast() holds (one page, every key inside the range).
 template <int DPAD, int WAVES>
 struct TileLoader {
   static constexpr int CPK = DPAD / 8;
@@ -132,20 +151,25 @@ struct TileLoader {
   static constexpr int HALF = INSTR / 2;
   static constexpr int KPI = 64 / CPK;
 
-  int doff[LPW];
-  int dkey[LPW];
-  int wave, lkey, klo, kend, P, st_b, nx_pg, nx_off;
+  int doff[LPW];  // per lane: byte offset of its 16 bytes for instruction n, relative to the key-0 base
+  int wave, lane, lkey, klo, kend, P, st_b;
+  int nx_pg, nx_off;                  // page cursor of the next tile to fetch
+  int f_j0, f_off, f_first, f_pa, f_pb;  // the fetched tile
   int64_t sp_b;
+  int64_t tA, tB;                     // byte offsets of key 0 on the first / second page
+  int tfirst, tlast;
+  uint32_t tsb;
   const char* kbase;
   const char* vbase;
   const __attribute__((address_space(4))) int* btc;
   uint32_t lds0;
 
-  __device__ __forceinline__ void init(const AttnParams& p, int seq, int kvh, int wave_, int lane, int klo_,
+  __device__ __forceinline__ void init(const AttnParams& p, int seq, int kvh, int wave_, int lane_, int klo_,
                                        int kend_, uint32_t lds0_) {
     wave = wave_;
-    klo = klo_;
-    kend = kend_;
+    lane = lane_;
+    klo = __builtin_amdgcn_readfirstlane(klo_);
+    kend = __builtin_amdgcn_readfirstlane(kend_);
     P = p.page_size;
     sp_b = p.stride_page * 2;
     st_b = (int)(p.stride_token * 2);  // 32 keys * stride fits in 32 bits (checked on the host)
@@ -155,56 +179,84 @@ struct TileLoader {
     // scalar loads, tracked by lgkmcnt, so they never drain the tile loads
     btc = (const __attribute__((address_space(4))) int*)(p.block_tables + (int64_t)seq * p.max_pages);
     lds0 = lds0_;
-    nx_pg = klo / P;
-    nx_off = klo - nx_pg * P;
-    lkey = lane / CPK;
-    const int lpos = lane % CPK, dchunks = p.head_dim >> 3;
+    nx_pg = __builtin_amdgcn_readfirstlane(klo / P);
+    nx_off = __builtin_amdgcn_readfirstlane(klo - nx_pg * P);
+    lkey = lane_ / CPK;
+    const int lpos = lane_ % CPK, dchunks = p.head_dim >> 3;
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
       const int inst = wave * LPW + n;
       const int region = inst / HALF;  // 0: K, 1: V (wave-uniform)
       const int ri = inst - region * HALF;
       int key, c;
-      if (region == 0) {  // K: the instruction's 64 slots are chunks 2 ri, 2 ri + 1 of keys 0..31
-        key = lane & (kKT - 1);
-        c = 2 * ri + (lane >> 5);
-      } else {
-        key = ri * KPI + lkey;
-        c = swz_v<DPAD>(key, lpos);
-      }
+      key = inst_key(region, ri);
+      if (region == 0) c = 2 * ri + (lane_ >> 5);  // K: chunks 2 ri, 2 ri + 1 of keys 0..31
+      else c = swz_v<DPAD>(key, lpos);
       c = c < dchunks ? c : dchunks - 1;  // head_dim < DPAD: any finite data (multiplied by 0 / discarded)
-      dkey[n] = key;
       doff[n] = key * st_b + c * 16;
     }
   }
 
-  // Issues tile `it` (keys klo + 32 it ...) into `stage`; calls must come in order.
-  __device__ __forceinline__ void issue(int it, int stage) {
-    const int j0 = klo + it * kKT;
-    const int pg = nx_pg, off = nx_off;
+  // Reads the page ids of tile `it` (keys klo + 32 it ...); calls come in tile order.
+  __device__ __forceinline__ void fetch(int it) {
+    f_j0 = klo + it * kKT;
+    const int pg = nx_pg;
+    f_off = nx_off;
     nx_off += kKT;
     while (nx_off >= P) nx_off -= P, ++nx_pg;
-    const int first_n = P - off;  // keys of the tile on the first page (a multiple of 16)
-    const int page_a = btc[__builtin_amdgcn_readfirstlane(pg)];
-    const int page_b =
-        (first_n < kKT && (pg + 1) * P < kend) ? btc[__builtin_amdgcn_readfirstlane(pg + 1)] : page_a;
-    const int64_t A = (int64_t)page_a * sp_b + (int64_t)off * st_b;
-    const int64_t B = (int64_t)page_b * sp_b - (int64_t)first_n * st_b;
-    const int lastkey = kend - 1 - j0;
-    const uint32_t sbase = lds0 + stage * STAGE_BYTES;
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      const int inst = wave * LPW + n;
-      const int region = inst / HALF;
-      const int ri = inst - region * HALF;
-      int key = dkey[n];
+    f_first = P - f_off;  // keys of the tile on the first page (a multiple of 16)
+    f_pa = btc[pg];
+    f_pb = (f_first < kKT && (pg + 1) * P < kend) ? btc[pg + 1] : f_pa;
+  }
+
+  // Page bases of the fetched tile, to be loaded into `stage`.
+  __device__ __forceinline__ void begin(int stage) {
+    tA = (int64_t)f_pa * sp_b + (int64_t)f_off * st_b;
+    tB = (int64_t)f_pb * sp_b - (int64_t)f_first * st_b;
+    tfirst = f_first;
+    tlast = kend - 1 - f_j0;
+    tsb = lds0 + stage * STAGE_BYTES;
+  }
+
+  __device__ __forceinline__ bool fast() const { return tfirst >= kKT && tlast >= kKT - 1; }
+
+  template <bool FAST>
+  __device__ __forceinline__ void part(int n) {
+    const int inst = wave * LPW + n;
+    const int region = inst / HALF;
+    const int ri = inst - region * HALF;
+    const char* base = region == 0 ? kbase : vbase;
+    const uint32_t dst = tsb + region * TILE_BYTES + ri * 1024;
+    if constexpr (FAST) {
+      dma16_sb(base + tA, (uint32_t)doff[n], dst);
+    } else {
+      int key = inst_key(region, ri);
       int o = doff[n];
-      if (key > lastkey) {  // past the work group's last key: reload a valid key (finite data, masked)
-        o += (lastkey - key) * st_b;
-        key = lastkey;
+      asm volatile("" : "+v"(o));  // keeps the per-lane 64-bit address out of loop-invariant code motion
+      if (key > tlast) {  // past the work group's last key: reload a valid key (finite data, masked)
+        o += (tlast - key) * st_b;
+        key = tlast;
       }
-      dma16((region == 0 ? kbase : vbase) + (key < first_n ? A : B) + o, sbase + region * TILE_BYTES + ri * 1024);
+      dma16(base + (key < tfirst ? tA : tB) + o, dst);
     }
+  }
+
+  // Issues tile `it` into `stage` in one go.
+  __device__ __forceinline__ void issue(int it, int stage) {
+    fetch(it);
+    begin(stage);
+    if (fast()) {
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) part<true>(n);
+    } else {
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) part<false>(n);
+    }
+  }
+
+  // Key (0..31 within the tile) that this lane loads in instruction `ri` of `region`.
+  __device__ __forceinline__ int inst_key(int region, int ri) const {
+    return region == 0 ? (lane & (kKT - 1)) : ri * KPI + lkey;
   }
 };
 
