@@ -21,8 +21,6 @@
 // insert a wait for all of them before every LDS read; completion is tracked
 // by hand with s_waitcnt vmcnt(N) plus a work-group barrier.
 
-#include <cstdlib>
-
 #include "pa_mfma.h"
 
 namespace pa {
@@ -281,16 +279,6 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 // ---- host side -------------------------------------------------------------
 
 namespace {
-// Work-group shapes (waves, row blocks per wave, stages), by head-dim bucket.
-// A tuning knob picks among the compiled shapes while measuring.
-int tune_cfg() {
-  static int c = [] {
-    const char* e = getenv("PA_TUNE_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  return c;
-}
-
 template <typename QT, int DPAD, int WAVES, int RB, int NST>
 struct Cfg {
   static hipError_t launch(const AttnParams& p, int nblocks, hipStream_t stream) {
@@ -302,21 +290,16 @@ struct Cfg {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST>,
                                                         64 * WAVES, 0);
   }
-  static constexpr int rows = 32 * WAVES * RB;
 };
 
-// Prefill (cfg 0, default): 8 waves x 32 rows, two waves per SIMD in
-// ping-pong.  cfg 1 / 2 (D <= 128): 4 waves x 64 rows / 4 waves x 32 rows.
+// Head dims padded to 64 or 128: 8 waves x 32 rows, two waves per SIMD in
+// ping-pong.  (Padded to 256: the one-wave-per-SIMD kernel of
+// attn_prefill_w4.hip, 4 waves x 64 rows.)  Both take 256 rows per group.
 template <typename QT, typename F>
-hipError_t with_cfg(int dpad, bool decode, F&& f) {
-  const int c = tune_cfg();
-  (void)decode;  // decode pass 1 has its own kernel (attn_decode.hip)
+hipError_t with_cfg(int dpad, F&& f) {
   switch (dpad) {
-    case 64:
-      return c == 1 ? f(Cfg<QT, 64, 4, 2, 4>()) : c == 2 ? f(Cfg<QT, 64, 4, 1, 4>()) : f(Cfg<QT, 64, 8, 1, 4>());
-    case 128:
-      return c == 1 ? f(Cfg<QT, 128, 4, 2, 4>()) : c == 2 ? f(Cfg<QT, 128, 4, 1, 4>()) : f(Cfg<QT, 128, 8, 1, 4>());
-    case 256: return f(Cfg<QT, 256, 8, 1, 4>());
+    case 64: return f(Cfg<QT, 64, 8, 1, 4>());
+    case 128: return f(Cfg<QT, 128, 8, 1, 4>());
     default: return hipErrorInvalidValue;
   }
 }
@@ -324,34 +307,24 @@ hipError_t with_cfg(int dpad, bool decode, F&& f) {
 
 hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
 hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu);
-static bool use_w4(int dpad) { return tune_cfg() == 3 && (dpad == 128 || dpad == 256); }
 
-// fp16 or bf16 q with KV of the same dtype; `decode` selects the decode shape.
-hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool decode, int nblocks,
-                                hipStream_t stream) {
-  if (use_w4(dpad)) return launch_attn_prefill_w4(p, q_kind, dpad, nblocks, stream);
+// Prefill pass 1 for fp16 or bf16 q with KV of the same dtype.
+hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
+  if (dpad == 256) return launch_attn_prefill_w4(p, q_kind, dpad, nblocks, stream);
   auto go = [&](auto cfg) { return decltype(cfg)::launch(p, nblocks, stream); };
-  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
-  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);
+  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, go);
+  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, go);
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu) {
-  if (use_w4(dpad)) return prefill_w4_occupancy(q_kind, dpad, blocks_per_cu);
+hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
+  if (dpad == 256) return prefill_w4_occupancy(q_kind, dpad, blocks_per_cu);
   auto go = [&](auto cfg) { return decltype(cfg)::occ(blocks_per_cu); };
-  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, decode, go);
-  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, decode, go);
+  if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, go);
+  if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, go);
   return hipErrorInvalidValue;
 }
 
-int mfma_dma_rows(int dpad, bool decode) {
-  int rows = 0;
-  auto go = [&](auto cfg) {
-    rows = decltype(cfg)::rows;
-    return hipSuccess;
-  };
-  (void)with_cfg<_Float16>(dpad, decode, go);
-  return rows;
-}
+int mfma_dma_rows(int dpad) { return dpad == 64 || dpad == 128 || dpad == 256 ? 256 : 0; }
 
 }  // namespace pa

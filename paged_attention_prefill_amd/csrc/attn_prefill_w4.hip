@@ -454,7 +454,6 @@ hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
 template <typename QT>
 hipError_t launch_w4_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
-    case 128: return launch_w4<QT, 128, 5>(p, nblocks, stream);
     case 256: return launch_w4<QT, 256, 5>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
@@ -462,7 +461,7 @@ hipError_t launch_w4_d(const AttnParams& p, int dpad, int nblocks, hipStream_t s
 }  // namespace
 
 // Prefill pass 1 for fp16 / bf16 q with KV of the same dtype, head dims padded
-// to 128 or 256; 256 query rows per work group.
+// to 256; 256 query rows per work group.
 hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
   if (q_kind == KV_F16) return launch_w4_d<_Float16>(p, dpad, nblocks, stream);
   if (q_kind == KV_BF16) return launch_w4_d<__bf16>(p, dpad, nblocks, stream);
@@ -471,8 +470,6 @@ hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int
 
 hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
-  if (dpad == 128)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_prefill_w4_kernel<_Float16, 128, 5>, 256, 0);
   if (dpad == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_prefill_w4_kernel<_Float16, 256, 5>, 256, 0);
   return hipErrorInvalidValue;

@@ -21,10 +21,10 @@ hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dp
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
                         float* out_lse, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
-hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, bool decode, int nblocks,
+hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks,
                                 hipStream_t stream);
-hipError_t mfma_dma_occupancy(int q_kind, int dpad, bool decode, int* blocks_per_cu);
-int mfma_dma_rows(int dpad, bool decode);
+hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
+int mfma_dma_rows(int dpad);
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
 int decode_rows_per_group();
 int mfma_rows_per_group();
@@ -165,7 +165,7 @@ KernelKind kernel_for(int q_dtype, int kv_dtype) {
 }
 int rows_for(KernelKind k, int dpad, bool decode) {
   if (k == K_VALU) return pa::valu_rows_per_group();
-  if (k == K_DMA) return decode ? pa::decode_rows_per_group() : pa::mfma_dma_rows(dpad, false);
+  if (k == K_DMA) return decode ? pa::decode_rows_per_group() : pa::mfma_dma_rows(dpad);
   return pa::mfma_rows_per_group();
 }
 
@@ -253,7 +253,7 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   if (st != PA_OK) return st;
   int occ = 1;
   hipError_t oe = hipSuccess;
-  if (kk == K_DMA) oe = pa::mfma_dma_occupancy(kind_of(q_dtype), dpad_of(head_dim), false, &occ);
+  if (kk == K_DMA) oe = pa::mfma_dma_occupancy(kind_of(q_dtype), dpad_of(head_dim), &occ);
   else if (kk == K_REGSTAGE) oe = pa::mfma_occupancy(kind_of(q_dtype), kind_of(kv_dtype), dpad_of(head_dim), &occ);
   if (oe != hipSuccess || occ < 1) occ = 1;
   const int64_t tiles_grid = ceil_div((int64_t)max_seqlen_q * g, rows) * num_seqs;
@@ -308,7 +308,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
                  : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, dp, (int)nblocks, stream)
-                                              : pa::launch_attn_mfma_dma(p, qk, dp, false, (int)nblocks, stream))
+                                              : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial) {
