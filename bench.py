@@ -103,6 +103,11 @@ class Call:
         return float(np.mean([a.elapsed_time(b) for a, b in self.times])) if self.times else float("nan")
 
 
+# The calls of one step of each workload, in launch order.
+WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "mixed_step": ["prefill", "decode"],
+                  "mixed_step_fp8": ["prefill", "decode"], "decode_batch": ["decode"], "varlen": ["prefill"]}
+
+
 def build_workload(name):
     """Returns (description, [Call specs]) for one step."""
     if name == "long_chunk":
@@ -141,6 +146,13 @@ def build_workload(name):
                 "kv_dtype": "bf16"}
         return desc, [("prefill", c, "auto")]
     raise SystemExit(f"unknown workload {name}")
+
+
+def prefill_kernel_name(desc):
+    """Pass-1 kernel that serves the prefill of this workload."""
+    if desc.get("kv_dtype") == "e5m2":
+        return "attn_mfma_kernel"
+    return "attn_prefill_w4_kernel" if desc.get("head_dim", 0) > 128 else "attn_mfma_dma_kernel"
 
 
 def call_flops(kind, case):
@@ -192,6 +204,66 @@ def copy_reference(steps):
     return 0
 
 
+def _counter_rows(path):
+    """(dispatch id, kernel name, value) of every dispatch in a rocprofv3 counter CSV tree."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def write_traffic(workload_name, pmc_dir):
+    """Turns the FETCH_SIZE / WRITE_SIZE runs of `workload_name` (and of --mode copy)
+    into per-call HBM bytes in profiles/traffic.json, tagged with the kernel sources."""
+    per = {}
+    factors = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = _counter_rows(os.path.join(pmc_dir, "pmccopy_" + counter))
+        if not copy:
+            raise SystemExit(f"no copy-reference dispatches under {pmc_dir}/pmccopy_{counter}")
+        kib = max(v for _, _, v in copy)
+        factors[counter] = float(1 << 30) / (kib * 1024.0)
+        # group this workload's dispatches into calls: a pass-1 kernel and the merges after it
+        calls = []
+        for _, name, v in _counter_rows(os.path.join(pmc_dir, "pmc_" + counter)):
+            if "attn_" in name:
+                calls.append([(name, v)])
+            elif "merge_kernel" in name and calls:
+                calls[-1].append((name, v))
+        per[counter] = calls
+    kinds = WORKLOAD_CALLS[workload_name]
+    out = {"sources_sha256": kernel_sources_hash(),
+           "about": "HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by "
+                    "the factors that make the same counters read 2^30 bytes for a 1 GiB device copy "
+                    "(bench.py --mode copy).",
+           "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"], "workloads": {}}
+    try:
+        old = json.load(open(TRAFFIC_FILE))
+        if old.get("sources_sha256") == out["sources_sha256"]:
+            out["workloads"] = old.get("workloads", {})
+    except (OSError, ValueError):
+        pass
+    entry = {}
+    for i, kind in enumerate(kinds):
+        f_calls = per["FETCH_SIZE"][i::len(kinds)]
+        w_calls = per["WRITE_SIZE"][i::len(kinds)]
+        names = [n for n, _ in f_calls[0]]
+        fetch = [float(np.mean([c[j][1] for c in f_calls])) for j in range(len(names))]
+        write = [float(np.mean([c[j][1] for c in w_calls])) for j in range(len(names))]
+        total = 1024.0 * (sum(fetch) * factors["FETCH_SIZE"] + sum(write) * factors["WRITE_SIZE"])
+        entry[kind] = {"kernels": names, "fetch_kib": fetch, "write_kib": write, "hbm_bytes_per_call": total}
+    out["workloads"][workload_name] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps({"mode": "traffic", "workload": workload_name, "factors": factors,
+                      "bytes_per_call": {k: v["hbm_bytes_per_call"] for k, v in entry.items()}}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,9 +274,14 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
-                    help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic"],
+                    help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
+                         "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU)")
+    ap.add_argument("--pmc-dir", default="gpurun_out",
+                    help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
+    if a.mode == "traffic":
+        return write_traffic(a.workload, a.pmc_dir)
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not built)"}))
@@ -271,7 +348,7 @@ def main():
         res["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS,
                            "traffic": measured_traffic(a.workload, "prefill"),
-                           "kernel": "attn_mfma_dma_kernel (+ merge_kernel when the keys are split)"}
+                           "kernel": prefill_kernel_name(desc) + " (+ merge_kernel when the keys are split)"}
     if "decode" in parts:
         dc = parts["decode"]
         res["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
