@@ -105,7 +105,9 @@ typedef struct pa_kv_cache {
 /*
  * Varlen paged prefill (InferMatrixLab/vllm-rlt PR #128, "Purpose", Prefill).
  *   q [total_q, num_q_heads, head_dim] (q_dtype); out same shape and dtype;
- *   lse nullable; scale multiplies q.k (k_scale folded in for fp8).
+ *   lse nullable; scale (positive, finite) multiplies q.k (k_scale, also
+ *   positive, folded in for fp8): the kernels take row maxima of the unscaled
+ *   scores, which commutes with a positive scale only.
  *   max_seqlen_q bounds every cu_seqlens_q[b+1] - cu_seqlens_q[b] (it sizes the
  *   static grid).  num_kv_splits: 1 = no key split; 2..64 = split every query
  *   tile's keys into that many whole-tile parts and merge; 0 = choose 1..4 by

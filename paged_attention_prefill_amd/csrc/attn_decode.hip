@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     if (issued < ntiles) tl.issue(issued, issued), ++issued;
 
   for (int it = 0; it < ntiles; ++it) {
-    wait_tiles<LPW, DIST - 1 < 3 ? DIST - 1 : 3>(issued - it - 1);
+    wait_tiles<LPW, DIST - 1>(issued - it - 1);
     lds_barrier();  // tile landed for all waves; previous partial scores consumed
     if (issued < ntiles) tl.issue(issued, issued % NST), ++issued;
     const int stage = it % NST;

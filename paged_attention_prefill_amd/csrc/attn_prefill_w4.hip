@@ -55,24 +55,6 @@ __device__ __forceinline__ void scores_ready(f32x16_t& s0, f32x16_t& s1) {
   asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s0), "+v"(s1));
 }
 
-// max(x[lane], x[lane ^ 32]) in every lane, through v_permlane32_swap (lanes
-// 32..63 of the first operand trade places with lanes 0..31 of the second).
-__device__ __forceinline__ float max_halves(float x) {
-  float t;
-  asm volatile(
-      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
-      : "+v"(x), "=&v"(t));
-  return x;
-}
-
-// max(a, b, c) without the canonicalizing moves the compiler adds around
-// fmaxf of MFMA results (the scores are never signalling NaNs).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // In-place scale of an accumulator held in AGPRs (read, multiply, write back
 // into the same register), so that the conditional rescale does not make the
 // compiler keep a second copy of the accumulators.

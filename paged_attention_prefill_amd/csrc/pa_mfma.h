@@ -44,20 +44,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most `ahead` tiles of LPW loads each are still in flight.
+// Wait until at most `ahead` (<= MAXA) tiles of LPW loads each are still in flight.
 template <int LPW, int MAXA>
 __device__ __forceinline__ void wait_tiles(int ahead) {
-  static_assert(MAXA <= 3 && MAXA * LPW <= 63, "vmcnt range");
-  if constexpr (MAXA >= 3) {
-    if (ahead >= 3) return wait_vmcnt<3 * LPW>();
-  }
-  if constexpr (MAXA >= 2) {
-    if (ahead >= 2) return wait_vmcnt<2 * LPW>();
-  }
+  static_assert(MAXA * LPW <= 63, "vmcnt range");
   if constexpr (MAXA >= 1) {
-    if (ahead >= 1) return wait_vmcnt<LPW>();
+    if (ahead >= MAXA) return wait_vmcnt<MAXA * LPW>();
+    return wait_tiles<LPW, MAXA - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_vmcnt<0>();
 }
 
 // Work-group barrier for the LDS ring.  __syncthreads() also waits for every
@@ -109,6 +105,24 @@ template <> struct Mf<__bf16> {
     return __builtin_bit_cast(uint32_t, v);
   }
 };
+
+// max(x[lane], x[lane ^ 32]) in every lane, through v_permlane32_swap (lanes
+// 32..63 of the first operand trade places with lanes 0..31 of the second).
+__device__ __forceinline__ float max_halves(float x) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
+}
+
+// max(a, b, c) without the canonicalizing moves the compiler adds around
+// fmaxf of MFMA results (the scores are never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Byte offset of lane (key r32, half hi)'s S^T operand at k-step 0 inside a K
 // tile; k-step kk adds kk * 2 * kKT * 16 bytes.

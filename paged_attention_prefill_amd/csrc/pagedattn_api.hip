@@ -114,6 +114,7 @@ int check_kv(const pa_kv_cache* kv, int q_dtype, int hq) {
     return fail(PA_ERR_UNSUPPORTED, "stride_token too large (32 slots must span < 2 GiB)");
   if (!std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
     return fail(PA_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be finite");
+  if (!(kv->k_scale > 0.0f)) return fail(PA_ERR_INVALID_ARGUMENT, "k_scale must be positive");
   if (kv->dtype != PA_FP8_E5M2 && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
     return fail(PA_ERR_UNSUPPORTED, "k_scale / v_scale apply to FP8_E5M2 KV only (must be 1)");
   return PA_OK;
@@ -341,7 +342,8 @@ int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, cons
   int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq,
                         total_q, max_seqlen_q, num_q_heads, kv);
   if (st != PA_OK) return st;
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
   if (num_kv_splits < 0 || num_kv_splits > 64) return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_splits must be in [0, 64]");
   if (num_seqs == 0 || total_q == 0) return ok();
   int splits = num_kv_splits;
@@ -369,7 +371,8 @@ int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, co
   int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
                         total_q, max_q_per_row, num_q_heads, kv);
   if (st != PA_OK) return st;
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
   if (max_q_per_row > PA_DECODE_MAX_Q)
     return fail(PA_ERR_UNSUPPORTED, "max_q_per_row %d > %d (longer rows go to pa_paged_prefill)", max_q_per_row,
                 PA_DECODE_MAX_Q);

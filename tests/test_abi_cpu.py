@@ -115,11 +115,14 @@ def _prefill(kv, **over):
     ({"stride_token": 100}, {}, ops.PA_ERR_INVALID_ARGUMENT),
     ({"k_pages": 0x10008}, {}, ops.PA_ERR_INVALID_ARGUMENT),
     ({"k_scale": 2.0}, {}, ops.PA_ERR_UNSUPPORTED),
+    ({"dtype": ops.PA_FP8_E5M2, "k_scale": -1.0}, {}, ops.PA_ERR_INVALID_ARGUMENT),
     ({}, {"q": 0x30004}, ops.PA_ERR_INVALID_ARGUMENT),
     ({}, {"splits": 2}, ops.PA_ERR_WORKSPACE),
     ({}, {"splits": 2, "ws": 0x80000, "ws_bytes": 100}, ops.PA_ERR_WORKSPACE),
     ({}, {"splits": 99}, ops.PA_ERR_INVALID_ARGUMENT),
     ({}, {"scale": float("nan")}, ops.PA_ERR_INVALID_ARGUMENT),
+    ({}, {"scale": 0.0}, ops.PA_ERR_INVALID_ARGUMENT),
+    ({}, {"scale": -0.1}, ops.PA_ERR_INVALID_ARGUMENT),
     ({}, {"num_seqs": -1}, ops.PA_ERR_INVALID_ARGUMENT),
     ({}, {"max_pages": 0}, ops.PA_ERR_INVALID_ARGUMENT),
     ({"num_pages": 0}, {}, ops.PA_ERR_INVALID_ARGUMENT),
