@@ -102,6 +102,9 @@ class Call:
     def ms(self):
         return float(np.mean([a.elapsed_time(b) for a, b in self.times])) if self.times else float("nan")
 
+    def ms_median(self):
+        return float(np.median([a.elapsed_time(b) for a, b in self.times])) if self.times else float("nan")
+
 
 # The calls of one step of each workload, in launch order.
 WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "mixed_step": ["prefill", "decode"],
@@ -264,6 +267,64 @@ def write_traffic(workload_name, pmc_dir):
     return 0
 
 
+def ceilings(seed=0):
+    """Measured chip ceilings beside the published peaks: a pure MFMA loop on
+    random and on zero fp16 operands (with the shader clock it ran at) and a
+    streaming read of 4 GiB."""
+    import ctypes
+    L = ops.lib()
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    L.pa_ceiling_mfma.argtypes = [P, P, I, I, P, P]
+    L.pa_ceiling_stream_read.argtypes = [P, ctypes.c_int64, P, I, P]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    res = {"mode": "ceilings", "cus": cus}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g = torch.Generator().manual_seed(seed)
+    blocks, iters = cus, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    for kind in ("random", "zero"):
+        a = torch.randn(128 * 8, generator=g) if kind == "random" else torch.zeros(128 * 8)
+        a = a.half().cuda()
+
+        def run():
+            st = L.pa_ceiling_mfma(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(sink.data_ptr()), blocks, iters,
+                                   ctypes.c_void_p(clocks.data_ptr()), sp)
+            assert st == 0, st
+        ms = timed(run, 3)
+        c = clocks.view(-1, 2).cpu().double()
+        ghz = float(torch.median(c[:, 0] / c[:, 1]) * 0.1)
+        flops = blocks * 4 * iters * 4 * 32768
+        res[f"mfma_f16_{kind}_tflops"] = flops / (ms * 1e-3) / 1e12
+        res[f"mfma_f16_{kind}_clock_ghz"] = ghz
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    rsink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")
+
+    def rd():
+        st = L.pa_ceiling_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(rsink.data_ptr()),
+                                      cus * 8, sp)
+        assert st == 0, st
+    ms = timed(rd, 5)
+    res["stream_read_gbs"] = nbytes / (ms * 1e-3) / 1e9
+    res["published"] = {"mfma_f16_dense_tflops": MFMA_F16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,9 +335,10 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
-                         "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU)")
+                         "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU); "
+                         "ceilings: a pure MFMA loop and a streaming read, measured")
     ap.add_argument("--pmc-dir", default="gpurun_out",
                     help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
@@ -290,6 +352,8 @@ def main():
     torch.cuda.set_device(0)
     if a.mode == "copy":
         return copy_reference(a.steps)
+    if a.mode == "ceilings":
+        return ceilings()
     ops.lib()
 
     log(f"building workload {a.workload} ...")
@@ -329,14 +393,14 @@ def main():
         if c.kind == "prefill":
             f = call_flops(c.kind, c.case)
             step_flops += f
-            parts["prefill"] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "flops": f, "splits": c.splits,
-                                "name": c.case.name}
+            parts["prefill"] = {"ms": ms, "ms_median": c.ms_median(), "tflops": f / (ms * 1e-3) / 1e12, "flops": f,
+                                "splits": c.splits, "name": c.case.name}
         else:
             b = call_bytes(c.kind, c.case, c.splits)
             f = call_flops(c.kind, c.case)
             step_flops += f
-            parts["decode"] = {"ms": ms, "gbs": b / (ms * 1e-3) / 1e9, "bytes": b, "splits": c.splits,
-                               "name": c.case.name}
+            parts["decode"] = {"ms": ms, "ms_median": c.ms_median(), "gbs": b / (ms * 1e-3) / 1e9, "bytes": b,
+                               "splits": c.splits, "name": c.case.name}
     value = step_flops / (ms_step * 1e-3) / 1e12
     res = {"metric": "paged-prefill TFLOPS (2K chunk @150K ctx, D256); split-KV decode HBM GB/s",
            "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -355,6 +419,22 @@ def main():
                                   "frac": dc["gbs"] / HBM_PEAK_GBS,
                                   "traffic": measured_traffic(a.workload, "decode"),
                                   "kernel": "attn_decode_kernel + merge_kernel"}
+    # decode with the caches flushed: a 1 GiB write between repetitions evicts
+    # the K/V left in the 256 MB Infinity Cache and the L2s by the step
+    dec = [c for c in calls if c.kind == "decode"]
+    if dec:
+        c = dec[0]
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        c.times = []
+        for _ in range(max(5, min(a.steps, 20))):
+            scratch.fill_(1.0)
+            c(stream, record=True)
+        torch.cuda.synchronize()
+        del scratch
+        ms = c.ms_median()
+        b = parts["decode"]["bytes"]
+        res["decode_cold"] = {"ms_median": ms, "gbs": b / (ms * 1e-3) / 1e9, "reps": len(c.times),
+                              "note": "1 GiB scratch write before each repetition"}
     if not a.no_cpu_baseline and "prefill" in parts:
         pre = [c for c in calls if c.kind == "prefill"][0].case
         if pre.num_seqs == 1:

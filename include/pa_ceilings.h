@@ -1,0 +1,33 @@
+/*
+ * Chip ceilings measured beside the published MI355X peaks (not part of the
+ * attention path; bench.py --mode ceilings calls them).
+ *
+ * pa_ceiling_mfma: `blocks` work groups of 4 waves (one per SIMD), each wave
+ *   issuing `iters` x 4 independent v_mfma_f32_32x32x16_f16 (32768 FLOP each)
+ *   on operands[0..127] (16-byte fp16 fragments, device memory the caller
+ *   fills); per-thread sums go to sink[blocks * 256].  clocks[2 b] and
+ *   clocks[2 b + 1] receive work group b's elapsed shader-clock and 100 MHz
+ *   real-time ticks.  Asynchronous on `stream` (a hipStream_t); 0 = launched, -1 = bad
+ *   argument, -4 = launch error.
+ * pa_ceiling_stream_read: `blocks` x 256 threads read `bytes` (a multiple of
+ *   16, 16-byte aligned) of `src` once with 16-byte loads; sink[blocks * 256]
+ *   receives one float per thread.  Same return codes.
+ */
+#ifndef PA_CEILINGS_H
+#define PA_CEILINGS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int pa_ceiling_mfma(const void *operands, float *sink, int32_t blocks, int32_t iters,
+                    unsigned long long *clocks, void *stream);
+int pa_ceiling_stream_read(const void *src, int64_t bytes, float *sink, int32_t blocks, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_CEILINGS_H */

@@ -1,0 +1,75 @@
+// Measured ceilings of the chip, reported beside the published peaks: a pure
+// MFMA loop (v_mfma_f32_32x32x16_f16, four independent accumulators per wave,
+// one wave per SIMD) and a streaming read.  Not part of the attention path.
+//
+// The MFMA loop also reads the shader clock (s_memtime) and the 100 MHz
+// real-time counter (s_memrealtime) at its start and end, so the clock the
+// chip actually ran at under that load can be stated.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_ceilings.h"
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256, 1) void mfma_loop(const uint4* __restrict__ operands, float* __restrict__ sink,
+                                                     int iters, unsigned long long* __restrict__ clocks) {
+  const int lane = threadIdx.x & 63;
+  const uint4 a = operands[lane], b = operands[64 + lane];
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  f32x16_t c0 = (f32x16_t)(0.0f), c1 = c0, c2 = c0, c3 = c0;
+  const half8_t ah = __builtin_bit_cast(half8_t, a), bh = __builtin_bit_cast(half8_t, b);
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+__global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src, long long n16,
+                                                   float* __restrict__ sink) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    acc ^= v0.x ^ v1.y ^ v2.z ^ v3.w;
+  }
+  for (; i < n16; i += stride) acc ^= src[i].x;
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc & 1u);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_ceiling_mfma(const void* operands, float* sink, int32_t blocks, int32_t iters,
+                    unsigned long long* clocks, void* stream_) {
+  const hipStream_t stream = (hipStream_t)stream_;
+  if (!operands || !sink || !clocks || blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, stream, (const uint4*)operands, sink, iters, clocks);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int pa_ceiling_stream_read(const void* src, int64_t bytes, float* sink, int32_t blocks, void* stream_) {
+  const hipStream_t stream = (hipStream_t)stream_;
+  if (!src || !sink || blocks <= 0 || bytes < 16 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return -1;
+  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (long long)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

@@ -80,10 +80,13 @@ def lib():
 
 
 def header_symbols():
-    """Function names declared in include/pagedattn.h."""
-    text = open(HEADER_PATH).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    """Function names declared in include/*.h."""
+    import glob
+    names = set()
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER_PATH), "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _check(status):
