@@ -419,22 +419,24 @@ def main():
                                   "frac": dc["gbs"] / HBM_PEAK_GBS,
                                   "traffic": measured_traffic(a.workload, "decode"),
                                   "kernel": "attn_decode_kernel + merge_kernel"}
-    # decode with the caches flushed: a 1 GiB write between repetitions evicts
-    # the K/V left in the 256 MB Infinity Cache and the L2s by the step
+    # decode with the caches flushed: reading 1 GiB between repetitions evicts
+    # the K/V left in the 256 MB Infinity Cache and the L2s by the step (a read,
+    # not a write: evicting dirty lines would put their write-back traffic on
+    # the decode's HBM time)
     dec = [c for c in calls if c.kind == "decode"]
     if dec:
         c = dec[0]
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         c.times = []
         for _ in range(max(5, min(a.steps, 20))):
-            scratch.fill_(1.0)
+            scratch.sum()
             c(stream, record=True)
         torch.cuda.synchronize()
         del scratch
         ms = c.ms_median()
         b = parts["decode"]["bytes"]
         res["decode_cold"] = {"ms_median": ms, "gbs": b / (ms * 1e-3) / 1e9, "reps": len(c.times),
-                              "note": "1 GiB scratch write before each repetition"}
+                              "note": "1 GiB scratch read before each repetition"}
     if not a.no_cpu_baseline and "prefill" in parts:
         pre = [c for c in calls if c.kind == "prefill"][0].case
         if pre.num_seqs == 1:
