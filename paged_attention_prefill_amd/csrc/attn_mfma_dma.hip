@@ -305,12 +305,13 @@ hipError_t with_cfg(int dpad, F&& f) {
 }
 }  // namespace
 
-hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
+hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                                  hipStream_t stream);
 hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu);
 
 // Prefill pass 1 for fp16 or bf16 q with KV of the same dtype.
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
-  if (dpad == 256) return launch_attn_prefill_w4(p, q_kind, dpad, nblocks, stream);
+  if (dpad == 256) return launch_attn_prefill_w4(p, q_kind, q_kind, dpad, nblocks, stream);
   auto go = [&](auto cfg) { return decltype(cfg)::launch(p, nblocks, stream); };
   if (q_kind == KV_F16) return with_cfg<_Float16>(dpad, go);
   if (q_kind == KV_BF16) return with_cfg<__bf16>(dpad, go);

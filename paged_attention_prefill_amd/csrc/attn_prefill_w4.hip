@@ -34,18 +34,26 @@ using namespace mf;
 
 namespace {
 
-// c = a * b (+ c unless `first`), accumulator in VGPRs.
-template <typename QT>
+// c = a * b (+ c unless `first`), accumulator in VGPRs.  VALU_A: `a` was just
+// written by VALU instructions (the widened fp8 K operand), which an MFMA may
+// read only after 2 wait states; the s_nop supplies 3.
+template <typename QT, bool VALU_A = false>
 __device__ __forceinline__ void mfma_s(f32x16_t& c, uint4 a, uint4 b, bool first) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 av = __builtin_bit_cast(i32x4, a), bv = __builtin_bit_cast(i32x4, b);
+#define PA_MFMA_S(OP)                                                                             \
+  if (first) asm volatile(OP " %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));                     \
+  else asm volatile(OP " %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
   if constexpr (__is_same(QT, _Float16)) {
-    if (first) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
-    else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+    if constexpr (VALU_A) {
+      PA_MFMA_S("s_nop 2\n\tv_mfma_f32_32x32x16_f16")
+    } else {
+      PA_MFMA_S("v_mfma_f32_32x32x16_f16")
+    }
   } else {
-    if (first) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
-    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+    PA_MFMA_S("v_mfma_f32_32x32x16_bf16")
   }
+#undef PA_MFMA_S
 }
 
 // Wait states between the last score MFMA and the first VALU read of its
@@ -79,19 +87,21 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 
 }  // namespace
 
-template <typename QT, int DPAD, int NST>
+// KV8: K and V are fp8 E5M2 (q fp16); the tiles stay 8-bit in LDS and are
+// widened to fp16 as their MFMA operands are read.
+template <typename QT, bool KV8, int DPAD, int NST>
 __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParams p) {
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
-  typedef TileLoader<DPAD, WAVES> TL;
+  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
   constexpr int LPW = TL::LPW;
   constexpr int NKK = DPAD / 16, NDB = DPAD / 32, NST2 = 2 * NDB;
   constexpr int DIST = NST - 2;  // tile i - 1 is still read in iteration i
-  constexpr int KPF = 3, VPF = 3;  // LDS operand reads issued ahead of their MFMA
+  constexpr int KPF = KV8 ? 2 : 3, VPF = 3;  // LDS operand reads issued ahead of their MFMA
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
-  static_assert(DIST >= 1 && DIST <= 3, "ring depth");
+  static_assert(DIST >= 1, "ring depth");
 
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
 
@@ -135,7 +145,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int d = kk * 16 + hi * 8;
+      // 16-bit K: k-step kk covers d 16 kk + 8 hi ..; fp8 K: the pair of
+      // k-steps 2j, 2j+1 covers the 16-byte chunk 2j + hi, low then high half
+      const int d = KV8 ? 32 * (kk >> 1) + 16 * hi + 8 * (kk & 1) : kk * 16 + hi * 8;
       qf[rb][kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
     }
   }
@@ -160,7 +172,13 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const int vkey = 4 * hi + (tk >> 2);
   const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
   const int vcl = 2 * (tg & 1) + ((tk & 3) >> 1);
-  const uint32_t vlane = TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
+  // fp8 V^T (read_vt8): input lane tk of group tg addresses row kr = tk / 2 of
+  // its 8-key block, key 8 (kr / 4) + 4 (tg / 2) + kr % 4, chunk 2 db + tg % 2
+  // in slot (chunk) ^ 2 kr; the d block enters by an XOR of 32 db per fragment
+  const int kr = tk >> 1;
+  const uint32_t vlane = KV8 ? TILE_BYTES + (8 * (kr >> 2) + 4 * (tg >> 1) + (kr & 3)) * ROWB + 16 * (tg & 1) +
+                                   8 * (tk & 1) + 32 * kr
+                              : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
   const float c = p.scale_log2;
 
   f32x16_t s[RB];
@@ -175,15 +193,24 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   auto qk = [&](int stage, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     const uint32_t kls = stage * STAGE_BYTES + klane;
+    // 16-bit K: one read per k-step; fp8 K: one 16-byte read per pair of k-steps
+    constexpr int NRD = KV8 ? NKK / 2 : NKK;
     uint4 kf[KPF];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kf[i] = *(const uint4*)(smem + kls + i * kKStep);
+    uint4 kw = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 a = kf[kk % KPF];
-      if (kk + KPF < NKK) kf[kk % KPF] = *(const uint4*)(smem + kls + (kk + KPF) * kKStep);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) mfma_s<QT>(s[rb], a, qf[rb][kk], kk == 0);
+      const int rd = KV8 ? kk >> 1 : kk;
+      uint4 a;
+      if (!KV8 || (kk & 1) == 0) {
+        kw = kf[rd % KPF];
+        if (rd + KPF < NRD) kf[rd % KPF] = *(const uint4*)(smem + kls + (rd + KPF) * kKStep);
+      }
+      if constexpr (KV8) a = (kk & 1) ? e5m2x8_to_f16(kw.z, kw.w) : e5m2x8_to_f16(kw.x, kw.y);
+      else a = kw;
+      mfma_s<QT, KV8>(s[0], a, qf[0][kk], kk == 0);
+      mfma_s<QT>(s[1], a, qf[1][kk], kk == 0);
       if constexpr (MODE != 0) {
         constexpr int EVERY = NKK / LPW;
         static_assert(NKK % LPW == 0, "DMA spread");
@@ -262,8 +289,10 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     pin_softmax();
   };
 
+  // V^T fragment n = (d block n / 2, key half n % 2)
   auto vt_read = [&](uint32_t vls, int n) {
-    return read_vt(smem + (vls ^ ((n >> 1) << 6)) + (n & 1) * 16 * ROWB, 8 * ROWB);
+    if constexpr (KV8) return read_vt8(smem + ((vls + (n & 1) * 16 * ROWB) ^ ((n >> 1) << 5)));
+    else return read_vt(smem + (vls ^ ((n >> 1) << 6)) + (n & 1) * 16 * ROWB, 8 * ROWB);
   };
 
   // O^T += V^T P^T for the tile in `stage` with the P in pcur.
@@ -428,32 +457,30 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 // ---- host side -------------------------------------------------------------
 
 namespace {
-template <typename QT, int DPAD, int NST>
+template <typename QT, bool KV8, int DPAD, int NST>
 hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, KV8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
-}
-template <typename QT>
-hipError_t launch_w4_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
-  switch (dpad) {
-    case 256: return launch_w4<QT, 256, 5>(p, nblocks, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 }  // namespace
 
-// Prefill pass 1 for fp16 / bf16 q with KV of the same dtype, head dims padded
-// to 256; 256 query rows per work group.
-hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
-  if (q_kind == KV_F16) return launch_w4_d<_Float16>(p, dpad, nblocks, stream);
-  if (q_kind == KV_BF16) return launch_w4_d<__bf16>(p, dpad, nblocks, stream);
+// Prefill pass 1, head dims padded to 256, 256 query rows per work group:
+// fp16 / bf16 q with KV of the same dtype (kv_kind = q_kind), or fp16 q with
+// fp8 E5M2 KV (kv_kind = KV_E5M2).
+hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                                  hipStream_t stream) {
+  if (dpad != 256) return hipErrorInvalidValue;
+  if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_w4<_Float16, true, 256, 8>(p, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, false, 256, 5>(p, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, false, 256, 5>(p, nblocks, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
   if (dpad == 256)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_prefill_w4_kernel<_Float16, 256, 5>, 256, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
+                                                        attn_prefill_w4_kernel<_Float16, false, 256, 5>, 256, 0);
   return hipErrorInvalidValue;
 }
 

@@ -76,9 +76,10 @@ __device__ __forceinline__ void drain_visible_loads() { __builtin_amdgcn_s_waitc
 //    in slot swz_v(k, c)), chosen so that the transpose reads of the PV
 //    operand are free of bank conflicts.  The swizzle is an involution.
 __device__ __forceinline__ int k_slot(int key, int c) { return c * kKT + key; }
-template <int DPAD>
+template <int DPAD, int ES = 2>
 __device__ __forceinline__ int swz_v(int key, int c) {
-  if constexpr (DPAD >= 128) return c ^ ((key & 3) << 2);
+  if constexpr (ES == 1) return c ^ (((key & 3) | ((key >> 1) & 4)) << 1);  // fp8, 16-chunk rows: see read_vt8
+  else if constexpr (DPAD >= 128) return c ^ ((key & 3) << 2);
   else return c ^ (((key >> 1) & 1) << 2);
 }
 
@@ -142,8 +143,34 @@ __device__ __forceinline__ uint4 read_vt(const char* a0, int eight_rows) {
   return a;
 }
 
+// ---- fp8 (E5M2) KV operands.  An E5M2 byte is the high byte of the fp16 of
+// the same value, so widening is a byte permute (exact).
+__device__ __forceinline__ uint32_t e5m2_lo2(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0x010C000Cu); }
+__device__ __forceinline__ uint32_t e5m2_hi2(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0x030C020Cu); }
+__device__ __forceinline__ uint4 e5m2x8_to_f16(uint32_t a, uint32_t b) {
+  return make_uint4(e5m2_lo2(a), e5m2_hi2(a), e5m2_lo2(b), e5m2_hi2(b));
+}
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32_t;
+
+// V^T fragment of the PV product from an fp8 V tile: one transpose read of
+// 8-bit elements.  Within each 16-lane group, input lane k supplies 8 bytes
+// (half k % 2 of a 16-byte chunk of row k / 2 of an 8-row block) and output
+// lane j receives byte j of each of the 8 rows, in row order: 8 keys of one d,
+// the A operand of a 32x32x16 MFMA after widening.  The rows a group
+// addresses are the 8 keys that the P^T operand pairs with this lane's
+// k-indices (16 ks + 8 (i / 4) + 4 (lane / 32) + i % 4, i = 0..7); the V chunk
+// swizzle c ^ 2 f(key), f(key) = (key & 3) | (bit 3 of key) << 2, puts those 8
+// rows' chunks in 8 different slots, so the reads are free of bank conflicts.
+__device__ __forceinline__ uint4 read_vt8(const char* a) {
+  const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_t*)a);
+  return e5m2x8_to_f16((uint32_t)r.x, (uint32_t)r.y);
+}
+
 // Gathers 32-key K and V tiles of one kv head through the block table into an
-// LDS ring (16-bit KV).  Stage layout: K tile (chunk-major) then V tile
+// LDS ring (ES = 2: 16-bit KV; ES = 1: fp8 KV, bytes copied as they are).
+// Stage layout: K tile (chunk-major) then V tile
 // (row-major, swizzled chunks), see above.  Every lane owns LPW 1 KB DMA
 // instructions per tile; a tile may straddle two pages of any size that is a
 // multiple of 16.  Keys at or past `kend` reload the last valid key (finite
@@ -153,9 +180,10 @@ __device__ __forceinline__ uint4 read_vt(const char* a0, int eight_rows) {
 // fetch(it) reads the tile's page ids (scalar loads), begin(stage) forms its
 // page bases, part<FAST>(n) issues DMA instruction n of this wave.  FAST may
 // be used when fast() holds (one page, every key inside the range).
-template <int DPAD, int WAVES>
+template <int DPAD, int WAVES, int ES = 2>
 struct TileLoader {
-  static constexpr int CPK = DPAD / 8;
+  static_assert(ES == 2 || (ES == 1 && DPAD == 256), "8-bit KV tiles are laid out for D 256");
+  static constexpr int CPK = DPAD * ES / 16;
   static constexpr int ROWB = CPK * 16;
   static constexpr int TILE_BYTES = kKT * ROWB;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
@@ -185,10 +213,10 @@ struct TileLoader {
     klo = __builtin_amdgcn_readfirstlane(klo_);
     kend = __builtin_amdgcn_readfirstlane(kend_);
     P = p.page_size;
-    sp_b = p.stride_page * 2;
-    st_b = (int)(p.stride_token * 2);  // 32 keys * stride fits in 32 bits (checked on the host)
-    kbase = (const char*)p.k_pages + (int64_t)kvh * p.stride_head * 2;
-    vbase = (const char*)p.v_pages + (int64_t)kvh * p.stride_head * 2;
+    sp_b = p.stride_page * ES;
+    st_b = (int)(p.stride_token * ES);  // 32 keys * stride fits in 32 bits (checked on the host)
+    kbase = (const char*)p.k_pages + (int64_t)kvh * p.stride_head * ES;
+    vbase = (const char*)p.v_pages + (int64_t)kvh * p.stride_head * ES;
     // page ids are read through the constant address space at a uniform index:
     // scalar loads, tracked by lgkmcnt, so they never drain the tile loads
     btc = (const __attribute__((address_space(4))) int*)(p.block_tables + (int64_t)seq * p.max_pages);
@@ -196,7 +224,7 @@ struct TileLoader {
     nx_pg = __builtin_amdgcn_readfirstlane(klo / P);
     nx_off = __builtin_amdgcn_readfirstlane(klo - nx_pg * P);
     lkey = lane_ / CPK;
-    const int lpos = lane_ % CPK, dchunks = p.head_dim >> 3;
+    const int lpos = lane_ % CPK, dchunks = (p.head_dim * ES) >> 4;
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
       const int inst = wave * LPW + n;
@@ -205,7 +233,7 @@ struct TileLoader {
       int key, c;
       key = inst_key(region, ri);
       if (region == 0) c = 2 * ri + (lane_ >> 5);  // K: chunks 2 ri, 2 ri + 1 of keys 0..31
-      else c = swz_v<DPAD>(key, lpos);
+      else c = swz_v<DPAD, ES>(key, lpos);
       c = c < dchunks ? c : dchunks - 1;  // head_dim < DPAD: any finite data (multiplied by 0 / discarded)
       doff[n] = key * st_b + c * 16;
     }

@@ -23,6 +23,8 @@ hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, vo
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks,
                                 hipStream_t stream);
+hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                                  hipStream_t stream);
 hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
 int mfma_dma_rows(int dpad);
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
@@ -155,13 +157,15 @@ int auto_splits(int64_t active_groups, int slots) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Which pass-1 kernel serves a dtype pair: fp32 -> exact-product VALU kernel;
-// fp16/bf16 with same-dtype KV -> MFMA kernel with the LDS DMA pipeline;
-// fp16 q with fp8_e5m2 KV -> MFMA kernel with register-staged dequant.
+// Which pass-1 kernel serves a call: fp32 -> exact-product VALU kernel;
+// fp16/bf16 with same-dtype KV -> MFMA kernels with the LDS DMA pipeline;
+// fp16 q with fp8_e5m2 KV -> the DMA prefill kernel (8-bit tiles widened at
+// the operand reads) for head dims padded to 256, otherwise the MFMA kernel
+// with register-staged dequant.
 enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
-KernelKind kernel_for(int q_dtype, int kv_dtype) {
+KernelKind kernel_for(int q_dtype, int kv_dtype, int dpad, bool decode) {
   if (q_dtype == PA_F32) return K_VALU;
-  if (kv_dtype == PA_FP8_E5M2) return K_REGSTAGE;
+  if (kv_dtype == PA_FP8_E5M2) return (!decode && dpad == 256) ? K_DMA : K_REGSTAGE;
   return K_DMA;
 }
 int rows_for(KernelKind k, int dpad, bool decode) {
@@ -247,7 +251,7 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   if (st != PA_OK) return fail(st, "%s", reason);
   if (total_q <= 0 || num_seqs <= 0) return 1;
   const int g = num_q_heads / num_kv_heads;
-  const KernelKind kk = kernel_for(q_dtype, kv_dtype);
+  const KernelKind kk = kernel_for(q_dtype, kv_dtype, dpad_of(head_dim), false);
   const int rows = rows_for(kk, dpad_of(head_dim), false);
   int cus = 0;
   st = device_cus(&cus);
@@ -269,7 +273,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
                          int splits, bool is_decode, void* workspace, size_t ws_bytes,
                          hipStream_t stream) {
   const int g = hq / kv->num_kv_heads;
-  const KernelKind kind = kernel_for(q_dtype, kv->dtype);
+  const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
   const int rows = rows_for(kind, dpad_of(kv->head_dim), is_decode);
   const int qtiles = (int)ceil_div((int64_t)max_q * g, rows);
   const int64_t nwork = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
@@ -309,7 +313,9 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
                  : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, dp, (int)nblocks, stream)
-                                              : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
+                                    : kk == pa::KV_E5M2
+                                        ? pa::launch_attn_prefill_w4(p, qk, kk, dp, (int)nblocks, stream)
+                                        : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial) {

@@ -336,6 +336,21 @@ def test_fp8_prefill_and_decode_small():
     compare("fp8 decode", "e5m2", out.float().cpu().numpy(), ref[100:], lse.cpu().numpy(), rl[100:])
 
 
+@pytest.mark.parametrize("D,P", [(64, 16), (128, 48), (160, 16), (256, 16), (256, 48), (256, 64)])
+def test_fp8_head_dims_and_page_sizes(D, P):
+    # fp8 KV: every head-dim bucket, page sizes that make tiles straddle pages
+    # (16, 48) or not (64); chunk and verify rows, k/v scales != 1
+    c = gen.make_case(f"fp8hd{D}p{P}", q_lens=[70, 5, 129], seq_lens=[70, 300, 1000], num_q_heads=6,
+                      num_kv_heads=2, head_dim=D, page_size=P, q_kind="f16", kv_kind="e5m2", seed=D + P,
+                      k_scale=0.75, v_scale=1.5)
+    ref, rl = run_oracle(c)
+    for splits in (1, 3):
+        out, lse = gpu_prefill(c, splits=splits)
+        compare(f"fp8 prefill D={D} P={P} S={splits}", "e5m2", out, ref, lse, rl)
+    out, lse = gpu_decode(gen.select_seqs(c, [1]), splits=4, max_q=5)
+    compare(f"fp8 decode D={D} P={P}", "e5m2", out.float().cpu().numpy(), ref[70:75], lse.cpu().numpy(), rl[70:75])
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
 def _sample_rows(case, n, seed, tokens=None):
