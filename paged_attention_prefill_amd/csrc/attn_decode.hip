@@ -22,10 +22,12 @@ namespace pa {
 
 using namespace mf;
 
-template <typename QT, int DPAD, int NST>
+// KV8: K and V are fp8 E5M2 (q fp16): 8-bit tiles in LDS, widened to fp16 as
+// the MFMA operands are read (same layouts as the prefill kernel's fp8 path).
+template <typename QT, bool KV8, int DPAD, int NST>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   constexpr int WAVES = 4;
-  typedef TileLoader<DPAD, WAVES> TL;
+  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
@@ -70,13 +72,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
 
-  // this wave's quarter of Q^T (B operand): d = 16 kk + 8 hi .. +7, kk in [wave*KKW, +KKW)
+  // this wave's quarter of Q^T (B operand), kk in [wave*KKW, +KKW): d = 16 kk + 8 hi .. +7
+  // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half)
+  static_assert(!KV8 || KKW % 2 == 0, "fp8 K is read in pairs of k-steps");
   uint4 qf[KKW];
   {
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int i = 0; i < KKW; ++i) {
-      const int d = (wave * KKW + i) * 16 + hi * 8;
+      const int kk = wave * KKW + i;
+      const int d = KV8 ? 32 * (kk >> 1) + 16 * hi + 8 * (kk & 1) : kk * 16 + hi * 8;
       qf[i] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
     }
   }
@@ -95,7 +100,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   const int vkey = 4 * hi + (tk >> 2);
   const int sv = DPAD >= 128 ? ((vkey & 3) << 2) : (((vkey >> 1) & 1) << 2);
   const int vcl = 2 * (tg & 1) + ((tk & 3) >> 1);
-  const uint32_t vlane = TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
+  const int kr = tk >> 1;  // fp8 V^T: see read_vt8
+  const uint32_t vlane = KV8 ? TILE_BYTES + (8 * (kr >> 2) + 4 * (tg >> 1) + (kr & 3)) * ROWB + 16 * (tg & 1) +
+                                   8 * (tk & 1) + 32 * kr
+                              : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
 
   drain_visible_loads();
   int issued = 0;
@@ -113,10 +121,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
 
     // partial S^T over this wave's quarter of the head dimension
     f32x16_t s = (f32x16_t)(0.0f);
+    uint4 kw = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < KKW; ++i) {
       const int kk = wave * KKW + i;
-      const uint4 a = *(const uint4*)(smem + sb + klane + kk * kKStep);
+      uint4 a;
+      if constexpr (KV8) {
+        if ((i & 1) == 0) kw = *(const uint4*)(smem + sb + klane + (kk >> 1) * kKStep);
+        a = (i & 1) ? e5m2x8_to_f16(kw.z, kw.w) : e5m2x8_to_f16(kw.x, kw.y);
+      } else {
+        a = *(const uint4*)(smem + sb + klane + kk * kKStep);
+      }
       s = Mf<QT>::run(a, qf[i], s);
     }
 #pragma unroll
@@ -169,10 +184,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     for (int j = 0; j < NDBW; ++j) {
       const int db = wave * NDBW + j;
       if (db < NDB) {
-        const uint32_t va = vls ^ (db << 6);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const uint4 a = read_vt(smem + va + ks * 16 * ROWB, 8 * ROWB);
+          uint4 a;
+          if constexpr (KV8) a = read_vt8(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
+          else a = read_vt(smem + (vls ^ (db << 6)) + ks * 16 * ROWB, 8 * ROWB);
           oacc[j] = Mf<QT>::run(a, pf[ks], oacc[j]);
         }
       }
@@ -210,24 +226,31 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
 // ---- host side -------------------------------------------------------------
 
 namespace {
-template <typename QT, int DPAD, int NST>
+template <typename QT, bool KV8, int DPAD, int NST>
 hipError_t launch_dec(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<QT, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_decode_kernel<QT, KV8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 template <typename QT>
 hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
-    case 64: return launch_dec<QT, 64, 5>(p, nblocks, stream);
-    case 128: return launch_dec<QT, 128, 4>(p, nblocks, stream);
-    case 256: return launch_dec<QT, 256, 4>(p, nblocks, stream);
+    case 64: return launch_dec<QT, false, 64, 5>(p, nblocks, stream);
+    case 128: return launch_dec<QT, false, 128, 4>(p, nblocks, stream);
+    case 256: return launch_dec<QT, false, 256, 4>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
-// Decode pass 1 for fp16 / bf16 q with KV of the same dtype; 32 rows per group.
-hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream) {
+// Decode pass 1, 32 rows per group: fp16 / bf16 q with KV of the same dtype
+// (kv_kind = q_kind), or fp16 q with fp8 E5M2 KV for head dims padded to 256.
+hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                              hipStream_t stream) {
+  if (kv_kind == KV_E5M2) {
+    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 8>(p, nblocks, stream);
+    return hipErrorInvalidValue;
+  }
+  if (q_kind != kv_kind) return hipErrorInvalidValue;
   if (q_kind == KV_F16) return launch_dec_d<_Float16>(p, dpad, nblocks, stream);
   if (q_kind == KV_BF16) return launch_dec_d<__bf16>(p, dpad, nblocks, stream);
   return hipErrorInvalidValue;

@@ -27,7 +27,8 @@ hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, 
                                   hipStream_t stream);
 hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
 int mfma_dma_rows(int dpad);
-hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int dpad, int nblocks, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
+                              hipStream_t stream);
 int decode_rows_per_group();
 int mfma_rows_per_group();
 int valu_rows_per_group();
@@ -159,13 +160,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Which pass-1 kernel serves a call: fp32 -> exact-product VALU kernel;
 // fp16/bf16 with same-dtype KV -> MFMA kernels with the LDS DMA pipeline;
-// fp16 q with fp8_e5m2 KV -> the DMA prefill kernel (8-bit tiles widened at
-// the operand reads) for head dims padded to 256, otherwise the MFMA kernel
-// with register-staged dequant.
+// fp16 q with fp8_e5m2 KV -> the DMA kernels (8-bit tiles widened at the
+// operand reads) for head dims padded to 256, otherwise the MFMA kernel with
+// register-staged dequant.
 enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
 KernelKind kernel_for(int q_dtype, int kv_dtype, int dpad, bool decode) {
   if (q_dtype == PA_F32) return K_VALU;
-  if (kv_dtype == PA_FP8_E5M2) return (!decode && dpad == 256) ? K_DMA : K_REGSTAGE;
+  if (kv_dtype == PA_FP8_E5M2) return dpad == 256 ? K_DMA : K_REGSTAGE;
+  (void)decode;
   return K_DMA;
 }
 int rows_for(KernelKind k, int dpad, bool decode) {
@@ -312,7 +314,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
-                 : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, dp, (int)nblocks, stream)
+                 : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, kk, dp, (int)nblocks, stream)
                                     : kk == pa::KV_E5M2
                                         ? pa::launch_attn_prefill_w4(p, qk, kk, dp, (int)nblocks, stream)
                                         : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
