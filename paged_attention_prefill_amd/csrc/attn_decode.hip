@@ -12,9 +12,12 @@
 //   * after a barrier every wave adds the four partials in the same order (so
 //     all waves hold bit-identical scores), runs the same online softmax, and
 //     accumulates O^T += V^T P^T for its own quarter of the output columns.
-// The K/V tiles come through the same LDS DMA ring as the prefill kernel, four
-// tiles in flight.  The output is an FP32 partial record per (token, q head,
-// part) that the merge pass combines.
+// The K/V tiles come through the same LDS DMA ring as the prefill kernel.  The
+// ring is kept shallow (one or two tiles in flight) so that two to four groups
+// share a CU: a group's own chain of LDS reads, MFMAs and softmax sets its
+// rate, and more resident groups hide it better than a deeper ring does.  The
+// output is an FP32 partial record per (token, q head, part) that the merge
+// pass combines.
 
 #include "pa_mfma.h"
 
@@ -234,9 +237,9 @@ hipError_t launch_dec(const AttnParams& p, int nblocks, hipStream_t stream) {
 template <typename QT>
 hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
-    case 64: return launch_dec<QT, false, 64, 5>(p, nblocks, stream);
-    case 128: return launch_dec<QT, false, 128, 4>(p, nblocks, stream);
-    case 256: return launch_dec<QT, false, 256, 4>(p, nblocks, stream);
+    case 64: return launch_dec<QT, false, 64, 3>(p, nblocks, stream);
+    case 128: return launch_dec<QT, false, 128, 2>(p, nblocks, stream);
+    case 256: return launch_dec<QT, false, 256, 2>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -247,7 +250,7 @@ hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t 
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream) {
   if (kv_kind == KV_E5M2) {
-    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 8>(p, nblocks, stream);
+    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 3>(p, nblocks, stream);
     return hipErrorInvalidValue;
   }
   if (q_kind != kv_kind) return hipErrorInvalidValue;
