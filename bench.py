@@ -121,7 +121,7 @@ def build_workload(name):
                             "decode of a q=1 row over the same cache",
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
                 "seq_len": 152048, "kv_dtype": "f16"}
-        return desc, [("prefill", pre, "auto"), ("decode", dec, 128)]
+        return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
     if name == "mixed_step":
         c = gen.mixed_step(kv_kind="f16")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
@@ -129,14 +129,14 @@ def build_workload(name):
         desc = {"workload": "mixed step: 784-token chunk after 104,000 cached tokens (prefill) + MTP verify row "
                             "q=5 at 240,000 (split-KV decode)", "num_q_heads": 24, "num_kv_heads": 4,
                 "head_dim": 256, "page_size": 816, "kv_dtype": "f16"}
-        return desc, [("prefill", chunk, "auto"), ("decode", ver, 128)]
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
     if name == "mixed_step_fp8":
         c = gen.mixed_step(kv_kind="e5m2")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000 (fp8)")
         chunk = gen.select_seqs(c, [1], name="prefill 784 after 104000 (fp8)")
         desc = {"workload": "mixed step, fp8_e5m2 KV", "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256,
                 "page_size": 816, "kv_dtype": "e5m2"}
-        return desc, [("prefill", chunk, "auto"), ("decode", ver, 128)]
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
     if name == "decode_batch":
         c = gen.decode_batch(kind="bf16")
         desc = {"workload": "split-KV decode batch: 32 rows q=1, lengths 0..10000, MHA 16 heads, D 128, page 16",

@@ -10,8 +10,9 @@
  *   real-time ticks.  Asynchronous on `stream` (a hipStream_t); 0 = launched, -1 = bad
  *   argument, -4 = launch error.
  * pa_ceiling_stream_read: `blocks` x 256 threads read `bytes` (a multiple of
- *   16, 16-byte aligned) of `src` once with 16-byte loads; sink[blocks * 256]
- *   receives one float per thread.  Same return codes.
+ *   16, 16-byte aligned) of `src` once with 16-byte non-temporal loads, each
+ *   block one contiguous range; sink[blocks * 256] receives one float per
+ *   thread.  Same return codes.
  */
 #ifndef PA_CEILINGS_H
 #define PA_CEILINGS_H

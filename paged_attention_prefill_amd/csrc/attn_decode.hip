@@ -1,47 +1,45 @@
-// Split-KV decode pass 1 on MFMA (fp16 / bf16): the head dimension of every
-// tile is split over the four waves of a work group.
+// Split-KV decode pass 1 on MFMA (fp16 / bf16 q; KV of the same dtype, or
+// fp8 E5M2 KV for head dims padded to 256).
 //
 // A decode row has q <= 16 tokens (InferMatrixLab/vllm-rlt PR #128, "Purpose",
 // Decode; MTP verify rows q = K+1, 1CatAI/1Cat-vLLM PR #616, "Purpose"), so a
 // work group holds one block of 32 GQA-packed query rows of one row and kv head
-// over one part of its keys.  With so few rows the attention is bound by HBM,
-// and a single wave doing the whole tile's math would stall on its own LDS
-// operand reads; instead all four waves work on every 32-key tile:
-//   * wave w forms the partial S^T = K Q^T over its quarter of the head
-//     dimension and leaves it in LDS;
-//   * after a barrier every wave adds the four partials in the same order (so
-//     all waves hold bit-identical scores), runs the same online softmax, and
-//     accumulates O^T += V^T P^T for its own quarter of the output columns.
-// The K/V tiles come through the same LDS DMA ring as the prefill kernel.  The
-// ring is kept shallow (one or two tiles in flight) so that two to four groups
-// share a CU: a group's own chain of LDS reads, MFMAs and softmax sets its
-// rate, and more resident groups hide it better than a deeper ring does.  The
-// output is an FP32 partial record per (token, q head, part) that the merge
+// over one part of its keys, and the pass is bound by HBM.  What limits it is
+// how many bytes each CU keeps in flight and how little the waves wait on one
+// another: each wave of the group walks its own 32-key tiles (every fourth
+// one) with the whole head dimension, through an LDS ring of its own, and
+// keeps its own online-softmax state; nothing in the tile loop waits for
+// another wave.  The four states are combined in LDS at the end, in a fixed
+// order, into one FP32 partial record per (token, q head, part) that the merge
 // pass combines.
-
 #include "pa_mfma.h"
 
 namespace pa {
 
 using namespace mf;
 
-// KV8: K and V are fp8 E5M2 (q fp16): 8-bit tiles in LDS, widened to fp16 as
-// the MFMA operands are read (same layouts as the prefill kernel's fp8 path).
-template <typename QT, bool KV8, int DPAD, int NST>
+// Wave w of the group owns tiles w, w + 4, w + 8, ... of the group's key range,
+// NSW stages of (K, V) tiles in its own part of LDS.  The K half of a stage is
+// refilled as soon as the wave's S^T = K Q^T has read it and the V half after
+// O^T += V^T P^T, so that between one and 2 NSW half-tiles per wave are always
+// in flight.  KV8: K and V are fp8 E5M2 (q fp16), 8-bit tiles in LDS widened
+// to fp16 as the MFMA operands are read.  The combined result depends only on
+// the row's own length and the part count.
+template <typename QT, bool KV8, int DPAD, int NSW>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   constexpr int WAVES = 4;
-  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
+  typedef TileLoader<DPAD, 1, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
-  constexpr int LPW = TL::LPW;
+  constexpr int HALF = TL::HALF;  // DMA instructions of one K (or V) tile
   constexpr int NKK = DPAD / 16, NDB = DPAD / 32;
-  constexpr int KKW = NKK / WAVES;            // k-steps of S^T per wave
-  constexpr int NDBW = (NDB + WAVES - 1) / WAVES;  // output d blocks per wave
-  constexpr int DIST = NST - 1;
+  constexpr int RING = WAVES * NSW * STAGE_BYTES;
+  static_assert(WAVES * NDB * 4 * 1024 <= RING, "the O exchange reuses the ring");
+  static_assert(NSW == 1 || NSW == 2, "ring depth");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
-  __shared__ f32x4_t sx[WAVES][4][64];  // partial scores: [wave][quarter][lane]
+  __shared__ __attribute__((aligned(1024))) char smem[RING];
+  __shared__ float2 mlx[WAVES][32];  // per wave and row: (m, l)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -75,28 +73,29 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
 
-  // this wave's quarter of Q^T (B operand), kk in [wave*KKW, +KKW): d = 16 kk + 8 hi .. +7
+  // Q^T (B operand) over the whole head dimension: k-step kk holds d = 16 kk + 8 hi .. +7
   // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half)
-  static_assert(!KV8 || KKW % 2 == 0, "fp8 K is read in pairs of k-steps");
-  uint4 qf[KKW];
+  uint4 qf[NKK];
   {
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
-    for (int i = 0; i < KKW; ++i) {
-      const int kk = wave * KKW + i;
+    for (int kk = 0; kk < NKK; ++kk) {
       const int d = KV8 ? 32 * (kk >> 1) + 16 * hi + 8 * (kk & 1) : kk * 16 + hi * 8;
-      qf[i] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
+      qf[kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
     }
   }
 
-  f32x16_t oacc[NDBW];
+  f32x16_t oacc[NDB];
 #pragma unroll
-  for (int j = 0; j < NDBW; ++j) oacc[j] = (f32x16_t)(0.0f);
+  for (int j = 0; j < NDB; ++j) oacc[j] = (f32x16_t)(0.0f);
   float m = kNegInf, lsum = 0.0f;
 
   const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
+  const int nt_w = ntiles > wave ? (ntiles - wave + WAVES - 1) / WAVES : 0;
+  const uint32_t wbase = wave * NSW * STAGE_BYTES;
   TL tl;
-  tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  tl.init(p, seq, kvh, 0, lane, klo + wave * kKT, kend, (uint32_t)(uintptr_t)(&smem[0]) + wbase);
+  tl.set_stride(WAVES * kKT);
 
   const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
@@ -108,48 +107,103 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
                                    8 * (tk & 1) + 32 * kr
                               : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
 
-  drain_visible_loads();
-  int issued = 0;
+  // DMA of the K or V half of the tile begun last (one wave issues all of a
+  // tile's instructions).  K instruction ri fills block ri (keys 8 (ri % 4) ..,
+  // chunks 8 (ri / 4) ..), V instruction ri keys KPI ri ..; the per-lane part
+  // of the source offset repeats every 2 (K) or 4 (V) instructions and the rest
+  // is uniform, so a whole-tile, whole-row load keeps 6 per-lane offsets
+  // instead of one per instruction.
+  constexpr int CPK = TL::CPK, KPI = TL::KPI, ES = KV8 ? 1 : 2;
+  const int st_b = tl.st_b;
+  const int dchunks = (p.head_dim * ES) >> 4;
+  const bool full_d = dchunks == CPK;
+  const int lkey = lane / CPK, lpos = lane % CPK;
+  uint32_t klb[2], vlb[4];
 #pragma unroll
-  for (int i = 0; i < DIST; ++i)
-    if (issued < ntiles) tl.issue(issued, issued), ++issued;
-
-  for (int it = 0; it < ntiles; ++it) {
-    wait_tiles<LPW, DIST - 1>(issued - it - 1);
-    lds_barrier();  // tile landed for all waves; previous partial scores consumed
-    if (issued < ntiles) tl.issue(issued, issued % NST), ++issued;
-    const int stage = it % NST;
-    const int j0 = klo + it * kKT;
-    const uint32_t sb = stage * STAGE_BYTES;
-
-    // partial S^T over this wave's quarter of the head dimension
-    f32x16_t s = (f32x16_t)(0.0f);
-    uint4 kw = make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < 2; ++r)
+    klb[r] = (uint32_t)((lane >> 3) * st_b + 16 * ((lane & 7) ^ (4 * r + (lane >> 4))));
 #pragma unroll
-    for (int i = 0; i < KKW; ++i) {
-      const int kk = wave * KKW + i;
-      uint4 a;
-      if constexpr (KV8) {
-        if ((i & 1) == 0) kw = *(const uint4*)(smem + sb + klane + (kk >> 1) * kKStep);
-        a = (i & 1) ? e5m2x8_to_f16(kw.z, kw.w) : e5m2x8_to_f16(kw.x, kw.y);
-      } else {
-        a = *(const uint4*)(smem + sb + klane + kk * kKStep);
+  for (int r = 0; r < 4; ++r) vlb[r] = (uint32_t)(lkey * st_b + 16 * swz_v<DPAD, ES>(r * KPI + lkey, lpos));
+
+  auto issue_k = [&]() {
+    const uint32_t dst0 = tl.tsb;
+    if (full_d && tl.fast()) {
+      const char* b = tl.kbase + tl.tA;
+#pragma unroll
+      for (int ri = 0; ri < HALF; ++ri)
+        dma16_sb(b + ((int64_t)(8 * (ri & 3)) * st_b + 128 * (ri >> 2)), klb[ri & 1], dst0 + ri * 1024);
+    } else {
+#pragma unroll
+      for (int ri = 0; ri < HALF; ++ri) {
+        int key = 8 * (ri & 3) + (lane >> 3);
+        int c = 8 * (ri >> 2) + ((lane & 7) ^ k_swz(key));
+        asm volatile("" : "+v"(key), "+v"(c));  // per tile, not hoisted into one register per instruction
+        c = min(c, dchunks - 1);
+        key = min(key, tl.tlast);  // past the group's last key: reload a valid key (finite data, masked)
+        dma16(tl.kbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
       }
-      s = Mf<QT>::run(a, qf[i], s);
     }
+  };
+  auto issue_v = [&]() {
+    const uint32_t dst0 = tl.tsb + TILE_BYTES;
+    if (full_d && tl.fast()) {
+      const char* b = tl.vbase + tl.tA;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) sx[wave][q4][lane] = (f32x4_t){s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-    lds_barrier();
-    // full scores, summed in the same order by every wave
+      for (int ri = 0; ri < HALF; ++ri) dma16_sb(b + (int64_t)(ri * KPI) * st_b, vlb[ri & 3], dst0 + ri * 1024);
+    } else {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4_t t = sx[0][q4][lane];
+      for (int ri = 0; ri < HALF; ++ri) {
+        int key = ri * KPI + lkey;
+        int c = swz_v<DPAD, ES>(key, lpos);
+        asm volatile("" : "+v"(key), "+v"(c));
+        c = min(c, dchunks - 1);
+        key = min(key, tl.tlast);
+        dma16(tl.vbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
+      }
+    }
+  };
+
+  drain_visible_loads();
+  int nh = 0;  // half-tiles issued, in the order K(0) V(0) K(1) V(1) ...
 #pragma unroll
-      for (int v = 1; v < WAVES; ++v) t += sx[v][q4][lane];
-      s[4 * q4] = t[0];
-      s[4 * q4 + 1] = t[1];
-      s[4 * q4 + 2] = t[2];
-      s[4 * q4 + 3] = t[3];
+  for (int i = 0; i < NSW; ++i)
+    if (i < nt_w) {
+      tl.fetch(i);
+      tl.begin(i);
+      issue_k();
+      issue_v();
+      nh += 2;
+    }
+
+  for (int i = 0; i < nt_w; ++i) {
+    const int st = NSW == 1 ? 0 : (i & 1);
+    const int j0 = klo + (wave + WAVES * i) * kKT;
+    const uint32_t sb = wbase + st * STAGE_BYTES;
+    const bool more = i + NSW < nt_w;
+
+    wait_tiles<HALF, 2 * NSW - 1>(nh - 2 * i - 1);  // K(i) landed
+    f32x16_t s0 = (f32x16_t)(0.0f), s1 = (f32x16_t)(0.0f);
+    if constexpr (KV8) {
+#pragma unroll
+      for (int kp = 0; kp < NKK / 2; ++kp) {
+        const uint4 kw = *(const uint4*)(smem + sb + k_frag(klane, kp));
+        s0 = Mf<QT>::run(e5m2x8_to_f16(kw.x, kw.y), qf[2 * kp], s0);
+        s1 = Mf<QT>::run(e5m2x8_to_f16(kw.z, kw.w), qf[2 * kp + 1], s1);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; kk += 2) {
+        s0 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk)), qf[kk], s0);
+        s1 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk + 1)), qf[kk + 1], s1);
+      }
+    }
+    f32x16_t s = s0 + s1;
+    if (more) {  // refill the K half of this stage with tile i + NSW
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      tl.fetch(i + NSW);
+      tl.begin(st);
+      issue_k();
+      ++nh;
     }
 
     float tmax = kNegInf;
@@ -166,7 +220,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
       const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
       lsum *= alpha;
 #pragma unroll
-      for (int j = 0; j < NDBW; ++j) oacc[j] *= alpha;
+      for (int j = 0; j < NDB; ++j) oacc[j] *= alpha;
       m = mnew;
     }
     const float mref = m == kNegInf ? 0.0f : m;
@@ -181,65 +235,92 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     }
     lsum += ls;
 
-    // O^T += V^T P^T for this wave's output columns
+    wait_tiles<HALF, 2 * NSW - 1>(nh - 2 * i - 2);  // V(i) landed
     const uint32_t vls = sb + vlane;
 #pragma unroll
-    for (int j = 0; j < NDBW; ++j) {
-      const int db = wave * NDBW + j;
-      if (db < NDB) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          uint4 a;
-          if constexpr (KV8) a = read_vt8(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
-          else a = read_vt(smem + (vls ^ (db << 6)) + ks * 16 * ROWB, 8 * ROWB);
-          oacc[j] = Mf<QT>::run(a, pf[ks], oacc[j]);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 a;
+        if constexpr (KV8) a = read_vt8(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
+        else a = read_vt(smem + (vls ^ (db << 6)) + ks * 16 * ROWB, 8 * ROWB);
+        oacc[db] = Mf<QT>::run(a, pf[ks], oacc[db]);
       }
+    }
+    if (more) {  // and its V half
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_v();
+      ++nh;
     }
   }
 
-  // ---- epilogue: FP32 record (o normalised, lse, pad); this wave's columns
+  // ---- combine the four waves' states, then the FP32 record of this part
   const float ltot = lsum + __shfl_xor(lsum, 32);
+  lds_barrier();  // every wave is done with its ring (all of its loads were waited for)
+  if (hi == 0) mlx[wave][r32] = make_float2(m, ltot);
+  f32x4_t* ox = (f32x4_t*)smem;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      ox[((wave * NDB + db) * 4 + rr) * 64 + lane] =
+          (f32x4_t){oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
+  lds_barrier();
+  float mv[WAVES], lv[WAVES];
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    const float2 t = mlx[v][r32];
+    mv[v] = t.x;
+    lv[v] = t.y;
+  }
+  float mall = mv[0];
+#pragma unroll
+  for (int v = 1; v < WAVES; ++v) mall = fmaxf(mall, mv[v]);
+  float av[WAVES];
+  float lall = 0.0f;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    av[v] = (mv[v] == kNegInf) ? 0.0f : fast_exp2(mv[v] - mall);
+    lall += av[v] * lv[v];
+  }
   if (!valid) return;
-  const bool empty = (m == kNegInf) || !(ltot > 0.0f);
-  const float inv = empty ? 0.0f : p.v_scale / ltot;
-  const float lse_nat = empty ? kNegInf : (m + __log2f(ltot)) * 0.69314718055994530942f;
+  const bool empty = (mall == kNegInf) || !(lall > 0.0f);
+  const float inv = empty ? 0.0f : p.v_scale / lall;
+  const float lse_nat = empty ? kNegInf : (mall + __log2f(lall)) * 0.69314718055994530942f;
   const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
   float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
 #pragma unroll
-  for (int j = 0; j < NDBW; ++j) {
-    const int db = wave * NDBW + j;
+  for (int j = 0; j < (NDB + WAVES - 1) / WAVES; ++j) {
+    const int db = wave + WAVES * j;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int d = db * 32 + 8 * rr + 4 * hi;
       if (db < NDB && d < p.head_dim) {
-        float2 a = {oacc[j][4 * rr + 0] * inv, oacc[j][4 * rr + 1] * inv};
-        float2 b = {oacc[j][4 * rr + 2] * inv, oacc[j][4 * rr + 3] * inv};
-        *(float2*)(rec + d) = a;
-        *(float2*)(rec + d + 2) = b;
+        f32x4_t o = (f32x4_t)(0.0f);
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) o += av[v] * ox[((v * NDB + db) * 4 + rr) * 64 + lane];
+        *(float2*)(rec + d) = make_float2(o[0] * inv, o[1] * inv);
+        *(float2*)(rec + d + 2) = make_float2(o[2] * inv, o[3] * inv);
       }
     }
   }
-  if (wave == 0 && hi == 0) {
-    float2 t = {lse_nat, 0.0f};
-    *(float2*)(rec + p.head_dim) = t;
-  }
+  if (wave == 0 && hi == 0) *(float2*)(rec + p.head_dim) = make_float2(lse_nat, 0.0f);
 }
 
 // ---- host side -------------------------------------------------------------
 
 namespace {
-template <typename QT, bool KV8, int DPAD, int NST>
+template <typename QT, bool KV8, int DPAD, int NSW>
 hipError_t launch_dec(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<QT, KV8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_decode_kernel<QT, KV8, DPAD, NSW>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 template <typename QT>
 hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
-    case 64: return launch_dec<QT, false, 64, 3>(p, nblocks, stream);
+    case 64: return launch_dec<QT, false, 64, 2>(p, nblocks, stream);
     case 128: return launch_dec<QT, false, 128, 2>(p, nblocks, stream);
-    case 256: return launch_dec<QT, false, 256, 2>(p, nblocks, stream);
+    case 256: return launch_dec<QT, false, 256, 1>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -250,7 +331,7 @@ hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t 
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream) {
   if (kv_kind == KV_E5M2) {
-    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 3>(p, nblocks, stream);
+    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 2>(p, nblocks, stream);
     return hipErrorInvalidValue;
   }
   if (q_kind != kv_kind) return hipErrorInvalidValue;

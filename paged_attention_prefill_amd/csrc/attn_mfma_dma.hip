@@ -124,16 +124,16 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 
   // S^T = K Q^T for this wave's rows, scale + mask, online softmax -> pf
   auto qk_softmax = [&](int stage, int j0) {
-    const uint32_t kls = stage * STAGE_BYTES + klane;
+    const uint32_t kls = stage * STAGE_BYTES;
     f32x16_t s[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s[rb] = (f32x16_t)(0.0f);
     // each K fragment read is issued one k-step ahead of the MFMA that uses it
-    uint4 a = *(const uint4*)(smem + kls);
+    uint4 a = *(const uint4*)(smem + kls + k_frag(klane, 0));
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       uint4 an;
-      if (kk + 1 < NKK) an = *(const uint4*)(smem + kls + (kk + 1) * kKStep);
+      if (kk + 1 < NKK) an = *(const uint4*)(smem + kls + k_frag(klane, kk + 1));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)

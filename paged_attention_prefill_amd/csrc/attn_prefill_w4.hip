@@ -192,12 +192,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   // vector memory unit takes them while the matrix cores are busy.
   auto qk = [&](int stage, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
-    const uint32_t kls = stage * STAGE_BYTES + klane;
+    const uint32_t kls = stage * STAGE_BYTES;
     // 16-bit K: one read per k-step; fp8 K: one 16-byte read per pair of k-steps
     constexpr int NRD = KV8 ? NKK / 2 : NKK;
     uint4 kf[KPF];
 #pragma unroll
-    for (int i = 0; i < KPF; ++i) kf[i] = *(const uint4*)(smem + kls + i * kKStep);
+    for (int i = 0; i < KPF; ++i) kf[i] = *(const uint4*)(smem + kls + k_frag(klane, i));
     uint4 kw = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
       uint4 a;
       if (!KV8 || (kk & 1) == 0) {
         kw = kf[rd % KPF];
-        if (rd + KPF < NRD) kf[rd % KPF] = *(const uint4*)(smem + kls + (rd + KPF) * kKStep);
+        if (rd + KPF < NRD) kf[rd % KPF] = *(const uint4*)(smem + kls + k_frag(klane, rd + KPF));
       }
       if constexpr (KV8) a = (kk & 1) ? e5m2x8_to_f16(kw.z, kw.w) : e5m2x8_to_f16(kw.x, kw.y);
       else a = kw;

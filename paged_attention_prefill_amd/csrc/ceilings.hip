@@ -40,16 +40,28 @@ __global__ __launch_bounds__(256, 1) void mfma_loop(const uint4* __restrict__ op
   }
 }
 
-__global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src, long long n16,
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Each block reads one contiguous range, eight 16-byte non-temporal loads per
+// lane in flight; every loaded word feeds the result so none is dropped.
+__global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ src, long long n16,
                                                    float* __restrict__ sink) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long per = ((n16 + gridDim.x - 1) / gridDim.x + 2047) / 2048 * 2048;
+  const long long lo = (long long)blockIdx.x * per;
+  const long long hi = lo + per < n16 ? lo + per : n16;
   uint32_t acc = 0;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    acc ^= v0.x ^ v1.y ^ v2.z ^ v3.w;
+  long long i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) acc ^= src[i].x;
+  for (; i < hi; i += 256) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
   sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc & 1u);
 }
 
@@ -68,7 +80,7 @@ int pa_ceiling_mfma(const void* operands, float* sink, int32_t blocks, int32_t i
 int pa_ceiling_stream_read(const void* src, int64_t bytes, float* sink, int32_t blocks, void* stream_) {
   const hipStream_t stream = (hipStream_t)stream_;
   if (!src || !sink || blocks <= 0 || bytes < 16 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return -1;
-  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (long long)(bytes / 16), sink);
+  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, stream, (const u32x4*)src, (long long)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

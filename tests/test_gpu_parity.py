@@ -380,7 +380,7 @@ def test_long_chunk_prefill_sampled(splits):
             lse[rows[:, 0], rows[:, 1]], rl)
     # the q=1 decode row over the same cache
     dec = gen.select_seqs(c, [1])
-    od, ld = gpu_decode(dec, splits=128, max_q=1)
+    od, ld = gpu_decode(dec, splits=64, max_q=1)
     rd, rld = run_oracle(dec, pools=(k, v))
     compare("long chunk decode row", "f16", od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
 
@@ -390,7 +390,7 @@ def test_mixed_step_sampled(kv_kind):
     c = gen.mixed_step(kv_kind=kv_kind)
     k, v = oracle_pools(c)
     ver = gen.select_seqs(c, [0])
-    od, ld = gpu_decode(ver, splits=128, max_q=5)
+    od, ld = gpu_decode(ver, splits=64, max_q=5)
     rd, rld = run_oracle(ver, pools=(k, v))
     compare(f"mixed verify row {kv_kind}", kv_kind, od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
     chunk = gen.select_seqs(c, [1])
