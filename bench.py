@@ -13,8 +13,9 @@ Prints ONE JSON line.  `value` is the step's algorithmic FLOPs (causal-exact:
 4 * D * Hq per attended pair) divided by the step time; the prefill TFLOPS and
 the decode GB/s are reported beside it, each from HIP events recorded on the
 stream the kernels run on.  `roofline` prices the dominant kernel (the prefill
-attention kernel) against the MFMA fp16 dense peak; `decode_roofline` prices
-the decode against the HBM peak.  `cpu_baseline` times the fp64 oracle on a
+attention kernel, timed alone: a split prefill runs as pass 1 and the merge
+with an event between them) against the MFMA fp16 dense peak;
+`decode_roofline` prices the decode call against the HBM peak.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload on the host cores.
 """
 
@@ -49,8 +50,9 @@ def kernel_sources_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload_name, part):
-    """HBM bytes per launch from the rocprofv3 counter runs, if taken on these sources."""
+def measured_traffic(workload_name, part, key="hbm_bytes_per_call"):
+    """HBM bytes per call (or, key="hbm_bytes_kernel", of its attention kernel alone) from the
+    rocprofv3 counter runs, if taken on these sources."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -58,7 +60,7 @@ def measured_traffic(workload_name, part):
     if t.get("sources_sha256") != kernel_sources_hash():
         return None
     e = t.get("workloads", {}).get(workload_name, {}).get(part)
-    return None if e is None else e.get("hbm_bytes_per_call")
+    return None if e is None else e.get(key)
 
 
 def log(*a):
@@ -80,6 +82,7 @@ class Call:
             nb = ops.decode_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
         self.ws = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=d["q"].device)
         self.times = []
+        self.pass1 = []  # (start, end of the attention kernel) of a split prefill
 
     def __call__(self, stream, record=False):
         c, d = self.case, self.d
@@ -87,7 +90,17 @@ class Call:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if self.kind == "prefill":
+        if self.kind == "prefill" and self.splits > 1:
+            # the two passes apart, so that the attention kernel is timed alone
+            parts = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
+                                      c.scale, k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits,
+                                      workspace=self.ws, stream=stream, merge=False)
+            if record:
+                em = torch.cuda.Event(enable_timing=True)
+                em.record(stream)
+                self.pass1.append((e0, em))
+            ops.merge_states(parts, self.out.dtype, out=self.out, lse=self.lse, stream=stream)
+        elif self.kind == "prefill":
             ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
                               k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits, out=self.out,
                               lse=self.lse, workspace=self.ws, stream=stream)
@@ -104,6 +117,12 @@ class Call:
 
     def ms_median(self):
         return float(np.median([a.elapsed_time(b) for a, b in self.times])) if self.times else float("nan")
+
+    def kernel_ms(self):
+        """Mean duration of the attention kernel alone (the whole call when it is one kernel)."""
+        if not self.pass1:
+            return self.ms()
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pass1]))
 
 
 # The calls of one step of each workload, in launch order.
@@ -258,7 +277,9 @@ def write_traffic(workload_name, pmc_dir):
         fetch = [float(np.mean([c[j][1] for c in f_calls])) for j in range(len(names))]
         write = [float(np.mean([c[j][1] for c in w_calls])) for j in range(len(names))]
         total = 1024.0 * (sum(fetch) * factors["FETCH_SIZE"] + sum(write) * factors["WRITE_SIZE"])
-        entry[kind] = {"kernels": names, "fetch_kib": fetch, "write_kib": write, "hbm_bytes_per_call": total}
+        first = 1024.0 * (fetch[0] * factors["FETCH_SIZE"] + write[0] * factors["WRITE_SIZE"])
+        entry[kind] = {"kernels": names, "fetch_kib": fetch, "write_kib": write, "hbm_bytes_per_call": total,
+                       "hbm_bytes_kernel": first}
     out["workloads"][workload_name] = entry
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -393,7 +414,9 @@ def main():
         if c.kind == "prefill":
             f = call_flops(c.kind, c.case)
             step_flops += f
+            kms = c.kernel_ms()
             parts["prefill"] = {"ms": ms, "ms_median": c.ms_median(), "tflops": f / (ms * 1e-3) / 1e12, "flops": f,
+                                "kernel_ms": kms, "kernel_tflops": f / (kms * 1e-3) / 1e12,
                                 "splits": c.splits, "name": c.case.name}
         else:
             b = call_bytes(c.kind, c.case, c.splits)
@@ -409,10 +432,11 @@ def main():
     res.update(parts)
     if "prefill" in parts:
         pf = parts["prefill"]
-        res["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS,
-                           "traffic": measured_traffic(a.workload, "prefill"),
-                           "kernel": prefill_kernel_name(desc) + " (+ merge_kernel when the keys are split)"}
+        res["roofline"] = {"bound": "mfma", "achieved": pf["kernel_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": pf["kernel_tflops"] / MFMA_F16_PEAK_TFLOPS,
+                           "traffic": measured_traffic(a.workload, "prefill", "hbm_bytes_kernel"),
+                           "kernel": prefill_kernel_name(desc),
+                           "kernel_ms": pf["kernel_ms"]}
     if "decode" in parts:
         dc = parts["decode"]
         res["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -116,6 +116,10 @@ typedef struct pa_kv_cache {
  *   With num_kv_splits != 1 the workspace must hold
  *   pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits)
  *   bytes of device memory (float-aligned); otherwise it may be NULL.
+ *   out (with lse) may be NULL when num_kv_splits >= 2: then only the first
+ *   pass runs and the workspace holds the FP32 records [total_q, num_q_heads,
+ *   num_kv_splits, head_dim + 2] for pa_merge_states (a caller that merges
+ *   these states with others, or times the passes apart).
  */
 int pa_paged_prefill(const void *q, int32_t q_dtype, void *out, float *lse,
                      const int32_t *cu_seqlens_q, const int32_t *seq_lens,
@@ -135,6 +139,8 @@ int pa_paged_prefill(const void *q, int32_t q_dtype, void *out, float *lse,
  *   output, its lse, one pad -- into the workspace laid out
  *   [total_q, num_q_heads, num_splits, head_dim + 2]; pass 2 (the merge)
  *   writes out and lse.  workspace_bytes >= pa_decode_workspace_bytes(...).
+ *   out (with lse) may be NULL: then only pass 1 runs and the records are left
+ *   in the workspace for pa_merge_states.
  */
 int pa_split_kv_decode(const void *q, int32_t q_dtype, void *out, float *lse,
                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,

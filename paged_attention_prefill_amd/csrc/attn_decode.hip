@@ -174,6 +174,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
       issue_v();
       nh += 2;
     }
+  // page ids are read one tile ahead of their use, so that the scalar loads
+  // are never waited for on the way to a refill
+  if (NSW < nt_w) tl.fetch(NSW);
 
   for (int i = 0; i < nt_w; ++i) {
     const int st = NSW == 1 ? 0 : (i & 1);
@@ -198,9 +201,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
       }
     }
     f32x16_t s = s0 + s1;
-    if (more) {  // refill the K half of this stage with tile i + NSW
+    if (more) {  // refill the K half of this stage with tile i + NSW (page ids fetched before)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      tl.fetch(i + NSW);
       tl.begin(st);
       issue_k();
       ++nh;
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue_v();
       ++nh;
+      if (i + NSW + 1 < nt_w) tl.fetch(i + NSW + 1);
     }
   }
 

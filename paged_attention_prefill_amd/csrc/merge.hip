@@ -2,14 +2,17 @@
 // (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode; also the log-sum-exp
 // merge of key-split prefill tiles, 1CatAI/1Cat-vLLM PR #1279, commit 5).
 //
-// One work group of 256 threads per (token, head).  Record s = (o_s[0..D),
+// One work group per (token, head): 256 threads, or 1024 when a row has 16
+// or more parts, so that each thread reads at most a few parts and the pass
+// costs about one memory round trip.  Record s = (o_s[0..D),
 // lse_s, pad) with o_s normalised.  M = max_s lse_s; w_s = exp(lse_s - M);
 // o = sum_s w_s o_s / sum_s w_s; lse = M + log sum_s w_s.  All parts empty ->
 // o = 0, lse = -inf; an empty part's o_s is never read into the sum.
 //
 // Thread t owns a pair of output columns (t % (D/2)) and a contiguous run of
 // parts (t / (D/2)); the runs are summed in ascending part order and then
-// combined in ascending run order.  The order depends only on S and D, so a
+// combined in ascending run order.  The order depends only on S and D (the
+// block size is a function of S), so a
 // row's result does not depend on the other rows of the call (batch
 // invariance), and the many parts of a long decode row are read in parallel.
 
@@ -18,7 +21,6 @@
 namespace pa {
 
 namespace {
-constexpr int kMT = 256;
 constexpr float kNegInfM = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -28,10 +30,11 @@ template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, floa
 }
 }  // namespace
 
-template <typename OT>
+template <typename OT, int kMT>
 __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ partials, int S, int D,
                                                     OT* __restrict__ out, float* __restrict__ out_lse) {
-  __shared__ float red[kMT / 64];
+  constexpr int NW = kMT / 64;
+  __shared__ float red[NW];
   __shared__ float2 part[kMT];
   __shared__ float dpart[kMT];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -46,16 +49,18 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
 
   const int DC = D >> 1;                 // float2 column pairs
-  const int SG = kMT / DC;               // runs of parts (>= 1 since D <= 256... D/2 <= 128)
+  const int SG = kMT / DC;               // runs of parts (>= 2 since D / 2 <= 128)
   const int dc = t % DC, sg = t / DC;
   const int per = (S + SG - 1) / SG;
   const int s0 = sg * per, s1 = min(S, s0 + per);
   float ax = 0.0f, ay = 0.0f, den = 0.0f;
   if (M != kNegInfM && sg < SG) {
-#pragma unroll 4
+#pragma unroll 8
     for (int s = s0; s < s1; ++s) {
       const float* r = rec + (int64_t)s * R;
       const float ls = r[D];
@@ -90,8 +95,12 @@ static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D,
                            hipStream_t stream) {
   const int64_t rows = (int64_t)ntok * H;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<OT>), dim3((unsigned)rows), dim3(kMT), 0, stream, partials, S, D, (OT*)out,
-                     out_lse);
+  if (S >= 16)
+    hipLaunchKernelGGL((merge_kernel<OT, 1024>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
+                       (OT*)out, out_lse);
+  else
+    hipLaunchKernelGGL((merge_kernel<OT, 256>), dim3((unsigned)rows), dim3(256), 0, stream, partials, S, D,
+                       (OT*)out, out_lse);
   return hipGetLastError();
 }
 

@@ -320,7 +320,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
                                         : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (partial) {
+  if (partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
     e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
@@ -336,8 +336,8 @@ static int check_common(const void* q, int q_dtype, void* out, const int32_t* cu
   int st = check_kv(kv, q_dtype, hq);
   if (st != PA_OK) return st;
   if (num_seqs == 0 || total_q == 0) return PA_OK;
-  if (!q || !out || !cu || !seq_lens || !bt) return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARGUMENT, "q / out must be 16-byte aligned");
+  if (!q || !cu || !seq_lens || !bt) return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(q) || (out && !aligned16(out))) return fail(PA_ERR_INVALID_ARGUMENT, "q / out must be 16-byte aligned");
   if (max_q < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max q length must be >= 1 when total_q > 0");
   return PA_OK;
 }
@@ -353,6 +353,8 @@ int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, cons
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
   if (num_kv_splits < 0 || num_kv_splits > 64) return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_splits must be in [0, 64]");
+  if (out == nullptr && (num_kv_splits < 2 || lse != nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "out may be NULL only with num_kv_splits >= 2 and lse NULL");
   if (num_seqs == 0 || total_q == 0) return ok();
   int splits = num_kv_splits;
   if (splits != 1) {
@@ -385,6 +387,7 @@ int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, co
     return fail(PA_ERR_UNSUPPORTED, "max_q_per_row %d > %d (longer rows go to pa_paged_prefill)", max_q_per_row,
                 PA_DECODE_MAX_Q);
   if (num_splits < 1 || num_splits > 4096) return fail(PA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 4096]");
+  if (out == nullptr && lse != nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "lse must be NULL when out is NULL");
   if (num_rows == 0 || total_q == 0) return ok();
   const size_t need = pa_decode_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_splits);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u))

@@ -151,17 +151,28 @@ def _workspace(workspace, nbytes, device):
     return workspace
 
 
+def _partials_view(workspace, total_q, Hq, D, splits):
+    n = total_q * Hq * splits * (D + 2)
+    return workspace.view(torch.float32)[:n].view(total_q, Hq, splits, D + 2)
+
+
 def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_seqlen_q, scale,
                   *, k_scale=1.0, v_scale=1.0, num_kv_splits=1, out=None, lse=None,
-                  return_lse=False, workspace=None, stream=None):
-    """pa_paged_prefill on torch tensors; returns out (and lse)."""
+                  return_lse=False, workspace=None, stream=None, merge=True):
+    """pa_paged_prefill on torch tensors; returns out (and lse).
+
+    merge=False (num_kv_splits >= 2): runs the first pass only and returns the
+    FP32 records [total_q, Hq, num_kv_splits, D + 2] for merge_states."""
     total_q, Hq, D = q.shape
     if not q.is_contiguous():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
     kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    if merge:
+        out = torch.empty_like(q) if out is None else out
+        if return_lse and lse is None:
+            lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    else:
+        out = lse = None
     B = int(seq_lens.numel())
     ws_bytes = prefill_workspace_bytes(total_q, Hq, D, num_kv_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
@@ -171,20 +182,28 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
                                   _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
                                   total_q, int(max_seqlen_q), Hq, ctypes.byref(kv), float(scale),
                                   int(num_kv_splits), _ptr(workspace), ws_have, _stream(stream)))
+    if not merge:
+        return _partials_view(workspace, total_q, Hq, D, num_kv_splits)
     return (out, lse) if return_lse or lse is not None else out
 
 
 def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
                     *, num_splits=16, k_scale=1.0, v_scale=1.0, out=None, lse=None,
-                    return_lse=False, workspace=None, stream=None):
-    """pa_split_kv_decode on torch tensors; returns out (and lse)."""
+                    return_lse=False, workspace=None, stream=None, merge=True):
+    """pa_split_kv_decode on torch tensors; returns out (and lse).
+
+    merge=False: runs pass 1 only and returns the FP32 records
+    [total_q, Hq, num_splits, D + 2] for merge_states."""
     total_q, Hq, D = q.shape
     if not q.is_contiguous():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
     kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    if merge:
+        out = torch.empty_like(q) if out is None else out
+        if return_lse and lse is None:
+            lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    else:
+        out = lse = None
     B = int(seq_lens.numel())
     ws_bytes = decode_workspace_bytes(total_q, Hq, D, num_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
@@ -194,6 +213,8 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
                                     _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
                                     total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale),
                                     int(num_splits), _ptr(workspace), ws_have, _stream(stream)))
+    if not merge:
+        return _partials_view(workspace, total_q, Hq, D, num_splits)
     return (out, lse) if return_lse or lse is not None else out
 
 

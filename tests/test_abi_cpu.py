@@ -161,3 +161,19 @@ def test_merge_rejects_bad_arguments():
     assert L.pa_merge_states(0x1000, 4, 4, 4, 64, 0x2000, ops.PA_FP8_E5M2, None, None) == ops.PA_ERR_UNSUPPORTED
     assert L.pa_merge_states(None, 4, 4, 4, 64, 0x2000, ops.PA_F16, None, None) == ops.PA_ERR_INVALID_ARGUMENT
     assert L.pa_merge_states(0x1000, 4, 0, 4, 64, 0x2000, ops.PA_F16, None, None) == ops.PA_OK
+
+
+def test_out_null_needs_split_and_no_lse():
+    """out may be NULL (pass 1 only) for a split prefill without lse, and for a decode without lse."""
+    kv = _fake_kv()
+    assert _prefill(kv, out=None) == ops.PA_ERR_INVALID_ARGUMENT  # one split: no pass to stop after
+    assert _prefill(kv, out=None, splits=0) == ops.PA_ERR_INVALID_ARGUMENT  # auto may choose one
+    assert _prefill(kv, out=None, splits=2, lse=0x90000) == ops.PA_ERR_INVALID_ARGUMENT
+    assert _prefill(kv, out=None, splits=2) == ops.PA_ERR_WORKSPACE  # accepted up to the workspace check
+    L = ops.lib()
+
+    def dec(out, lse):
+        return L.pa_split_kv_decode(0x30000, ops.PA_F16, out, lse, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
+                                    ctypes.byref(kv), 0.1, 16, None, 0, None)
+    assert dec(None, 0x90000) == ops.PA_ERR_INVALID_ARGUMENT
+    assert dec(None, None) == ops.PA_ERR_WORKSPACE

@@ -322,6 +322,31 @@ def test_merge_states_matches_oracle_merge():
     assert np.isneginf(lse[0, 0].item()) and not out[0, 0].any()
 
 
+def test_first_pass_only_then_merge_equals_the_merged_call():
+    """out = NULL leaves the FP32 records in the workspace; merge_states over them gives the merged call's
+    output and lse bit for bit (prefill with a key split, and decode)."""
+    c = gen.make_case("p1", q_lens=[40, 3], seq_lens=[500, 1300], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      page_size=48, q_kind="bf16", seed=63)
+    d = gen.to_device(c)
+    out, lse = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
+                                 num_kv_splits=3, return_lse=True)
+    parts = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
+                              num_kv_splits=3, merge=False)
+    assert parts.shape == (c.total_q, 8, 3, 130)
+    o2, l2 = ops.merge_states(parts, torch.bfloat16, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), out.view(torch.int16)) and torch.equal(l2, lse)
+    one = gen.select_seqs(c, [1])
+    dd = gen.to_device(one)
+    out, lse = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 3, one.scale,
+                                   num_splits=7, return_lse=True)
+    parts = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 3, one.scale,
+                                num_splits=7, merge=False)
+    o2, l2 = ops.merge_states(parts, torch.bfloat16, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), out.view(torch.int16)) and torch.equal(l2, lse)
+
+
 # ------------------------------------------------------------------ fp8 KV
 
 def test_fp8_prefill_and_decode_small():
