@@ -290,12 +290,14 @@ def write_traffic(workload_name, pmc_dir):
 
 def ceilings(seed=0):
     """Measured chip ceilings beside the published peaks: a pure MFMA loop on
-    random and on zero fp16 operands (with the shader clock it ran at) and a
+    random and on zero fp16 operands (with the shader clock it ran at), the same
+    loop fed a fresh random A fragment from LDS for every pair of MFMAs, and a
     streaming read of 4 GiB."""
     import ctypes
     L = ops.lib()
     P, I = ctypes.c_void_p, ctypes.c_int32
     L.pa_ceiling_mfma.argtypes = [P, P, I, I, P, P]
+    L.pa_ceiling_mfma_lds.argtypes = [P, P, I, I, P, P]
     L.pa_ceiling_stream_read.argtypes = [P, ctypes.c_int64, P, I, P]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
@@ -331,6 +333,19 @@ def ceilings(seed=0):
         flops = blocks * 4 * iters * 4 * 32768
         res[f"mfma_f16_{kind}_tflops"] = flops / (ms * 1e-3) / 1e12
         res[f"mfma_f16_{kind}_clock_ghz"] = ghz
+        res[f"mfma_f16_{kind}_cycles_per_mfma"] = float(torch.median(c[:, 0])) / (iters * 4)
+    # fresh A fragments from LDS for every pair of MFMAs (attention's operand traffic)
+    ops_lds = torch.randn((2048 + 256) * 8, generator=g).half().cuda()
+
+    def run_lds():
+        st = L.pa_ceiling_mfma_lds(ctypes.c_void_p(ops_lds.data_ptr()), ctypes.c_void_p(sink.data_ptr()), blocks,
+                                   iters, ctypes.c_void_p(clocks.data_ptr()), sp)
+        assert st == 0, st
+    ms = timed(run_lds, 3)
+    c = clocks.view(-1, 2).cpu().double()
+    res["mfma_f16_lds_random_tflops"] = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    res["mfma_f16_lds_random_clock_ghz"] = float(torch.median(c[:, 0] / c[:, 1]) * 0.1)
+    res["mfma_f16_lds_random_cycles_per_mfma"] = float(torch.median(c[:, 0])) / (iters * 4)
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
     rsink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")

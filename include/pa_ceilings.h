@@ -9,6 +9,12 @@
  *   clocks[2 b + 1] receive work group b's elapsed shader-clock and 100 MHz
  *   real-time ticks.  Asynchronous on `stream` (a hipStream_t); 0 = launched, -1 = bad
  *   argument, -4 = launch error.
+ * pa_ceiling_mfma_lds: the same loop, but every pair of MFMAs takes a new A
+ *   fragment read from LDS (the operand traffic of attention's S^T phase):
+ *   operands[0..2047] (32 KB of 16-byte fp16 fragments, copied to LDS) and
+ *   operands[2048..2303] (four register fragments); per iteration 2 LDS reads
+ *   and 4 MFMAs (iters is rounded down to even).  sink / clocks / return
+ *   codes as pa_ceiling_mfma.
  * pa_ceiling_stream_read: `blocks` x 256 threads read `bytes` (a multiple of
  *   16, 16-byte aligned) of `src` once with 16-byte non-temporal loads, each
  *   block one contiguous range; sink[blocks * 256] receives one float per
@@ -25,6 +31,8 @@ extern "C" {
 
 int pa_ceiling_mfma(const void *operands, float *sink, int32_t blocks, int32_t iters,
                     unsigned long long *clocks, void *stream);
+int pa_ceiling_mfma_lds(const void *operands, float *sink, int32_t blocks, int32_t iters,
+                        unsigned long long *clocks, void *stream);
 int pa_ceiling_stream_read(const void *src, int64_t bytes, float *sink, int32_t blocks, void *stream);
 
 #ifdef __cplusplus

@@ -253,17 +253,18 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
       tmax[rb] = max_halves(tmax[rb]) * c;
       need[rb] = __any(tmax[rb] > m[rb] + kTau);
     } else if (k == 5) {
-      const float mnew = need[rb] ? fmaxf(m[rb], tmax[rb]) : m[rb];
+      const float mnew = need[rb] ? max2f(m[rb], tmax[rb]) : m[rb];
       alpha[rb] = (need[rb] && mnew != kNegInf) ? fast_exp2(m[rb] - mnew) : 1.0f;
       m[rb] = mnew;
       nref[rb] = mnew == kNegInf ? 0.0f : -mnew;
-      ls[rb] = 0.0f;
     } else if (k < 14) {
       const int q = k - 6;  // elements 2q, 2q + 1 -> packed word q
       const float e0 = fast_exp2(__builtin_fmaf(s[rb][2 * q], c, nref[rb]));
       const float e1 = fast_exp2(__builtin_fmaf(s[rb][2 * q + 1], c, nref[rb]));
-      ls[rb] += e0 + e1;
-      ((uint32_t*)pnew[rb])[q] = Mf<QT>::pack2(e0, e1);
+      const uint32_t pk = Mf<QT>::pack2(e0, e1);
+      ((uint32_t*)pnew[rb])[q] = pk;
+      // the row sum adds the rounded P that the PV product uses
+      ls[rb] = Mf<QT>::sum2(pk, q == 0 ? 0.0f : ls[rb]);
     } else {
       lsum[rb] = __builtin_fmaf(lsum[rb], alpha[rb], ls[rb]);
     }

@@ -1,6 +1,9 @@
 // Measured ceilings of the chip, reported beside the published peaks: a pure
 // MFMA loop (v_mfma_f32_32x32x16_f16, four independent accumulators per wave,
-// one wave per SIMD) and a streaming read.  Not part of the attention path.
+// one wave per SIMD) on fixed operands, the same loop fed a fresh A fragment
+// from LDS for every pair of MFMAs (the operand traffic of attention's S^T
+// phase: new K data each k-step, two query blocks per fragment), and a
+// streaming read.  Not part of the attention path.
 //
 // The MFMA loop also reads the shader clock (s_memtime) and the 100 MHz
 // real-time counter (s_memrealtime) at its start and end, so the clock the
@@ -29,6 +32,58 @@ __global__ __launch_bounds__(256, 1) void mfma_loop(const uint4* __restrict__ op
     c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c2, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c3, 0, 0, 0);
   }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// operands: 2048 16-byte fragments (32 KB, copied to LDS) then 4 x 64 B
+// fragments kept in registers
+__global__ __launch_bounds__(256, 1) void mfma_lds_loop(const uint4* __restrict__ operands,
+                                                         float* __restrict__ sink, int iters,
+                                                         unsigned long long* __restrict__ clocks) {
+  __shared__ uint4 pool[2048];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < 2048; i += 256) pool[i] = operands[i];
+  const half8_t b0 = __builtin_bit_cast(half8_t, operands[2048 + lane]);
+  const half8_t b1 = __builtin_bit_cast(half8_t, operands[2048 + 64 + lane]);
+  const half8_t b2 = __builtin_bit_cast(half8_t, operands[2048 + 128 + lane]);
+  const half8_t b3 = __builtin_bit_cast(half8_t, operands[2048 + 192 + lane]);
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  f32x16_t c0 = (f32x16_t)(0.0f), c1 = c0, c2 = c0, c3 = c0;
+  // fragment f (of 32) is pool[64 f + lane]; iteration it uses fragments 2 it, 2 it + 1 (mod 32),
+  // read one iteration ahead.  The reads are issued from inline assembly with the wait written
+  // out (lgkmcnt(2): the pair read last may still be in flight), so the loop measures the
+  // matrix cores and not the LDS latency.
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t base = (uint32_t)(uintptr_t)&pool[lane];
+  i32x4 a0, a1, n0, n1;
+  uint32_t addr = base;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024" : "=v"(a0), "=v"(a1) : "v"(addr) : "memory");
+  for (int it = 0; it + 1 < iters; it += 2) {
+    const uint32_t af = base + (uint32_t)(((2 * it + 2) & 31) * 1024);
+    const uint32_t ag = base + (uint32_t)(((2 * it + 4) & 31) * 1024);
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024" : "=v"(n0), "=v"(n1) : "v"(af) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a0), "+v"(a1) :: "memory");
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a0), b0, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a0), b1, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a1), b2, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a1), b3, c3, 0, 0, 0);
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024" : "=v"(a0), "=v"(a1) : "v"(ag) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(n0), "+v"(n1) :: "memory");
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, n0), b0, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, n0), b1, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, n1), b2, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, n1), b3, c3, 0, 0, 0);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a0), "+v"(a1) :: "memory");
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
@@ -74,6 +129,15 @@ int pa_ceiling_mfma(const void* operands, float* sink, int32_t blocks, int32_t i
   const hipStream_t stream = (hipStream_t)stream_;
   if (!operands || !sink || !clocks || blocks <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, stream, (const uint4*)operands, sink, iters, clocks);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int pa_ceiling_mfma_lds(const void* operands, float* sink, int32_t blocks, int32_t iters,
+                        unsigned long long* clocks, void* stream_) {
+  const hipStream_t stream = (hipStream_t)stream_;
+  if (!operands || !sink || !clocks || blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_lds_loop, dim3(blocks), dim3(256), 0, stream, (const uint4*)operands, sink, iters,
+                     clocks);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -114,6 +114,11 @@ template <> struct Mf<_Float16> {
     h2 v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // acc + both halves of a packed pair, products and sum in fp32 (one v_dot2)
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, p), (h2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  }
 };
 template <> struct Mf<__bf16> {
   static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
@@ -124,6 +129,10 @@ template <> struct Mf<__bf16> {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     b2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, p), (b2){(__bf16)1.0f, (__bf16)1.0f}, acc, false);
   }
 };
 
@@ -142,6 +151,11 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 
@@ -277,8 +291,12 @@ struct TileLoader {
     nx_off += kstep;
     while (nx_off >= P) nx_off -= P, ++nx_pg;
     f_first = P - f_off;  // keys of the tile on the first page (a multiple of 16)
+    // both ids are loaded without a branch on the first (the second page's id
+    // is only used when the tile reaches it; otherwise the first is re-read),
+    // so nothing waits for these loads before the tile's refill begins
+    const int pg2 = (f_first < kKT && (pg + 1) * P < kend) ? pg + 1 : pg;
     f_pa = btc[pg];
-    f_pb = (f_first < kKT && (pg + 1) * P < kend) ? btc[pg + 1] : f_pa;
+    f_pb = btc[pg2];
   }
 
   // Page bases of the fetched tile, to be loaded into `stage`.
