@@ -160,7 +160,7 @@ def build_workload(name):
         c = gen.decode_batch(kind="bf16")
         desc = {"workload": "split-KV decode batch: 32 rows q=1, lengths 0..10000, MHA 16 heads, D 128, page 16",
                 "num_q_heads": 16, "num_kv_heads": 16, "head_dim": 128, "page_size": 16, "kv_dtype": "bf16"}
-        return desc, [("decode", c, 8)]
+        return desc, [("decode", c, 16)]
     if name == "varlen":
         c = gen.varlen_prefill(kind="bf16")
         desc = {"workload": "varlen paged prefill: q 64/300/1024/2048 after 0/777/4096/8192, Hq 32, Hkv 8, D 128, "

@@ -25,8 +25,13 @@ using namespace mf;
 // in flight.  KV8: K and V are fp8 E5M2 (q fp16), 8-bit tiles in LDS widened
 // to fp16 as the MFMA operands are read.  The combined result depends only on
 // the row's own length and the part count.
+// Head dims up to 128 are held to 256 registers so that two groups share a CU
+// (with one ring stage per wave at D 128: 64 KB of LDS per group): a decode
+// batch has many short parts, and a second resident group hides each part's
+// first-tile latency.
 template <typename QT, bool KV8, int DPAD, int NSW>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DPAD <= 128 ? 2 : 1)))
+void attn_decode_kernel(const AttnParams p) {
   constexpr int WAVES = 4;
   typedef TileLoader<DPAD, 1, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
@@ -322,7 +327,7 @@ template <typename QT>
 hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
     case 64: return launch_dec<QT, false, 64, 2>(p, nblocks, stream);
-    case 128: return launch_dec<QT, false, 128, 2>(p, nblocks, stream);
+    case 128: return launch_dec<QT, false, 128, 1>(p, nblocks, stream);
     case 256: return launch_dec<QT, false, 256, 1>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
