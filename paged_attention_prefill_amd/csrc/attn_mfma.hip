@@ -111,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 
   int w = xcd_remap(blockIdx.x);
   if (w >= p.num_work) return;
-  const int qtile = w % p.qtiles;
+  // a sequence's last query tiles see the most keys: they are handed out first
+  const int qtile = p.qtiles - 1 - w % p.qtiles;
   w /= p.qtiles;
   const int split = w % p.num_splits;
   w /= p.num_splits;

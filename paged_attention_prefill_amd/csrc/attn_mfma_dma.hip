@@ -50,7 +50,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 
   int w = xcd_remap(blockIdx.x);
   if (w >= p.num_work) return;
-  const int qtile = w % p.qtiles;
+  // a sequence's last query tiles see the most keys: they are handed out first
+  const int qtile = p.qtiles - 1 - w % p.qtiles;
   w /= p.qtiles;
   const int split = w % p.num_splits;
   w /= p.num_splits;

@@ -41,14 +41,17 @@ struct AttnParams {
 // Block index -> work index.  Work groups are handed to the 8 XCDs round
 // robin; runs of kXcdGroup consecutive work items (neighbouring query tiles of
 // one sequence, kv head and key part, which read the same K/V) are kept on one
-// XCD so that they share its L2, and successive runs go to successive XCDs so
-// that every XCD gets a share of every sequence.  The grid is padded to a
-// multiple of 8 * kXcdGroup; the mapping is a bijection on the padded range
-// whatever the real placement is, so it only affects locality.
+// XCD so that they share its L2.  Row r of 8 runs goes to the 8 XCDs rotated
+// by r, so that a pattern of busy and empty runs that repeats every 2, 4 or 8
+// runs (a static grid sized for the longest sequence leaves such holes behind
+// the shorter ones) is spread over all XCDs instead of piling on some.  The
+// grid is padded to a multiple of 8 * kXcdGroup; the mapping is a bijection on
+// the padded range, so it only affects locality and balance.
 constexpr int kXcdGroup = 16;
 __device__ __forceinline__ int xcd_remap(int bid) {
   const int xcd = bid & 7, k = bid >> 3;
-  return ((k / kXcdGroup) * 8 + xcd) * kXcdGroup + (k % kXcdGroup);
+  const int row = k / kXcdGroup;
+  return (row * 8 + ((xcd - row) & 7)) * kXcdGroup + (k % kXcdGroup);
 }
 
 // Key range [lo, hi) of part `s` of a row with L keys cut into S parts of
