@@ -113,7 +113,9 @@ void attn_decode_kernel(const AttnParams p) {
                               : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
 
   // DMA of the K or V half of the tile begun last (one wave issues all of a
-  // tile's instructions).  K instruction ri fills block ri (keys 8 (ri % 4) ..,
+  // tile's instructions), with the non-temporal cache policy: a part's keys
+  // are read once, and streaming them past the caches instead of allocating
+  // lines for them moves the q=1 row over a 152K-token cache 14 % faster.  K instruction ri fills block ri (keys 8 (ri % 4) ..,
   // chunks 8 (ri / 4) ..), V instruction ri keys KPI ri ..; the per-lane part
   // of the source offset repeats every 2 (K) or 4 (V) instructions and the rest
   // is uniform, so a whole-tile, whole-row load keeps 6 per-lane offsets
@@ -136,7 +138,7 @@ void attn_decode_kernel(const AttnParams p) {
       const char* b = tl.kbase + tl.tA;
 #pragma unroll
       for (int ri = 0; ri < HALF; ++ri)
-        dma16_sb(b + ((int64_t)(8 * (ri & 3)) * st_b + 128 * (ri >> 2)), klb[ri & 1], dst0 + ri * 1024);
+        dma16_sb<true>(b + ((int64_t)(8 * (ri & 3)) * st_b + 128 * (ri >> 2)), klb[ri & 1], dst0 + ri * 1024);
     } else {
 #pragma unroll
       for (int ri = 0; ri < HALF; ++ri) {
@@ -145,7 +147,7 @@ void attn_decode_kernel(const AttnParams p) {
         asm volatile("" : "+v"(key), "+v"(c));  // per tile, not hoisted into one register per instruction
         c = min(c, dchunks - 1);
         key = min(key, tl.tlast);  // past the group's last key: reload a valid key (finite data, masked)
-        dma16(tl.kbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
+        dma16<true>(tl.kbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
       }
     }
   };
@@ -154,7 +156,7 @@ void attn_decode_kernel(const AttnParams p) {
     if (full_d && tl.fast()) {
       const char* b = tl.vbase + tl.tA;
 #pragma unroll
-      for (int ri = 0; ri < HALF; ++ri) dma16_sb(b + (int64_t)(ri * KPI) * st_b, vlb[ri & 3], dst0 + ri * 1024);
+      for (int ri = 0; ri < HALF; ++ri) dma16_sb<true>(b + (int64_t)(ri * KPI) * st_b, vlb[ri & 3], dst0 + ri * 1024);
     } else {
 #pragma unroll
       for (int ri = 0; ri < HALF; ++ri) {
@@ -163,7 +165,7 @@ void attn_decode_kernel(const AttnParams p) {
         asm volatile("" : "+v"(key), "+v"(c));
         c = min(c, dchunks - 1);
         key = min(key, tl.tlast);
-        dma16(tl.vbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
+        dma16<true>(tl.vbase + (key < tl.tfirst ? tl.tA : tl.tB) + (key * st_b + c * 16), dst0 + ri * 1024);
       }
     }
   };
