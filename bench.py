@@ -254,7 +254,7 @@ def write_traffic(workload_name, pmc_dir):
         for _, name, v in _counter_rows(os.path.join(pmc_dir, "pmc_" + counter)):
             if "attn_" in name:
                 calls.append([(name, v)])
-            elif "merge_kernel" in name and calls:
+            elif "merge" in name and calls:
                 calls[-1].append((name, v))
         per[counter] = calls
     kinds = WORKLOAD_CALLS[workload_name]

@@ -2,9 +2,10 @@
 // (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode; also the log-sum-exp
 // merge of key-split prefill tiles, 1CatAI/1Cat-vLLM PR #1279, commit 5).
 //
-// One work group per (token, head): 256 threads, or 1024 when a row has 16
-// or more parts, so that each thread reads at most a few parts and the pass
-// costs about one memory round trip.  Record s = (o_s[0..D),
+// Rows with 16 or more parts (a long decode row): one work group of 1024
+// threads per (token, head), so that each thread reads at most a few parts and
+// the pass costs about one memory round trip.  Fewer parts: one wave per row
+// (merge_rows_kernel below).  Record s = (o_s[0..D),
 // lse_s, pad) with o_s normalised.  M = max_s lse_s; w_s = exp(lse_s - M);
 // o = sum_s w_s o_s / sum_s w_s; lse = M + log sum_s w_s.  All parts empty ->
 // o = 0, lse = -inf; an empty part's o_s is never read into the sum.
@@ -12,7 +13,7 @@
 // Thread t owns a pair of output columns (t % (D/2)) and a contiguous run of
 // parts (t / (D/2)); the runs are summed in ascending part order and then
 // combined in ascending run order.  The order depends only on S and D (the
-// block size is a function of S), so a
+// kernel is a function of S), so a
 // row's result does not depend on the other rows of the call (batch
 // invariance), and the many parts of a long decode row are read in parallel.
 
@@ -90,6 +91,46 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
   }
 }
 
+// Few parts (S < 16, e.g. a key-split prefill): one wave per (token, head),
+// four rows per work group; lane l owns column pairs l, l + 64, ... and walks
+// the S parts in ascending order.  One read of every record byte, no LDS, no
+// barrier: a prefill with many rows and two to four parts is bound by HBM
+// instead of by work-group launches.
+template <typename OT>
+__global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict__ partials, int S, int D,
+                                                         int64_t rows, OT* __restrict__ out,
+                                                         float* __restrict__ out_lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int R = D + 2;
+  const float* rec = partials + row * (int64_t)S * R;
+  float M = kNegInfM;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) M = fmaxf(M, rec[(int64_t)s * R + D]);
+  const int DC = D >> 1;
+  for (int dc = lane; dc < DC; dc += 64) {
+    float ax = 0.0f, ay = 0.0f, den = 0.0f;
+    if (M != kNegInfM) {
+#pragma unroll 4
+      for (int s = 0; s < S; ++s) {
+        const float* r = rec + (int64_t)s * R;
+        const float ls = r[D];
+        const float2 v = *(const float2*)(r + 2 * dc);
+        const bool live = ls != kNegInfM;
+        const float ws = live ? exp2f((ls - M) * kLog2e) : 0.0f;
+        ax = live ? fmaf(ws, v.x, ax) : ax;
+        ay = live ? fmaf(ws, v.y, ay) : ay;
+        den += ws;
+      }
+    }
+    const bool empty = M == kNegInfM || !(den > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / den;
+    put2<OT>(out + row * D + 2 * dc, ax * inv, ay * inv);
+    if (out_lse != nullptr && dc == 0) out_lse[row] = empty ? kNegInfM : M + logf(den);
+  }
+}
+
 template <typename OT>
 static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out, float* out_lse,
                            hipStream_t stream) {
@@ -99,8 +140,8 @@ static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D,
     hipLaunchKernelGGL((merge_kernel<OT, 1024>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
                        (OT*)out, out_lse);
   else
-    hipLaunchKernelGGL((merge_kernel<OT, 256>), dim3((unsigned)rows), dim3(256), 0, stream, partials, S, D,
-                       (OT*)out, out_lse);
+    hipLaunchKernelGGL((merge_rows_kernel<OT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, partials, S,
+                       D, rows, (OT*)out, out_lse);
   return hipGetLastError();
 }
 
