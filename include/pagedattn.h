@@ -150,6 +150,38 @@ int pa_split_kv_decode(const void *q, int32_t q_dtype, void *out, float *lse,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Split-KV decode / verify with absolute part boundaries.  Speculative
+ * verification checks a verify row against serial decoding token by token, so
+ * it needs the packed row to match the decode bit for bit (InferMatrixLab/
+ * vllm-rlt PR #128, "Purpose", Prefill, the paragraph after the change list);
+ * a verify row of K+1 tokens stands for K+1 decode steps (1CatAI/1Cat-vLLM
+ * PR #616 original, "Purpose", the token-wise expansion of small-q rows).  Same arguments, layouts and ownership as pa_split_kv_decode,
+ * except the partition: part s of every row covers keys
+ * [s*part_keys, (s+1)*part_keys) intersected with [0, L), and the last part
+ * (s = num_parts - 1) runs on to L, so rows longer than num_parts*part_keys
+ * are still exact (their last part is just longer).  part_keys is a positive
+ * multiple of PA_DECODE_SPLIT_TILE.  Because the boundaries do not depend on
+ * the row's length, the running max of every query row moves on that row's
+ * own scores only, and the merge associates its sums by part index alone
+ * (empty trailing parts add exact zeros), token i of a verify row of q
+ * tokens at length L gives the same bits as a q = 1 row at length L - q + 1 + i,
+ * in any batch and with any num_parts that covers it.  With out = NULL only
+ * pass 1 runs, as for pa_split_kv_decode; pa_merge_states then combines the
+ * records in its own order (equal within rounding, not bit for bit, to this
+ * call's merge, which groups parts by index modulo a count fixed by head_dim).
+ * workspace_bytes >=
+ * pa_decode_workspace_bytes(total_q, num_q_heads, head_dim, num_parts).
+ * Returns PA_ERR_INVALID_ARGUMENT for a bad part_keys, otherwise as
+ * pa_split_kv_decode.
+ */
+int pa_split_kv_decode_fixed(const void *q, int32_t q_dtype, void *out, float *lse,
+                             const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                             const int32_t *block_tables, int32_t num_rows, int32_t max_pages_per_seq,
+                             int32_t total_q, int32_t max_q_per_row, int32_t num_q_heads,
+                             const pa_kv_cache *kv, float scale, int32_t part_keys, int32_t num_parts,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Merge of FP32 partial softmax states (InferMatrixLab/vllm-rlt PR #128,
  * "Purpose", Decode: the second kernel).
  *   partials [num_tokens, num_heads, num_splits, head_dim + 2] float32, record =

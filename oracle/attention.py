@@ -174,17 +174,27 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
     return out, lse
 
 
-def split_ranges(seq_len, num_splits, tile=SPLIT_TILE):
-    """Key ranges of the S tile-aligned parts of a row of length seq_len."""
+def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0):
+    """Key ranges of the S parts of a row of length seq_len.
+
+    part_keys == 0: S tile-aligned parts cut from the row's own length
+    (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode).  part_keys > 0:
+    absolute parts [s * part_keys, (s + 1) * part_keys) clipped to the row,
+    the last part running on to seq_len -- boundaries that do not move with the
+    row's length, which is what lets a verify row be compared with serial
+    decoding token for token (same page, "Purpose", Prefill)."""
     L = int(seq_len)
+    if part_keys:
+        C = int(part_keys)
+        return [(min(s * C, L), L if s == num_splits - 1 else min((s + 1) * C, L)) for s in range(num_splits)]
     tiles = -(-L // tile)
     per = -(-tiles // num_splits)
     return [(min(s * per * tile, L), min((s + 1) * per * tile, L)) for s in range(num_splits)]
 
 
-def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE):
+def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0):
     """Per-part partial states of rows over one sequence: (o_s [S, n, D], lse_s [S, n])."""
-    ranges = split_ranges(K.shape[0], num_splits, tile)
+    ranges = split_ranges(K.shape[0], num_splits, tile, part_keys)
     os_, ls_ = [], []
     for lo, hi in ranges:
         o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi)

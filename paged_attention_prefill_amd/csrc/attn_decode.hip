@@ -68,7 +68,7 @@ void attn_decode_kernel(const AttnParams p) {
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, klo, khi);
+  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
   const int last_tok = (min(row0 + 32, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
 
@@ -224,9 +224,14 @@ void attn_decode_kernel(const AttnParams p) {
       tmax = fmaxf(tmax, v);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__any(tmax > m + kTau)) {
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
+    // the running max of a row moves on that row's own scores only (a row
+    // that does not need it is multiplied by exactly 1), so a row's bits do
+    // not depend on the other rows packed with it: a verify row's token
+    // equals the q = 1 row of the same length
+    const bool upd = tmax > m + kTau;
+    if (__any(upd)) {
+      const float mnew = upd ? fmaxf(m, tmax) : m;
+      const float alpha = (!upd || mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int j = 0; j < NDB; ++j) oacc[j] *= alpha;

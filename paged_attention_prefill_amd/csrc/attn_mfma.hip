@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, klo, khi);
+  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
 
   const int prow = row0 + wave * 32 + r32;
   const bool valid = prow < nrows;
@@ -241,9 +241,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
       tmax = fmaxf(tmax, v);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__any(tmax > m + kTau)) {
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
+    // per-row update of the running max (rows that do not need it are
+    // multiplied by exactly 1), so a row's bits do not depend on its neighbours
+    const bool upd = tmax > m + kTau;
+    if (__any(upd)) {
+      const float mnew = upd ? fmaxf(m, tmax) : m;
+      const float alpha = (!upd || mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, klo, khi);
+  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
   const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow0 = row0 + wave * WROWS;

@@ -10,9 +10,10 @@
 // o = sum_s w_s o_s / sum_s w_s; lse = M + log sum_s w_s.  All parts empty ->
 // o = 0, lse = -inf; an empty part's o_s is never read into the sum.
 //
-// Thread t owns a pair of output columns (t % (D/2)) and a contiguous run of
-// parts (t / (D/2)); the runs are summed in ascending part order and then
-// combined in ascending run order.  The order depends only on S and D (the
+// Thread t owns a pair of output columns (t % (D/2)) and a run of parts
+// (t / (D/2)): a contiguous run, or every SG-th part for absolute parts; each
+// run is summed in ascending part order and the runs are combined in
+// ascending run order.  The order depends only on S and D (the
 // kernel is a function of S), so a
 // row's result does not depend on the other rows of the call (batch
 // invariance), and the many parts of a long decode row are read in parallel.
@@ -31,7 +32,11 @@ template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, floa
 }
 }  // namespace
 
-template <typename OT, int kMT>
+// STRIDED: part s goes to run s % SG instead of to a contiguous run, so the
+// association of the sums is a function of the part index and D alone; empty
+// trailing parts add exact zeros, and a row cut into absolute parts gives the
+// same bits whatever the part count of the call.
+template <typename OT, int kMT, bool STRIDED>
 __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ partials, int S, int D,
                                                     OT* __restrict__ out, float* __restrict__ out_lse) {
   constexpr int NW = kMT / 64;
@@ -57,12 +62,12 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
   const int DC = D >> 1;                 // float2 column pairs
   const int SG = kMT / DC;               // runs of parts (>= 2 since D / 2 <= 128)
   const int dc = t % DC, sg = t / DC;
-  const int per = (S + SG - 1) / SG;
-  const int s0 = sg * per, s1 = min(S, s0 + per);
+  const int per = STRIDED ? SG : (S + SG - 1) / SG;
+  const int s0 = STRIDED ? sg : sg * per, s1 = STRIDED ? S : min(S, s0 + per), ds = STRIDED ? SG : 1;
   float ax = 0.0f, ay = 0.0f, den = 0.0f;
   if (M != kNegInfM && sg < SG) {
 #pragma unroll 8
-    for (int s = s0; s < s1; ++s) {
+    for (int s = s0; s < s1; s += ds) {
       const float* r = rec + (int64_t)s * R;
       const float ls = r[D];
       const float2 v = *(const float2*)(r + 2 * dc);
@@ -133,11 +138,14 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
 
 template <typename OT>
 static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out, float* out_lse,
-                           hipStream_t stream) {
+                           bool strided, hipStream_t stream) {
   const int64_t rows = (int64_t)ntok * H;
   if (rows == 0) return hipSuccess;
-  if (S >= 16)
-    hipLaunchKernelGGL((merge_kernel<OT, 1024>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
+  if (strided)
+    hipLaunchKernelGGL((merge_kernel<OT, 1024, true>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
+                       (OT*)out, out_lse);
+  else if (S >= 16)
+    hipLaunchKernelGGL((merge_kernel<OT, 1024, false>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
                        (OT*)out, out_lse);
   else
     hipLaunchKernelGGL((merge_rows_kernel<OT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, partials, S,
@@ -146,11 +154,11 @@ static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D,
 }
 
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, hipStream_t stream) {
+                        float* out_lse, bool strided, hipStream_t stream) {
   switch (out_kind) {
-    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, stream);
-    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, stream);
-    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, stream);
+    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, strided, stream);
+    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, strided, stream);
+    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, strided, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,6 +31,7 @@ struct AttnParams {
   int64_t stride_page, stride_token, stride_head;  // elements
   int num_seqs, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size;
   int num_splits;
+  int part_keys;           // 0: parts cut from each row's own length; > 0: absolute parts of this many keys
   int write_partial;       // 1: records to `partial`; 0: final out/lse
   int qtiles;              // q tiles per (sequence, kv head) in the grid
   int num_work;            // work items (the grid is padded beyond it)
@@ -54,13 +55,22 @@ __device__ __forceinline__ int xcd_remap(int bid) {
   return (row * 8 + ((xcd - row) & 7)) * kXcdGroup + (k % kXcdGroup);
 }
 
-// Key range [lo, hi) of part `s` of a row with L keys cut into S parts of
-// whole kSplitTile-key tiles: per = ceil(ceil(L / T) / S).
-__device__ __forceinline__ void split_range(int L, int S, int s, int& lo, int& hi) {
-  const int tiles = (L + kSplitTile - 1) / kSplitTile;
-  const int per = (tiles + S - 1) / S;
-  const long long a = (long long)s * per * kSplitTile;
-  const long long b = a + (long long)per * kSplitTile;
+// Key range [lo, hi) of part `s` of a row with L keys.  part_keys == 0: S
+// parts of whole kSplitTile-key tiles cut from the row's own length,
+// per = ceil(ceil(L / T) / S) tiles each.  part_keys > 0 (a multiple of T):
+// absolute parts [s * part_keys, (s + 1) * part_keys), the last part (s = S - 1)
+// running on to L, so that the boundaries do not depend on L at all.
+__device__ __forceinline__ void split_range(int L, int S, int s, int part_keys, int& lo, int& hi) {
+  long long a, b;
+  if (part_keys > 0) {
+    a = (long long)s * part_keys;
+    b = s == S - 1 ? (long long)L : a + part_keys;
+  } else {
+    const int tiles = (L + kSplitTile - 1) / kSplitTile;
+    const int per = (tiles + S - 1) / S;
+    a = (long long)s * per * kSplitTile;
+    b = a + (long long)per * kSplitTile;
+  }
   lo = (int)(a < L ? a : L);
   hi = (int)(b < L ? b : L);
 }

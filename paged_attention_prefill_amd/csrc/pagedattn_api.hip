@@ -19,7 +19,7 @@ hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dp
 hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                             hipStream_t stream);
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, hipStream_t stream);
+                        float* out_lse, bool strided, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks,
                                 hipStream_t stream);
@@ -272,7 +272,7 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
 static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
                          const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
                          int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
-                         int splits, bool is_decode, void* workspace, size_t ws_bytes,
+                         int splits, int part_keys, bool is_decode, void* workspace, size_t ws_bytes,
                          hipStream_t stream) {
   const int g = hq / kv->num_kv_heads;
   const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
@@ -306,6 +306,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.head_dim = kv->head_dim;
   p.page_size = kv->page_size;
   p.num_splits = splits;
+  p.part_keys = part_keys;
   p.write_partial = partial ? 1 : 0;
   p.qtiles = qtiles;
   p.num_work = (int)nwork;
@@ -321,7 +322,8 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
-    e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, stream);
+    e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, part_keys > 0,
+                         stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   (void)ws_bytes;
@@ -369,15 +371,15 @@ int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, cons
     if (splits < 0) return splits;
   }
   return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_seqs,
-                       max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, false,
+                       max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, 0, false,
                        workspace, workspace_bytes, (hipStream_t)stream);
 }
 
-int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+static int decode_call(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
                        const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
                        int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
                        int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t part_keys, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
                         total_q, max_q_per_row, num_q_heads, kv);
   if (st != PA_OK) return st;
@@ -394,8 +396,30 @@ int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, co
     return fail(PA_ERR_WORKSPACE, "decode needs %zu bytes of 8-byte aligned workspace (got %zu)", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
-                       total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, true, workspace,
+                       total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, part_keys, true, workspace,
                        workspace_bytes, (hipStream_t)stream);
+}
+
+int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                       const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
+                       int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
+                       int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, 0, workspace, workspace_bytes,
+                     stream);
+}
+
+int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                             const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
+                             int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
+                             int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t part_keys,
+                             int32_t num_parts, void* workspace, size_t workspace_bytes, void* stream) {
+  if (part_keys < PA_DECODE_SPLIT_TILE || part_keys % PA_DECODE_SPLIT_TILE != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "part_keys must be a positive multiple of %d", PA_DECODE_SPLIT_TILE);
+  return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_parts, part_keys, workspace,
+                     workspace_bytes, stream);
 }
 
 int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,
@@ -411,7 +435,7 @@ int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_token
   if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
     return fail(PA_ERR_UNSUPPORTED, "too many rows");
   hipError_t e = pa::launch_merge(partials, num_splits, num_tokens, num_heads, head_dim, out, kind_of(out_dtype),
-                                  out_lse, (hipStream_t)stream);
+                                  out_lse, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -173,6 +173,18 @@ def select_seqs(case, idx, name=None):
                    seq_lens=case.seq_lens[idx].copy(), block_tables=case.block_tables[idx].copy())
 
 
+def expand_row(case, b, name=None):
+    """Row b (q tokens at length L) as q separate q=1 rows at lengths
+    L - q + 1 .. L over the same pages: the token-wise expansion of a verify row."""
+    cu = case.cu_seqlens_q.astype(np.int64)
+    t0, q_len = int(cu[b]), int(cu[b + 1] - cu[b])
+    L = int(case.seq_lens[b])
+    lens = np.array([L - q_len + 1 + i for i in range(q_len)], dtype=np.int32)
+    return replace(case, name=name or f"{case.name}[{b}] token-wise", q=case.q[t0:t0 + q_len].clone(),
+                   cu_seqlens_q=np.arange(q_len + 1, dtype=np.int32), seq_lens=lens,
+                   block_tables=np.repeat(case.block_tables[b:b + 1], q_len, axis=0))
+
+
 # ---------------------------------------------------------------------------
 # The five workloads, shaped like the pages' measurements
 # ---------------------------------------------------------------------------

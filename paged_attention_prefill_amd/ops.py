@@ -60,6 +60,7 @@ def lib():
         L.pa_paged_prefill.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                        ctypes.POINTER(KvCache), ctypes.c_float, _I, _P, _SZ, _P]
         L.pa_split_kv_decode.argtypes = L.pa_paged_prefill.argtypes
+        L.pa_split_kv_decode_fixed.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, _P, _SZ, _P]
         L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.pa_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.pa_prefill_workspace_bytes.restype = _SZ
@@ -70,7 +71,8 @@ def lib():
         L.pa_prefill_auto_splits.argtypes = [_I] * 8
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
-        for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_merge_states", "pa_check_supported",
+        for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_split_kv_decode_fixed", "pa_merge_states",
+                     "pa_check_supported",
                      "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
             if name != "pa_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -188,10 +190,12 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
 
 
 def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
-                    *, num_splits=16, k_scale=1.0, v_scale=1.0, out=None, lse=None,
+                    *, num_splits=16, part_keys=0, k_scale=1.0, v_scale=1.0, out=None, lse=None,
                     return_lse=False, workspace=None, stream=None, merge=True):
     """pa_split_kv_decode on torch tensors; returns out (and lse).
 
+    part_keys > 0: pa_split_kv_decode_fixed, num_splits absolute parts of
+    part_keys keys each (the last one running on to the row's end).
     merge=False: runs pass 1 only and returns the FP32 records
     [total_q, Hq, num_splits, D + 2] for merge_states."""
     total_q, Hq, D = q.shape
@@ -208,11 +212,14 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     ws_bytes = decode_workspace_bytes(total_q, Hq, D, num_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_split_kv_decode(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
-                                    _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
-                                    _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
-                                    total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale),
-                                    int(num_splits), _ptr(workspace), ws_have, _stream(stream)))
+    args = (_ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
+            _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
+            total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale))
+    tail = (_ptr(workspace), ws_have, _stream(stream))
+    if part_keys:
+        _check(lib().pa_split_kv_decode_fixed(*args, int(part_keys), int(num_splits), *tail))
+    else:
+        _check(lib().pa_split_kv_decode(*args, int(num_splits), *tail))
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_splits)
     return (out, lse) if return_lse or lse is not None else out

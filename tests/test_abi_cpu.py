@@ -155,6 +155,21 @@ def test_decode_rejects_long_rows_and_small_workspace():
     assert dec(ws=0x80004, ws_bytes=need) == ops.PA_ERR_WORKSPACE  # misaligned
 
 
+def test_fixed_part_decode_rejects_bad_part_sizes():
+    L = ops.lib()
+    kv = _fake_kv()
+
+    def dec(part_keys, parts=8, ws=None, ws_bytes=0):
+        return L.pa_split_kv_decode_fixed(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4,
+                                          1, 8, ctypes.byref(kv), 0.1, part_keys, parts, ws, ws_bytes, None)
+    for bad in (0, -32, 16, 48, 100):
+        assert dec(bad) == ops.PA_ERR_INVALID_ARGUMENT, bad
+    assert dec(64, parts=0) == ops.PA_ERR_INVALID_ARGUMENT
+    assert dec(64) == ops.PA_ERR_WORKSPACE  # accepted up to the workspace check
+    need = ops.decode_workspace_bytes(4, 8, 128, 8)
+    assert dec(64, ws=0x80000, ws_bytes=need - 1) == ops.PA_ERR_WORKSPACE
+
+
 def test_merge_rejects_bad_arguments():
     L = ops.lib()
     assert L.pa_merge_states(0x1000, 0, 4, 4, 64, 0x2000, ops.PA_F16, None, None) == ops.PA_ERR_INVALID_ARGUMENT

@@ -303,6 +303,62 @@ def test_peaked_scores():
     compare("peaked decode", "f16", out.float().cpu().numpy(), ref[-4:], lse.cpu().numpy(), rl[-4:])
 
 
+# ------------------------------------------------- absolute parts: verify row == serial decode
+
+def gpu_decode_fixed(case, d=None, part_keys=512, parts=8, max_q=None):
+    d = d or gen.to_device(case)
+    max_q = max_q or max(1, case.max_seqlen_q)
+    say(f"  fixed-part decode {case.name}: rows={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} P={case.page_size} part_keys={part_keys} parts={parts} max_q={max_q}")
+    out, lse = ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], max_q, case.scale,
+                                   num_splits=parts, part_keys=part_keys, k_scale=case.k_scale,
+                                   v_scale=case.v_scale, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+@pytest.mark.parametrize("part_keys,parts", [(512, 20), (256, 4), (2048, 64)])
+def test_fixed_part_decode_matches_oracle(decode_bf16, part_keys, parts):
+    """Absolute parts, including a last part that runs on past parts * part_keys."""
+    c, d, (ref, rl) = decode_bf16
+    out, lse = gpu_decode_fixed(c, d, part_keys, parts, max_q=1)
+    compare(f"fixed-part decode C={part_keys} S={parts}", "bf16", out.float().cpu().numpy(), ref,
+            lse.cpu().numpy(), rl)
+
+
+# (q dtype, KV dtype, D, Hq, Hkv, page, L, q of the verify row)
+VERIFY_CASES = [
+    ("f16", "f16", 256, 24, 4, 816, 5000, 5),
+    ("f16", "e5m2", 256, 24, 4, 816, 5000, 5),
+    ("bf16", "bf16", 128, 16, 16, 16, 3001, 5),
+    ("f16", "f16", 64, 8, 2, 32, 1234, 16),
+    ("f32", "f32", 64, 4, 1, 16, 700, 4),
+    ("f16", "e5m2", 128, 8, 2, 48, 2000, 3),
+]
+
+
+@pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,L,q", VERIFY_CASES)
+def test_verify_row_equals_serial_decode_bitwise(qk, kvk, D, Hq, Hkv, P, L, q):
+    """Token i of a verify row (q tokens at length L, in a batch with other rows)
+    gives the same bits as a q=1 row at length L - q + 1 + i, with absolute parts
+    and a different part count in the two calls."""
+    case = gen.make_case(f"verify_{qk}_{kvk}_D{D}", q_lens=[q, 1, 7], seq_lens=[L, 900, 1500], num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, page_size=P, q_kind=qk, kv_kind=kvk, seed=41 + D + q)
+    ser = gen.expand_row(case, 0)
+    C = 256
+    parts = -(-L // C)
+    out_v, lse_v = gpu_decode_fixed(case, part_keys=C, parts=parts + 3, max_q=7 if q < 7 else q)
+    out_s, lse_s = gpu_decode_fixed(ser, part_keys=C, parts=parts, max_q=1)
+    assert torch.equal(bits(out_v[:q]), bits(out_s)), "verify row differs from the serial decode rows"
+    assert torch.equal(lse_v[:q].view(torch.int32), lse_s.view(torch.int32)), "lse differs"
+    ref, rl = run_oracle(case)
+    compare(f"verify {qk}/{kvk} D{D}", kvk, out_v.float().cpu().numpy(), ref, lse_v.cpu().numpy(), rl)
+
+
 def test_merge_states_matches_oracle_merge():
     rng = np.random.default_rng(61)
     N, H, S, D = 7, 3, 5, 128

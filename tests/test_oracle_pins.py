@@ -295,6 +295,61 @@ def test_split_ranges_partition_properties():
     assert oracle.split_ranges(100, 16)[:4] == [(0, 32), (32, 64), (64, 96), (96, 100)]
 
 
+def test_absolute_split_ranges_partition_properties():
+    """Absolute parts: [s C, (s + 1) C) clipped to the row, the last part running on
+    to L; the boundaries of a shorter row are those of a longer row cut at its end."""
+    for C in [32, 96, 512]:
+        for S in [1, 3, 8]:
+            longest = oracle.split_ranges(10 ** 6, S, part_keys=C)
+            for L in [0, 1, 31, 32, 33, 95, 96, 97, 511, 512, 513, 1500, 4097]:
+                r = oracle.split_ranges(L, S, part_keys=C)
+                assert len(r) == S and r[0][0] == 0 and r[-1][1] == L
+                for (a, b), (c, d) in zip(r, r[1:]):
+                    assert b == c and a <= b
+                for s, (a, b) in enumerate(r[:-1]):
+                    assert (a, b) == (min(s * C, L), min((s + 1) * C, L))
+                    assert (a, b) == (min(longest[s][0], L), min(longest[s][1], L))
+                assert r[-1][0] == min((S - 1) * C, L)
+    assert oracle.split_ranges(100, 4, part_keys=32) == [(0, 32), (32, 64), (64, 96), (96, 100)]
+    assert oracle.split_ranges(300, 2, part_keys=64) == [(0, 64), (64, 300)]
+    assert oracle.split_ranges(50, 3, part_keys=64) == [(0, 50), (50, 50), (50, 50)]
+
+
+@pytest.mark.parametrize("C,S", [(32, 10), (64, 2), (96, 4), (512, 1)])
+def test_absolute_split_merge_equals_unsplit(C, S):
+    case = gen.make_case("split_abs", q_lens=[5], seq_lens=[300], num_q_heads=2, num_kv_heads=1,
+                         head_dim=16, page_size=16, q_kind="f32", seed=29)
+    q = gen.to_numpy64(case.q)[:, 0, :]
+    K = oracle.gather_dense_kv(gen.to_numpy64(case.k_pool), case.block_tables[0], 300, 0)
+    V = oracle.gather_dense_kv(gen.to_numpy64(case.v_pool), case.block_tables[0], 300, 0)
+    counts = oracle.visible_key_count(300, 5, np.arange(5))
+    o, l = oracle.attention_rows(q, K, V, counts, case.scale)
+    os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S, part_keys=C)
+    om, lm = oracle.merge_partials(os_, ls_)
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, l, atol=1e-13)
+
+
+def test_token_wise_expansion_of_a_verify_row():
+    """A verify row of q tokens at length L equals q decode rows at lengths
+    L - q + 1 .. L over the same pages (the token-wise expansion), in the oracle."""
+    case = gen.make_case("verify", q_lens=[5, 3], seq_lens=[200, 90], num_q_heads=4, num_kv_heads=2,
+                         head_dim=32, page_size=16, q_kind="f32", seed=31)
+    k = gen.to_numpy64(case.k_pool)
+    v = gen.to_numpy64(case.v_pool)
+    o, l = oracle.paged_attention(gen.to_numpy64(case.q), k, v, case.cu_seqlens_q, case.seq_lens,
+                                  case.block_tables, case.scale)
+    for b in range(2):
+        ex = gen.expand_row(case, b)
+        assert list(ex.seq_lens) == [int(case.seq_lens[b]) - int(case.q_lens[b]) + 1 + i
+                                     for i in range(int(case.q_lens[b]))]
+        oe, le = oracle.paged_attention(gen.to_numpy64(ex.q), k, v, ex.cu_seqlens_q, ex.seq_lens,
+                                        ex.block_tables, ex.scale)
+        t0, t1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
+        np.testing.assert_allclose(oe, o[t0:t1], atol=1e-13)
+        np.testing.assert_allclose(le, l[t0:t1], atol=1e-13)
+
+
 # ---------------------------------------------------------------- fp8
 
 def test_e5m2_decoder_matches_torch_on_all_bytes():
