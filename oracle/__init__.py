@@ -26,6 +26,7 @@ Modules:
                 merge, work counts).
   brute      -- a pure-Python triple loop for tiny cases, used to pin the
                 numpy oracle.
+  kv_write   -- the KV write into pages, with the E5M2 quantisation.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (brute force,
 closed forms, a torch fp64 SDPA cross-check, invariants, planted mistakes).
@@ -45,4 +46,5 @@ from .attention import (  # noqa: F401
     attended_pairs,
 )
 from .fp8 import e5m2_to_float64  # noqa: F401
+from .kv_write import e5m2_encode, quantize_e5m2, write_kv  # noqa: F401
 from .brute import brute_paged_attention  # noqa: F401

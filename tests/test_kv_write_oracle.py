@@ -1,0 +1,84 @@
+"""Pins of the KV-write oracle (CPU): the E5M2 encoder against torch's
+float8_e5m2 conversion and hand-checked values, and the slot arithmetic of the
+write against the oracle's own gather."""
+
+import numpy as np
+import torch
+
+import oracle
+from paged_attention_prefill_amd import inputs as gen
+
+
+def test_e5m2_encoder_matches_torch_on_every_finite_fp16_value():
+    """Every fp16 bit pattern below the saturation point: ties, subnormals,
+    both signs (torch's conversion rounds to nearest even, without saturation)."""
+    h = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.float16)
+    x = h.to(torch.float32)
+    keep = torch.isfinite(x) & (x.abs() < 61440)
+    x = x[keep]
+    want = x.to(torch.float8_e5m2).view(torch.uint8).numpy()
+    got = oracle.e5m2_encode(x.numpy().astype(np.float64))
+    assert (got == want).all(), int((got != want).sum())
+
+
+def test_e5m2_encoder_matches_torch_on_random_float32():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 12, 200000))).astype(np.float32)
+    x = x[np.abs(x) < 61440]
+    want = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert (oracle.e5m2_encode(x.astype(np.float64)) == want).all()
+
+
+def test_e5m2_encoder_special_values():
+    cases = [(1.0, 0x3C), (1.125, 0x3C), (1.375, 0x3E), (1.25, 0x3D), (57344.0, 0x7B), (61439.0, 0x7B),
+             (61440.0, 0x7B), (1e30, 0x7B), (np.inf, 0x7B), (-np.inf, 0xFB), (-70000.0, 0xFB), (2.0 ** -16, 0x01),
+             (2.0 ** -17, 0x00), (3 * 2.0 ** -18, 0x01), (2.0 ** -14, 0x04), (0.875 * 2.0 ** -14, 0x04),
+             (-0.0, 0x80), (0.0, 0x00), (-1e-9, 0x80)]
+    for v, c in cases:
+        assert int(oracle.e5m2_encode(np.array([v]))[0]) == c, (v, hex(c))
+    nan = oracle.e5m2_encode(np.array([np.nan, -np.nan]))
+    assert list(nan) == [0x7F, 0xFF]
+
+
+def test_e5m2_round_trip_of_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) < 0x7C])
+    vals = oracle.e5m2_to_float64(codes)
+    back = oracle.e5m2_encode(vals)
+    assert (back == codes).all()
+
+
+def test_quantize_divides_in_float32():
+    # 1/3 in float32 is below the fp64 third; 0.1 * 3 lands at a tie-free value either way
+    x = np.array([1.0, 0.75, 3.0], dtype=np.float32)
+    got = oracle.quantize_e5m2(x, 3.0)
+    q = x / np.float32(3.0)
+    assert (got == oracle.e5m2_encode(q.astype(np.float64))).all()
+
+
+def test_write_places_each_token_at_its_slot():
+    """After the write, the sequence's last q_len keys (gathered by the oracle
+    through the block table) are exactly the new rows, and nothing else moved."""
+    case = gen.make_case("kvw", q_lens=[5, 0, 17], seq_lens=[40, 9, 17], num_q_heads=4, num_kv_heads=2,
+                         head_dim=32, page_size=16, q_kind="f32", seed=51, poison=False)
+    rng = np.random.default_rng(52)
+    T = case.total_q
+    kn = rng.standard_normal((T, 2, 32))
+    vn = rng.standard_normal((T, 2, 32))
+    kp = gen.to_numpy64(case.k_pool)
+    vp = gen.to_numpy64(case.v_pool)
+    ko, vo = oracle.write_kv(kp, vp, kn, vn, case.cu_seqlens_q, case.seq_lens, case.block_tables)
+    changed = np.zeros(kp.shape[:2], dtype=bool)
+    for b in range(case.num_seqs):
+        L, q = int(case.seq_lens[b]), int(case.q_lens[b])
+        t0 = int(case.cu_seqlens_q[b])
+        for h in range(2):
+            K = oracle.gather_dense_kv(ko, case.block_tables[b], L, h)
+            V = oracle.gather_dense_kv(vo, case.block_tables[b], L, h)
+            np.testing.assert_array_equal(K[L - q:], kn[t0:t0 + q, h])
+            np.testing.assert_array_equal(V[L - q:], vn[t0:t0 + q, h])
+            K0 = oracle.gather_dense_kv(kp, case.block_tables[b], L, h)
+            np.testing.assert_array_equal(K[:L - q], K0[:L - q])
+        for pos in range(L - q, L):
+            changed[int(case.block_tables[b][pos // 16]), pos % 16] = True
+    np.testing.assert_array_equal(ko[~changed], kp[~changed])
+    np.testing.assert_array_equal(vo[~changed], vp[~changed])
