@@ -197,6 +197,34 @@ int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_token
                     int32_t num_heads, int32_t head_dim, void *out, int32_t out_dtype,
                     float *out_lse, void *stream);
 
+/*
+ * KV write: the new tokens' K and V into their cache pages, before the
+ * attention that reads them (a chunk's keys are in the cache when its prefill
+ * runs: 1CatAI/1Cat-vLLM PR #1279, commit 3, the second half reading the first
+ * half's KV writes; fp8_e5m2 cache with a per-tensor scale: 1CatAI/1Cat-vLLM
+ * PR #616 original, "Test Result", fp8_e5m2 KV paragraph).
+ *   k_new, v_new [total_q, kv->num_kv_heads, kv->head_dim] in src_dtype,
+ *   contiguous, 16-byte aligned (device, caller-owned, read only).  Sequence b's
+ *   new tokens are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (q_len of them,
+ *   q_len <= max_q); token t goes to position seq_lens[b] - q_len + t (its last
+ *   q_len slots, seq_lens counting the new tokens), i.e. page
+ *   block_tables[b][pos / page_size], slot pos % page_size.  Tokens with a
+ *   negative position (q_len > seq_len) are not written.
+ *   The cache (kv->k_pages, kv->v_pages: written through, despite the const of
+ *   the descriptor) has src_dtype, which is copied exactly, or FP8_E5M2 (with
+ *   F16 src), byte = E5M2 of (x / scale) computed in fp32 (k_scale for K,
+ *   v_scale for V, both positive), rounded to nearest with ties to even and
+ *   saturated to +-57344; NaN stays NaN (0x7F with its sign).  Nothing else in
+ *   the cache is touched.  Device metadata is trusted (pa_validate_metadata
+ *   checks host copies); two new tokens must not map to the same slot.
+ *   Asynchronous on `stream`; returns the argument / support statuses of
+ *   pa_paged_prefill.
+ */
+int pa_write_kv(const void *k_new, const void *v_new, int32_t src_dtype, const int32_t *cu_seqlens_q,
+                const int32_t *seq_lens, const int32_t *block_tables, int32_t num_seqs,
+                int32_t max_pages_per_seq, int32_t total_q, int32_t max_q, const pa_kv_cache *kv,
+                void *stream);
+
 /* Workspace sizes in bytes (host-only, no HIP call). */
 size_t pa_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_kv_splits);

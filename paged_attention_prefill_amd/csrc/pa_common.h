@@ -39,6 +39,20 @@ struct AttnParams {
   float v_scale;
 };
 
+// Arguments of the KV write (new tokens' K and V into their cache pages).
+struct KvWriteParams {
+  const void* k_new;       // [total_q, Hkv, D], source dtype
+  const void* v_new;
+  const int* cu_seqlens_q; // [B + 1]: the new tokens of each sequence
+  const int* seq_lens;     // [B]: lengths after the write
+  const int* block_tables; // [B, max_pages]
+  void* k_pages;           // cache pages (cache dtype)
+  void* v_pages;
+  int64_t stride_page, stride_token, stride_head;  // elements of the cache dtype
+  int num_seqs, max_pages, max_q, num_kv_heads, head_dim, page_size;
+  float k_scale, v_scale;  // fp8 cache: byte = E5M2(x / scale)
+};
+
 // Block index -> work index.  Work groups are handed to the 8 XCDs round
 // robin; runs of kXcdGroup consecutive work items (neighbouring query tiles of
 // one sequence, kv head and key part, which read the same K/V) are kept on one

@@ -30,6 +30,7 @@ int mfma_dma_rows(int dpad);
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream);
 int decode_rows_per_group();
+hipError_t launch_kv_write(const KvWriteParams& w, int src_kind, bool fp8, hipStream_t stream);
 int mfma_rows_per_group();
 int valu_rows_per_group();
 }  // namespace pa
@@ -420,6 +421,47 @@ int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* l
   return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
                      total_q, max_q_per_row, num_q_heads, kv, scale, num_parts, part_keys, workspace,
                      workspace_bytes, stream);
+}
+
+int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const int32_t* cu_seqlens_q,
+                const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
+                int32_t total_q, int32_t max_q, const pa_kv_cache* kv, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q < 0 || max_pages_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative size or max_pages_per_seq < 1");
+  if (kv == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  int st = check_kv(kv, src_dtype, kv->num_kv_heads);
+  if (st != PA_OK) return st;
+  if (kv->dtype == PA_FP8_E5M2 && !(kv->v_scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "v_scale must be positive for an FP8_E5M2 cache");
+  if (num_seqs == 0 || total_q == 0) return ok();
+  if (!k_new || !v_new || !cu_seqlens_q || !seq_lens || !block_tables)
+    return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(PA_ERR_INVALID_ARGUMENT, "k_new / v_new must be 16-byte aligned");
+  if (max_q < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_q must be >= 1 when total_q > 0");
+  const int64_t bps = ((int64_t)max_q * kv->num_kv_heads * (kv->head_dim / 8) + 255) / 256;
+  if (bps * num_seqs >= ((int64_t)1 << 31)) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  pa::KvWriteParams w;
+  w.k_new = k_new;
+  w.v_new = v_new;
+  w.cu_seqlens_q = cu_seqlens_q;
+  w.seq_lens = seq_lens;
+  w.block_tables = block_tables;
+  w.k_pages = const_cast<void*>(kv->k_pages);
+  w.v_pages = const_cast<void*>(kv->v_pages);
+  w.stride_page = kv->stride_page;
+  w.stride_token = kv->stride_token;
+  w.stride_head = kv->stride_head;
+  w.num_seqs = num_seqs;
+  w.max_pages = max_pages_per_seq;
+  w.max_q = max_q;
+  w.num_kv_heads = kv->num_kv_heads;
+  w.head_dim = kv->head_dim;
+  w.page_size = kv->page_size;
+  w.k_scale = kv->k_scale;
+  w.v_scale = kv->v_scale;
+  hipError_t e = pa::launch_kv_write(w, kind_of(src_dtype), kv->dtype == PA_FP8_E5M2, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "KV write launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,

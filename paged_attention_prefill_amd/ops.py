@@ -62,6 +62,7 @@ def lib():
         L.pa_split_kv_decode.argtypes = L.pa_paged_prefill.argtypes
         L.pa_split_kv_decode_fixed.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, _P, _SZ, _P]
         L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
+        L.pa_write_kv.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), _P]
         L.pa_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.pa_prefill_workspace_bytes.restype = _SZ
         L.pa_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
@@ -72,6 +73,7 @@ def lib():
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
         for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_split_kv_decode_fixed", "pa_merge_states",
+                     "pa_write_kv",
                      "pa_check_supported",
                      "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
             if name != "pa_status_string":
@@ -223,6 +225,23 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_splits)
     return (out, lse) if return_lse or lse is not None else out
+
+
+def write_kv(k_new, v_new, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q, *, k_scale=1.0,
+             v_scale=1.0, stream=None):
+    """pa_write_kv: k_new / v_new [total_q, Hkv, D] into the pages at each sequence's
+    last q_len positions (uint8 pages: fp8_e5m2 of x / scale)."""
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if not t.is_contiguous() or t.dim() != 3:
+            raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous [total_q, Hkv, D] tensor")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "k_new and v_new must share shape and dtype")
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    B = int(seq_lens.numel())
+    _check(lib().pa_write_kv(_ptr(k_new), _ptr(v_new), _dtype(k_new), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
+                             _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B,
+                             block_tables.shape[-1], int(k_new.shape[0]), int(max_q), ctypes.byref(kv),
+                             _stream(stream)))
 
 
 def merge_states(partials, out_dtype=torch.float32, *, out=None, lse=None, return_lse=False, stream=None):
