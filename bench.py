@@ -212,6 +212,40 @@ def cpu_baseline(case, budget_rows, seed=0):
             "seconds": dt}
 
 
+def kv_write_timing(case, d, reps):
+    """Writes the prefill chunk's K and V (fp16 / bf16 rows) into the case's cache
+    at the chunk's positions, and into an fp8_e5m2 cache of the same geometry;
+    HIP events on the current stream, median over reps, priced in HBM GB/s."""
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(7)
+    shape = (case.total_q, case.num_kv_heads, case.head_dim)
+    kn = torch.randn(shape, generator=g, device="cuda").to(d["q"].dtype)
+    vn = torch.randn(shape, generator=g, device="cuda").to(d["q"].dtype)
+    out = {}
+    targets = [(case.kv_kind, d["k"], d["v"])]
+    if case.kv_kind != "e5m2" and case.q_kind == "f16":
+        k8 = torch.zeros(d["k"].shape, dtype=torch.uint8, device="cuda")
+        targets.append(("e5m2", k8, torch.zeros_like(k8)))
+    src = "f16" if d["q"].dtype == torch.float16 else "bf16"
+    for kv_kind, kp, vp in targets:
+        times = []
+        for i in range(reps + 3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ops.write_kv(kn, vn, kp, vp, d["cu"], d["seq_lens"], d["bt"], max(1, case.max_seqlen_q), stream=stream)
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in times[3:]]))
+        b = workload.kv_write_bytes(case.cu_seqlens_q, case.seq_lens, case.num_kv_heads, case.head_dim,
+                                    case.page_size, src, kv_kind)
+        out[kv_kind] = {"ms_median": ms, "bytes": b, "gbs": b / (ms * 1e-3) / 1e9,
+                        "frac_of_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["what"] = (f"write of the chunk's {case.total_q} new K and V rows ({case.num_kv_heads} kv heads, "
+                   f"D {case.head_dim}) into its pages; not part of the step's value")
+    return out
+
+
 def copy_reference(steps):
     """A plain device copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     n = 1 << 28
@@ -258,6 +292,11 @@ def write_traffic(workload_name, pmc_dir):
                 calls[-1].append((name, v))
         per[counter] = calls
     kinds = WORKLOAD_CALLS[workload_name]
+
+    def kind_of(call):  # a call's kind by its pass-1 kernel (the run also holds extra decode repetitions)
+        if len(kinds) == 1:
+            return kinds[0]
+        return "decode" if "attn_decode" in call[0][0] else "prefill"
     out = {"sources_sha256": kernel_sources_hash(),
            "about": "HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by "
                     "the factors that make the same counters read 2^30 bytes for a 1 GiB device copy "
@@ -270,9 +309,9 @@ def write_traffic(workload_name, pmc_dir):
     except (OSError, ValueError):
         pass
     entry = {}
-    for i, kind in enumerate(kinds):
-        f_calls = per["FETCH_SIZE"][i::len(kinds)]
-        w_calls = per["WRITE_SIZE"][i::len(kinds)]
+    for kind in kinds:
+        f_calls = [c for c in per["FETCH_SIZE"] if kind_of(c) == kind]
+        w_calls = [c for c in per["WRITE_SIZE"] if kind_of(c) == kind]
         names = [n for n, _ in f_calls[0]]
         fetch = [float(np.mean([c[j][1] for c in f_calls])) for j in range(len(names))]
         write = [float(np.mean([c[j][1] for c in w_calls])) for j in range(len(names))]
@@ -476,6 +515,9 @@ def main():
         b = parts["decode"]["bytes"]
         res["decode_cold"] = {"ms_median": ms, "gbs": b / (ms * 1e-3) / 1e9, "reps": len(c.times),
                               "note": "1 GiB scratch read before each repetition"}
+    pre = [c for c in calls if c.kind == "prefill"]
+    if pre:
+        res["kv_write"] = kv_write_timing(pre[0].case, pre[0].d, max(5, min(a.steps, 20)))
     if not a.no_cpu_baseline and "prefill" in parts:
         pre = [c for c in calls if c.kind == "prefill"][0].case
         if pre.num_seqs == 1:

@@ -46,3 +46,19 @@ def decode_bytes(cu_seqlens_q, seq_lens, num_q_heads, num_kv_heads, head_dim, pa
     bt = int(sum(-(-int(x) // int(page_size)) for x in L)) * 4
     partial = 2 * total_q * int(num_q_heads) * int(num_splits) * (int(head_dim) + 2) * 4
     return kv + qo + bt + partial
+
+
+def kv_write_bytes(cu_seqlens_q, seq_lens, num_kv_heads, head_dim, page_size, src_kind, kv_kind):
+    """KV write: the new K and V rows read once and written once into the cache,
+    plus cu_seqlens_q, seq_lens and the block-table entries the new tokens map to."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    total_q = int(cu[-1])
+    rows = total_q * int(num_kv_heads) * int(head_dim) * 2
+    pages = 0
+    for b in range(len(L)):
+        q = int(cu[b + 1] - cu[b])
+        lo = max(0, int(L[b]) - q)
+        if int(L[b]) > lo:
+            pages += (int(L[b]) - 1) // int(page_size) - lo // int(page_size) + 1
+    return rows * (Q_BYTES[src_kind] + KV_BYTES[kv_kind]) + (2 * len(L) + 1) * 4 + pages * 4
