@@ -45,6 +45,6 @@ from .attention import (  # noqa: F401
     merge_partials,
     attended_pairs,
 )
-from .fp8 import e5m2_to_float64  # noqa: F401
-from .kv_write import e5m2_encode, quantize_e5m2, write_kv  # noqa: F401
+from .fp8 import e4m3_to_float64, e5m2_to_float64  # noqa: F401
+from .kv_write import e4m3_encode, e5m2_encode, fp8_encode, quantize_e5m2, quantize_fp8, write_kv  # noqa: F401
 from .brute import brute_paged_attention  # noqa: F401

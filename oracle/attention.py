@@ -30,7 +30,7 @@ whole in memory.  Everything is float64; inputs are upcast exactly.
 
 import numpy as np
 
-from .fp8 import e5m2_to_float64
+from .fp8 import e4m3_to_float64, e5m2_to_float64
 
 # Decode split tile (keys); see the module docstring for the reading.
 SPLIT_TILE = 32
@@ -40,7 +40,7 @@ def dequantize_pool(pool, kind, scale=1.0):
     """Exact float64 values of a KV page pool.
 
     ``kind`` is 'float' for any IEEE float storage (fp32, fp16, or bf16 already
-    widened by the caller) or 'e5m2' for a uint8 array of fp8_e5m2 bytes, whose
+    widened by the caller), 'e5m2' or 'e4m3' for a uint8 array of fp8 bytes, whose
     values are decode(byte) * scale (per-tensor scale; 1CatAI/1Cat-vLLM PR #616,
     fp8_e5m2 KV paragraph of "Test Result").
     """
@@ -48,6 +48,8 @@ def dequantize_pool(pool, kind, scale=1.0):
         return np.asarray(pool, dtype=np.float64)
     if kind == "e5m2":
         return e5m2_to_float64(np.asarray(pool)) * float(scale)
+    if kind == "e4m3":
+        return e4m3_to_float64(np.asarray(pool)) * float(scale)
     raise ValueError(f"unknown pool kind {kind!r}")
 
 

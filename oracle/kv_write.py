@@ -7,11 +7,12 @@ What is computed (the pages give the step, not its arithmetic):
   KV writes); token t of a sequence with q new tokens and length L (counting
   them) lands at position L - q + t, page block_table[pos // P], slot pos % P;
 * an fp8_e5m2 cache with a per-tensor scale (1CatAI/1Cat-vLLM PR #616,
-  original description, "Test Result", fp8_e5m2 KV paragraph).  The pages do
-  not say how a value becomes a byte.  Reading: byte = the E5M2 value nearest
-  to x / scale, the quotient taken in float32 (as the kernel takes it), ties
-  to the even code, magnitudes past the largest finite E5M2 (57344) saturated
-  to it, NaN kept NaN (0x7F with the sign bit).
+  original description, "Test Result", fp8_e5m2 KV paragraph), and an e4m3
+  path named by the same page's "Test Plan".  The pages do not say how a value
+  becomes a byte.  Reading: byte = the fp8 value nearest to x / scale, the
+  quotient taken in float32 (as the kernel takes it), ties to the even code,
+  magnitudes past the largest finite value (57344 for E5M2, 448 for E4M3)
+  saturated to it, NaN kept NaN (0x7F with the sign bit).
 
 The encoder is written as that definition: it searches the table of all
 finite E5M2 values (decoded by ``oracle.fp8`` from the bit layout) for the
@@ -21,44 +22,65 @@ inside the finite range and against hand-checked values.
 
 import numpy as np
 
-from .fp8 import e5m2_to_float64
+from .fp8 import e4m3_to_float64, e5m2_to_float64
 
 E5M2_MAX = 57344.0
-_CODES = np.arange(0, 0x7C)                 # +0 .. +57344, ascending values
-_VALUES = e5m2_to_float64(_CODES)
+E4M3_MAX = 448.0
+# every finite non-negative code of each format, in ascending order of value
+_TABLES = {"e5m2": (np.arange(0, 0x7C), e5m2_to_float64(np.arange(0, 0x7C)), E5M2_MAX),
+           "e4m3": (np.arange(0, 0x7F), e4m3_to_float64(np.arange(0, 0x7F)), E4M3_MAX)}
 
 
-def e5m2_encode(y):
-    """E5M2 bytes (uint8) of the float values y: nearest finite value, ties to
-    the even code, saturating at +-57344, NaN -> 0x7F | sign."""
+def fp8_encode(y, fmt):
+    """fp8 bytes (uint8) of the float values y: the nearest finite value of the
+    format, ties to the even code, saturating at the largest finite magnitude,
+    NaN -> 0x7F | sign (a NaN code of both formats)."""
+    codes, values, vmax = _TABLES[fmt]
     y = np.asarray(y, dtype=np.float64)
     a = np.abs(y)
     sign = np.signbit(y).astype(np.int64) << 7
-    a_sat = np.minimum(np.where(np.isnan(a), 0.0, a), E5M2_MAX)
-    hi = np.searchsorted(_VALUES, a_sat, side="left")     # first table value >= a
-    hi = np.minimum(hi, len(_VALUES) - 1)
+    a_sat = np.minimum(np.where(np.isnan(a), 0.0, a), vmax)
+    hi = np.searchsorted(values, a_sat, side="left")     # first table value >= a
+    hi = np.minimum(hi, len(values) - 1)
     lo = np.maximum(hi - 1, 0)
-    d_lo = a_sat - _VALUES[lo]
-    d_hi = _VALUES[hi] - a_sat
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_CODES[hi] % 2 == 0))
-    code = np.where(pick_hi, _CODES[hi], _CODES[lo])
-    code = np.where(a_sat == _VALUES[hi], _CODES[hi], code)
+    d_lo = a_sat - values[lo]
+    d_hi = values[hi] - a_sat
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    code = np.where(pick_hi, codes[hi], codes[lo])
+    code = np.where(a_sat == values[hi], codes[hi], code)
     code = np.where(np.isnan(y), 0x7F, code)
     return (code | sign).astype(np.uint8)
 
 
+def e5m2_encode(y):
+    """E5M2 bytes: nearest finite value, ties to even, saturating at +-57344."""
+    return fp8_encode(y, "e5m2")
+
+
+def e4m3_encode(y):
+    """E4M3 bytes: nearest finite value, ties to even, saturating at +-448."""
+    return fp8_encode(y, "e4m3")
+
+
+def quantize_fp8(x, scale, fmt="e5m2"):
+    """fp8 bytes of x / scale, the quotient formed in float32."""
+    q = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return fp8_encode(q.astype(np.float64), fmt)
+
+
 def quantize_e5m2(x, scale):
     """E5M2 bytes of x / scale, the quotient formed in float32."""
-    q = np.asarray(x, dtype=np.float32) / np.float32(scale)
-    return e5m2_encode(q.astype(np.float64))
+    return quantize_fp8(x, scale, "e5m2")
 
 
 def write_kv(k_pool, v_pool, k_new, v_new, cu_seqlens_q, seq_lens, block_tables, fp8=False,
              k_scale=1.0, v_scale=1.0):
     """Copies of the pools [num_pages, P, Hkv, D] with the new tokens written.
 
-    k_new, v_new [total_q, Hkv, D] (float values); fp8 pools are uint8 byte arrays.
+    k_new, v_new [total_q, Hkv, D] (float values); fp8 pools are uint8 byte
+    arrays, fp8 = True or "e5m2" for E5M2 bytes, "e4m3" for E4M3 bytes.
     """
+    fmt = "e5m2" if fp8 is True else fp8
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     P = k_out.shape[1]
@@ -73,8 +95,8 @@ def write_kv(k_pool, v_pool, k_new, v_new, cu_seqlens_q, seq_lens, block_tables,
             page = int(block_tables[b][pos // P])
             row = int(cu[b]) + t
             if fp8:
-                k_out[page, pos % P] = quantize_e5m2(k_new[row], k_scale)
-                v_out[page, pos % P] = quantize_e5m2(v_new[row], v_scale)
+                k_out[page, pos % P] = quantize_fp8(k_new[row], k_scale, fmt)
+                v_out[page, pos % P] = quantize_fp8(v_new[row], v_scale, fmt)
             else:
                 k_out[page, pos % P] = k_new[row]
                 v_out[page, pos % P] = v_new[row]

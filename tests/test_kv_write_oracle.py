@@ -82,3 +82,37 @@ def test_write_places_each_token_at_its_slot():
             changed[int(case.block_tables[b][pos // 16]), pos % 16] = True
     np.testing.assert_array_equal(ko[~changed], kp[~changed])
     np.testing.assert_array_equal(vo[~changed], vp[~changed])
+
+
+# ---------------------------------------------------------------- E4M3
+
+def test_e4m3_decoder_matches_torch_on_all_bytes():
+    codes = np.arange(256)
+    want = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.e4m3_to_float64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert np.nanmax(got) == 448.0 and int(np.isnan(got).sum()) == 2
+
+
+def test_e4m3_encoder_matches_torch_on_every_fp16_value_in_range():
+    """Every fp16 bit pattern up to 464 (torch's conversion, which rounds to
+    nearest even and turns larger magnitudes into NaN)."""
+    h = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.float16)
+    x = h.to(torch.float32)
+    x = x[torch.isfinite(x) & (x.abs() <= 464)]
+    want = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(x.numpy().astype(np.float64))
+    assert (got == want).all(), int((got != want).sum())
+
+
+def test_e4m3_encoder_specials_and_round_trip():
+    cases = [(448.0, 0x7E), (464.0, 0x7E), (465.0, 0x7E), (1e6, 0x7E), (np.inf, 0x7E), (-np.inf, 0xFE),
+             (1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -11, 0x01),
+             (2.0 ** -6, 0x08), (-0.0, 0x80)]
+    for v, c in cases:
+        assert int(oracle.e4m3_encode(np.array([v]))[0]) == c, (v, hex(c))
+    assert list(oracle.e4m3_encode(np.array([np.nan, -np.nan]))) == [0x7F, 0xFF]
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    assert (oracle.e4m3_encode(oracle.e4m3_to_float64(codes)) == codes).all()
