@@ -19,9 +19,13 @@
  *    rows in the call for fixed (num_splits, max_q_per_row, dtypes, head_dim).
  *  - pa_merge_states: that second pass on its own (also used by prefill
  *    splits).
- *  - fp8_e5m2 KV (1CatAI/1Cat-vLLM PR #616, fp8_e5m2 paragraph of "Test
- *    Result"): bytes are dequantized inside the kernels, value = e5m2(byte) *
- *    k_scale (or v_scale).
+ *  - fp8 KV (1CatAI/1Cat-vLLM PR #616, fp8_e5m2 paragraph of "Test Result";
+ *    the same page's "Test Plan" names an e4m3 path too): E5M2 or E4M3 bytes
+ *    are dequantized inside the kernels, value = decode(byte) * k_scale (or
+ *    v_scale); q and out stay fp16.
+ *  - pa_split_kv_decode_fixed: decode with absolute part boundaries, so that
+ *    a verify row equals serial decoding bit for bit.
+ *  - pa_write_kv: the new tokens' K/V into their pages (fp8: quantised).
  *
  * Conventions shared by all calls
  *  - Every data pointer is DEVICE memory owned by the caller; the library
@@ -83,7 +87,8 @@ typedef enum pa_dtype {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
-  PA_FP8_E5M2 = 3
+  PA_FP8_E5M2 = 3,  /* OCP E5M2 bytes: bias 15, infinities and NaNs */
+  PA_FP8_E4M3 = 4   /* OCP E4M3 ("fn") bytes: bias 7, no infinities, 0x7F / 0xFF NaN, max 448 */
 } pa_dtype;
 
 /* One paged KV cache (K and V share the geometry). Host struct, device pointers. */
@@ -98,7 +103,7 @@ typedef struct pa_kv_cache {
   int32_t num_kv_heads;
   int32_t head_dim;      /* multiple of 16 in [16, 256]; contiguous */
   int32_t dtype;         /* pa_dtype */
-  float k_scale;         /* FP8_E5M2 only (must be 1 otherwise) */
+  float k_scale;         /* fp8 KV only (must be 1 otherwise): value = decode(byte) * scale */
   float v_scale;
 } pa_kv_cache;
 
@@ -212,9 +217,10 @@ int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_token
  *   negative position (q_len > seq_len) are not written.
  *   The cache (kv->k_pages, kv->v_pages: written through, despite the const of
  *   the descriptor) has src_dtype, which is copied exactly, or FP8_E5M2 (with
- *   F16 src), byte = E5M2 of (x / scale) computed in fp32 (k_scale for K,
- *   v_scale for V, both positive), rounded to nearest with ties to even and
- *   saturated to +-57344; NaN stays NaN (0x7F with its sign).  Nothing else in
+ *   F16 src) or FP8_E4M3 (with F16 src), byte = the fp8 code of (x / scale)
+ *   computed in fp32 (k_scale for K, v_scale for V, both positive), rounded to
+ *   nearest with ties to even and saturated to the largest finite magnitude
+ *   (57344 for E5M2, 448 for E4M3); NaN stays NaN (0x7F with its sign).  Nothing else in
  *   the cache is touched.  Device metadata is trusted (pa_validate_metadata
  *   checks host copies); two new tokens must not map to the same slot.
  *   Asynchronous on `stream`; returns the argument / support statuses of

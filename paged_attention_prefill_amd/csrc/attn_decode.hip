@@ -22,16 +22,17 @@ using namespace mf;
 // NSW stages of (K, V) tiles in its own part of LDS.  The K half of a stage is
 // refilled as soon as the wave's S^T = K Q^T has read it and the V half after
 // O^T += V^T P^T, so that between one and 2 NSW half-tiles per wave are always
-// in flight.  KV8: K and V are fp8 E5M2 (q fp16), 8-bit tiles in LDS widened
-// to fp16 as the MFMA operands are read.  The combined result depends only on
+// in flight.  F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16), 8-bit tiles in
+// LDS widened to fp16 as the MFMA operands are read.  The combined result depends only on
 // the row's own length and the part count.
 // Head dims up to 128 are held to 256 registers so that two groups share a CU
 // (with one ring stage per wave at D 128: 64 KB of LDS per group): a decode
 // batch has many short parts, and a second resident group hides each part's
 // first-tile latency.
-template <typename QT, bool KV8, int DPAD, int NSW>
+template <typename QT, int F8, int DPAD, int NSW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DPAD <= 128 ? 2 : 1)))
 void attn_decode_kernel(const AttnParams p) {
+  constexpr bool KV8 = F8 != 0;
   constexpr int WAVES = 4;
   typedef TileLoader<DPAD, 1, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
@@ -197,8 +198,8 @@ void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
       for (int kp = 0; kp < NKK / 2; ++kp) {
         const uint4 kw = *(const uint4*)(smem + sb + k_frag(klane, kp));
-        s0 = Mf<QT>::run(e5m2x8_to_f16(kw.x, kw.y), qf[2 * kp], s0);
-        s1 = Mf<QT>::run(e5m2x8_to_f16(kw.z, kw.w), qf[2 * kp + 1], s1);
+        s0 = Mf<QT>::run(fp8x8_to_f16<F8>(kw.x, kw.y), qf[2 * kp], s0);
+        s1 = Mf<QT>::run(fp8x8_to_f16<F8>(kw.z, kw.w), qf[2 * kp + 1], s1);
       }
     } else {
 #pragma unroll
@@ -256,7 +257,7 @@ void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint4 a;
-        if constexpr (KV8) a = read_vt8(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
+        if constexpr (KV8) a = read_vt8<F8>(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
         else a = read_vt(smem + (vls ^ (db << 6)) + ks * 16 * ROWB, 8 * ROWB);
         oacc[db] = Mf<QT>::run(a, pf[ks], oacc[db]);
       }
@@ -325,29 +326,31 @@ void attn_decode_kernel(const AttnParams p) {
 // ---- host side -------------------------------------------------------------
 
 namespace {
-template <typename QT, bool KV8, int DPAD, int NSW>
+template <typename QT, int F8, int DPAD, int NSW>
 hipError_t launch_dec(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<QT, KV8, DPAD, NSW>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_decode_kernel<QT, F8, DPAD, NSW>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 template <typename QT>
 hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t stream) {
   switch (dpad) {
-    case 64: return launch_dec<QT, false, 64, 2>(p, nblocks, stream);
-    case 128: return launch_dec<QT, false, 128, 1>(p, nblocks, stream);
-    case 256: return launch_dec<QT, false, 256, 1>(p, nblocks, stream);
+    case 64: return launch_dec<QT, 0, 64, 2>(p, nblocks, stream);
+    case 128: return launch_dec<QT, 0, 128, 1>(p, nblocks, stream);
+    case 256: return launch_dec<QT, 0, 256, 1>(p, nblocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
 // Decode pass 1, 32 rows per group: fp16 / bf16 q with KV of the same dtype
-// (kv_kind = q_kind), or fp16 q with fp8 E5M2 KV for head dims padded to 256.
+// (kv_kind = q_kind), or fp16 q with fp8 KV (E5M2 or E4M3) for head dims
+// padded to 256.
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream) {
-  if (kv_kind == KV_E5M2) {
-    if (q_kind == KV_F16 && dpad == 256) return launch_dec<_Float16, true, 256, 2>(p, nblocks, stream);
-    return hipErrorInvalidValue;
+  if (kv_kind == KV_E5M2 || kv_kind == KV_E4M3) {
+    if (q_kind != KV_F16 || dpad != 256) return hipErrorInvalidValue;
+    return kv_kind == KV_E5M2 ? launch_dec<_Float16, KV_E5M2, 256, 2>(p, nblocks, stream)
+                              : launch_dec<_Float16, KV_E4M3, 256, 2>(p, nblocks, stream);
   }
   if (q_kind != kv_kind) return hipErrorInvalidValue;
   if (q_kind == KV_F16) return launch_dec_d<_Float16>(p, dpad, nblocks, stream);

@@ -69,6 +69,7 @@ template <> struct Mfma<__bf16> {
 // Raw 8-element chunk of the KV storage type.
 template <int KVK> struct Chunk { typedef uint4 raw; };
 template <> struct Chunk<KV_E5M2> { typedef uint2 raw; };
+template <> struct Chunk<KV_E4M3> { typedef uint2 raw; };
 
 template <int KVK>
 __device__ __forceinline__ uint4 to_compute(typename Chunk<KVK>::raw x) {
@@ -77,6 +78,9 @@ __device__ __forceinline__ uint4 to_compute(typename Chunk<KVK>::raw x) {
     e5m2x4_to_f16x4(x.x, r.x, r.y);
     e5m2x4_to_f16x4(x.y, r.z, r.w);
     return r;
+  } else if constexpr (KVK == KV_E4M3) {
+    return make_uint4(e4m3x2_to_f16x2<false>(x.x), e4m3x2_to_f16x2<true>(x.x), e4m3x2_to_f16x2<false>(x.y),
+                      e4m3x2_to_f16x2<true>(x.y));
   } else {
     return x;
   }
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   constexpr int CPK = DPAD / 8;    // 8-element chunks per key row
   constexpr int KPASS = CPK / 8;   // K chunks each thread loads per tile
   constexpr int KKEYS = kThreads / CPK;  // keys per K pass
-  constexpr int ESZ = KVK == KV_E5M2 ? 1 : 2;
+  constexpr int ESZ = (KVK == KV_E5M2 || KVK == KV_E4M3) ? 1 : 2;
   typedef typename Chunk<KVK>::raw Raw;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * KS];
@@ -343,12 +347,13 @@ static hipError_t launch_d(const AttnParams& p, int dpad, int nblocks, hipStream
   }
 }
 
-// q_kind: KV_F16 or KV_BF16; kv_kind: same as q_kind, or KV_E5M2 with fp16 q.
+// q_kind: KV_F16 or KV_BF16; kv_kind: same as q_kind, or KV_E5M2 / KV_E4M3 with fp16 q.
 hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                             hipStream_t stream) {
   if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_d<_Float16, KV_F16>(p, dpad, nblocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_d<__bf16, KV_BF16>(p, dpad, nblocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_d<_Float16, KV_E5M2>(p, dpad, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_E4M3) return launch_d<_Float16, KV_E4M3>(p, dpad, nblocks, stream);
   return hipErrorInvalidValue;
 }
 
@@ -378,6 +383,7 @@ hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu)
   if (q_kind == KV_F16 && kv_kind == KV_F16) return occ_d<_Float16, KV_F16>(dpad, blocks_per_cu);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16) return occ_d<__bf16, KV_BF16>(dpad, blocks_per_cu);
   if (q_kind == KV_F16 && kv_kind == KV_E5M2) return occ_d<_Float16, KV_E5M2>(dpad, blocks_per_cu);
+  if (q_kind == KV_F16 && kv_kind == KV_E4M3) return occ_d<_Float16, KV_E4M3>(dpad, blocks_per_cu);
   return hipErrorInvalidValue;
 }
 

@@ -87,10 +87,12 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 
 }  // namespace
 
-// KV8: K and V are fp8 E5M2 (q fp16); the tiles stay 8-bit in LDS and are
-// widened to fp16 as their MFMA operands are read.
-template <typename QT, bool KV8, int DPAD, int NST>
+// F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16); the tiles stay 8-bit in
+// LDS and are widened to fp16 as their MFMA operands are read.  F8 = 0: KV of
+// the q dtype.
+template <typename QT, int F8, int DPAD, int NST>
 __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParams p) {
+  constexpr bool KV8 = F8 != 0;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
   typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
         kw = kf[rd % KPF];
         if (rd + KPF < NRD) kf[rd % KPF] = *(const uint4*)(smem + kls + k_frag(klane, rd + KPF));
       }
-      if constexpr (KV8) a = (kk & 1) ? e5m2x8_to_f16(kw.z, kw.w) : e5m2x8_to_f16(kw.x, kw.y);
+      if constexpr (KV8) a = (kk & 1) ? fp8x8_to_f16<F8>(kw.z, kw.w) : fp8x8_to_f16<F8>(kw.x, kw.y);
       else a = kw;
       mfma_s<QT, KV8>(s[0], a, qf[0][kk], kk == 0);
       mfma_s<QT>(s[1], a, qf[1][kk], kk == 0);
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 
   // V^T fragment n = (d block n / 2, key half n % 2)
   auto vt_read = [&](uint32_t vls, int n) {
-    if constexpr (KV8) return read_vt8(smem + ((vls + (n & 1) * 16 * ROWB) ^ ((n >> 1) << 5)));
+    if constexpr (KV8) return read_vt8<F8>(smem + ((vls + (n & 1) * 16 * ROWB) ^ ((n >> 1) << 5)));
     else return read_vt(smem + (vls ^ ((n >> 1) << 6)) + (n & 1) * 16 * ROWB, 8 * ROWB);
   };
 
@@ -459,22 +461,23 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 // ---- host side -------------------------------------------------------------
 
 namespace {
-template <typename QT, bool KV8, int DPAD, int NST>
+template <typename QT, int F8, int DPAD, int NST>
 hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, KV8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 }  // namespace
 
 // Prefill pass 1, head dims padded to 256, 256 query rows per work group:
 // fp16 / bf16 q with KV of the same dtype (kv_kind = q_kind), or fp16 q with
-// fp8 E5M2 KV (kv_kind = KV_E5M2).
+// fp8 KV (kv_kind = KV_E5M2 or KV_E4M3).
 hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                                   hipStream_t stream) {
   if (dpad != 256) return hipErrorInvalidValue;
-  if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_w4<_Float16, true, 256, 8>(p, nblocks, stream);
-  if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, false, 256, 5>(p, nblocks, stream);
-  if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, false, 256, 5>(p, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_w4<_Float16, KV_E5M2, 256, 8>(p, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_E4M3) return launch_w4<_Float16, KV_E4M3, 256, 8>(p, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, 0, 256, 5>(p, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, 0, 256, 5>(p, nblocks, stream);
   return hipErrorInvalidValue;
 }
 
@@ -482,7 +485,7 @@ hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
   if (dpad == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        attn_prefill_w4_kernel<_Float16, false, 256, 5>, 256, 0);
+                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5>, 256, 0);
   return hipErrorInvalidValue;
 }
 

@@ -3,8 +3,10 @@
 // them; 1CatAI/1Cat-vLLM PR #1279, commit 3, the second half reading the first
 // half's KV writes).  Same dtype: an exact copy.  fp8 E5M2 cache (1CatAI/
 // 1Cat-vLLM PR #616 original, "Test Result", fp8_e5m2 KV paragraph, per-tensor
-// scale): byte = E5M2 of (x / scale) computed in fp32, rounded to nearest with
-// ties to even, saturated to +-57344 (the largest finite E5M2), NaN kept NaN.
+// scale; the same page's "Test Plan" names an e4m3 path): byte = the fp8 code
+// of (x / scale) computed in fp32, rounded to nearest with ties to even,
+// saturated to the largest finite value (57344 for E5M2, 448 for E4M3), NaN
+// kept NaN.
 //
 // One thread per 8 elements of one (token, kv head) row: a 16-byte load of
 // fp16 / bf16 (32 of fp32) and a 16-byte store (8 for E5M2), coalesced along
@@ -40,7 +42,33 @@ __device__ __forceinline__ uint32_t f32_to_e5m2_sat(float x) {
   return sign | code;
 }
 
-template <typename ST, bool FP8>
+// E4M3 byte of a float32: nearest even on the 20 dropped mantissa bits of a
+// normal result (|x| >= 2^-6), units of 2^-9 below, saturation to 0x7E (448;
+// 0x7F is the format's NaN), NaN -> 0x7F (sign kept).
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  uint32_t code;
+  if (a >= 0x3C800000u) {
+    const uint32_t r = (a + 0x0007FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;  // past 448 (and infinities): saturate
+  } else {
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);  // 0..8 (8 = 2^-6, the smallest normal)
+  }
+  return sign | code;
+}
+
+template <int F8>
+__device__ __forceinline__ uint32_t f32_to_fp8_sat(float x) {
+  if constexpr (F8 == KV_E4M3) return f32_to_e4m3_sat(x);
+  else return f32_to_e5m2_sat(x);
+}
+
+// F8 = 0: copy; KV_E5M2 / KV_E4M3: quantise.
+template <typename ST, int F8>
 __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_new, const ST* __restrict__ v_new,
                                                        const int* __restrict__ cu_seqlens_q,
                                                        const int* __restrict__ seq_lens,
@@ -69,7 +97,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_
   for (int kvi = 0; kvi < 2; ++kvi) {
     const ST* s = (kvi == 0 ? k_new : v_new) + src;
     char* base = kvi == 0 ? k_pages : v_pages;
-    if constexpr (FP8) {
+    if constexpr (F8 != 0) {
       const float sc = kvi == 0 ? k_scale : v_scale;
       float x[8];
       if constexpr (sizeof(ST) == 4) {
@@ -84,8 +112,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo |= f32_to_e5m2_sat(x[i] / sc) << (8 * i);
-        hi |= f32_to_e5m2_sat(x[i + 4] / sc) << (8 * i);
+        lo |= f32_to_fp8_sat<F8>(x[i] / sc) << (8 * i);
+        hi |= f32_to_fp8_sat<F8>(x[i + 4] / sc) << (8 * i);
       }
       *(uint2*)(base + dst) = make_uint2(lo, hi);
     } else {
@@ -100,31 +128,32 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_
   }
 }
 
-template <typename ST>
-hipError_t launch_kv(const KvWriteParams& w, bool fp8, hipStream_t stream) {
+template <typename ST, int F8>
+hipError_t launch_kv_f(const KvWriteParams& w, hipStream_t stream) {
   const int64_t items = (int64_t)w.max_q * w.num_kv_heads * (w.head_dim >> 3);
   const int bps = (int)((items + 255) / 256);
   const dim3 grid((unsigned)((int64_t)bps * w.num_seqs));
-  if (fp8)
-    hipLaunchKernelGGL((kv_write_kernel<ST, true>), grid, dim3(256), 0, stream, (const ST*)w.k_new,
-                       (const ST*)w.v_new, w.cu_seqlens_q, w.seq_lens, w.block_tables, w.max_pages,
-                       (char*)w.k_pages, (char*)w.v_pages, w.stride_page, w.stride_token, w.stride_head,
-                       w.page_size, w.num_kv_heads, w.head_dim, bps, w.k_scale, w.v_scale);
-  else
-    hipLaunchKernelGGL((kv_write_kernel<ST, false>), grid, dim3(256), 0, stream, (const ST*)w.k_new,
-                       (const ST*)w.v_new, w.cu_seqlens_q, w.seq_lens, w.block_tables, w.max_pages,
-                       (char*)w.k_pages, (char*)w.v_pages, w.stride_page, w.stride_token, w.stride_head,
-                       w.page_size, w.num_kv_heads, w.head_dim, bps, 1.0f, 1.0f);
+  hipLaunchKernelGGL((kv_write_kernel<ST, F8>), grid, dim3(256), 0, stream, (const ST*)w.k_new, (const ST*)w.v_new,
+                     w.cu_seqlens_q, w.seq_lens, w.block_tables, w.max_pages, (char*)w.k_pages, (char*)w.v_pages,
+                     w.stride_page, w.stride_token, w.stride_head, w.page_size, w.num_kv_heads, w.head_dim, bps,
+                     w.k_scale, w.v_scale);
   return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_kv(const KvWriteParams& w, int cache_kind, hipStream_t stream) {
+  if (cache_kind == KV_E5M2) return launch_kv_f<ST, KV_E5M2>(w, stream);
+  if (cache_kind == KV_E4M3) return launch_kv_f<ST, KV_E4M3>(w, stream);
+  return launch_kv_f<ST, 0>(w, stream);
 }
 
 }  // namespace
 
-hipError_t launch_kv_write(const KvWriteParams& w, int src_kind, bool fp8, hipStream_t stream) {
+hipError_t launch_kv_write(const KvWriteParams& w, int src_kind, int cache_kind, hipStream_t stream) {
   switch (src_kind) {
-    case KV_F32: return launch_kv<float>(w, fp8, stream);
-    case KV_F16: return launch_kv<_Float16>(w, fp8, stream);
-    case KV_BF16: return launch_kv<__bf16>(w, fp8, stream);
+    case KV_F32: return launch_kv<float>(w, cache_kind, stream);
+    case KV_F16: return launch_kv<_Float16>(w, cache_kind, stream);
+    case KV_BF16: return launch_kv<__bf16>(w, cache_kind, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,7 +11,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum KvKind : int { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_E5M2 = 3 };
+enum KvKind : int { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_E5M2 = 3, KV_E4M3 = 4 };
 
 // Keys per tile of the split partition (the decode parts and the prefill parts
 // are both cut on this grid).
@@ -90,6 +90,14 @@ __device__ __forceinline__ void split_range(int L, int S, int s, int part_keys, 
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp8 E4M3 bytes (byte 2 w and 2 w + 1 of x) -> two fp16 in one 32-bit
+// word, lower byte in the lower half: the gfx950 conversion with a scale of 1
+// (every E4M3 value is exact in fp16).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+}
 
 // fp8 E5M2 byte -> fp16 bits: E5M2 is the high byte of an fp16 with the same
 // sign/exponent/mantissa layout, so the conversion is exact.

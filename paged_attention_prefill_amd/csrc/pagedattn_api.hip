@@ -30,7 +30,7 @@ int mfma_dma_rows(int dpad);
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream);
 int decode_rows_per_group();
-hipError_t launch_kv_write(const KvWriteParams& w, int src_kind, bool fp8, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteParams& w, int src_kind, int cache_kind, hipStream_t stream);
 int mfma_rows_per_group();
 int valu_rows_per_group();
 }  // namespace pa
@@ -58,9 +58,12 @@ size_t dtype_size(int dt) {
     case PA_F16: return 2;
     case PA_BF16: return 2;
     case PA_FP8_E5M2: return 1;
+    case PA_FP8_E4M3: return 1;
     default: return 0;
   }
 }
+
+bool is_fp8(int dt) { return dt == PA_FP8_E5M2 || dt == PA_FP8_E4M3; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -69,12 +72,12 @@ int check_supported(int q_dtype, int kv_dtype, int head_dim, int page_size, int 
                     const char** reason) {
   const char* r = nullptr;
   int st = PA_OK;
-  if (dtype_size(q_dtype) == 0 || q_dtype == PA_FP8_E5M2) {
+  if (dtype_size(q_dtype) == 0 || is_fp8(q_dtype)) {
     st = PA_ERR_UNSUPPORTED, r = "q dtype must be F32, F16 or BF16";
   } else if (dtype_size(kv_dtype) == 0) {
     st = PA_ERR_UNSUPPORTED, r = "unknown KV dtype";
-  } else if (!(kv_dtype == q_dtype || (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_F16))) {
-    st = PA_ERR_UNSUPPORTED, r = "KV dtype must equal q dtype, or be FP8_E5M2 with F16 q";
+  } else if (!(kv_dtype == q_dtype || (is_fp8(kv_dtype) && q_dtype == PA_F16))) {
+    st = PA_ERR_UNSUPPORTED, r = "KV dtype must equal q dtype, or be FP8_E5M2 / FP8_E4M3 with F16 q";
   } else if (head_dim < 16 || head_dim > 256 || head_dim % 16 != 0) {
     st = PA_ERR_UNSUPPORTED, r = "head_dim must be a multiple of 16 in [16, 256]";
   } else if (page_size < 16 || page_size % 16 != 0) {
@@ -95,6 +98,7 @@ int kind_of(int dt) {
     case PA_F32: return pa::KV_F32;
     case PA_F16: return pa::KV_F16;
     case PA_BF16: return pa::KV_BF16;
+    case PA_FP8_E4M3: return pa::KV_E4M3;
     default: return pa::KV_E5M2;
   }
 }
@@ -119,8 +123,8 @@ int check_kv(const pa_kv_cache* kv, int q_dtype, int hq) {
   if (!std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
     return fail(PA_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be finite");
   if (!(kv->k_scale > 0.0f)) return fail(PA_ERR_INVALID_ARGUMENT, "k_scale must be positive");
-  if (kv->dtype != PA_FP8_E5M2 && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
-    return fail(PA_ERR_UNSUPPORTED, "k_scale / v_scale apply to FP8_E5M2 KV only (must be 1)");
+  if (!is_fp8(kv->dtype) && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
+    return fail(PA_ERR_UNSUPPORTED, "k_scale / v_scale apply to fp8 KV only (must be 1)");
   return PA_OK;
 }
 
@@ -167,7 +171,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
 KernelKind kernel_for(int q_dtype, int kv_dtype, int dpad, bool decode) {
   if (q_dtype == PA_F32) return K_VALU;
-  if (kv_dtype == PA_FP8_E5M2) return dpad == 256 ? K_DMA : K_REGSTAGE;
+  if (is_fp8(kv_dtype)) return dpad == 256 ? K_DMA : K_REGSTAGE;
   (void)decode;
   return K_DMA;
 }
@@ -311,13 +315,13 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.write_partial = partial ? 1 : 0;
   p.qtiles = qtiles;
   p.num_work = (int)nwork;
-  p.scale_log2 = scale * (kv->dtype == PA_FP8_E5M2 ? kv->k_scale : 1.0f) * 1.4426950408889634f;
-  p.v_scale = kv->dtype == PA_FP8_E5M2 ? kv->v_scale : 1.0f;
+  p.scale_log2 = scale * (is_fp8(kv->dtype) ? kv->k_scale : 1.0f) * 1.4426950408889634f;
+  p.v_scale = is_fp8(kv->dtype) ? kv->v_scale : 1.0f;
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
                  : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, kk, dp, (int)nblocks, stream)
-                                    : kk == pa::KV_E5M2
+                                    : (kk == pa::KV_E5M2 || kk == pa::KV_E4M3)
                                         ? pa::launch_attn_prefill_w4(p, qk, kk, dp, (int)nblocks, stream)
                                         : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
                                  : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
@@ -431,8 +435,8 @@ int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const i
   if (kv == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "kv is NULL");
   int st = check_kv(kv, src_dtype, kv->num_kv_heads);
   if (st != PA_OK) return st;
-  if (kv->dtype == PA_FP8_E5M2 && !(kv->v_scale > 0.0f))
-    return fail(PA_ERR_INVALID_ARGUMENT, "v_scale must be positive for an FP8_E5M2 cache");
+  if (is_fp8(kv->dtype) && !(kv->v_scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "v_scale must be positive for an fp8 cache");
   if (num_seqs == 0 || total_q == 0) return ok();
   if (!k_new || !v_new || !cu_seqlens_q || !seq_lens || !block_tables)
     return fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -459,7 +463,8 @@ int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const i
   w.page_size = kv->page_size;
   w.k_scale = kv->k_scale;
   w.v_scale = kv->v_scale;
-  hipError_t e = pa::launch_kv_write(w, kind_of(src_dtype), kv->dtype == PA_FP8_E5M2, (hipStream_t)stream);
+  hipError_t e = pa::launch_kv_write(w, kind_of(src_dtype), is_fp8(kv->dtype) ? kind_of(kv->dtype) : 0,
+                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "KV write launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -8,13 +8,13 @@ Recipe (every case):
   * ``rng = numpy.random.default_rng(seed)``; draws in this order: extra row
     lengths (decode batch only), the page permutation, q, k pages, v pages.
   * q, k, v ~ N(0, 1) drawn in float32, then rounded to the storage dtype
-    (round-to-nearest-even through torch's casts); fp8_e5m2 KV is N(0, 1)
-    rounded to E5M2 with per-tensor scale 1.0.
+    (round-to-nearest-even through torch's casts); fp8 KV is N(0, 1) rounded
+    to E5M2 (or E4M3) with per-tensor scale 1.0, stored as bytes.
   * Each sequence gets ceil(seq_len / page_size) pages.  The pool holds those
     plus spare pages (10 % by default, at least ``min_spare``); the page ids
     are a random permutation of the pool, so pages are out of order.
   * Poison: spare pages and the slots past seq_len in a sequence's last page
-    hold NaN (E5M2 byte 0x7F for fp8).  Block-table entries past a sequence's
+    hold NaN (byte 0x7F for fp8, a NaN in both formats).  Block-table entries past a sequence's
     pages point at a poisoned spare page, so any read outside the visible
     range turns the result into NaN instead of touching memory out of bounds.
   * KV layout: logical [num_pages, page_size, Hkv, D] with D contiguous; the
@@ -28,7 +28,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-E5M2_NAN_BYTE = 0x7F
+FP8_NAN_BYTE = 0x7F  # a NaN of both E5M2 and E4M3
+E5M2_NAN_BYTE = FP8_NAN_BYTE
 
 _TORCH_DTYPES = {
     "f32": torch.float32,
@@ -52,7 +53,7 @@ class PagedCase:
     head_dim: int
     scale: float
     q_kind: str                     # 'f32' | 'f16' | 'bf16'
-    kv_kind: str                    # 'f32' | 'f16' | 'bf16' | 'e5m2'
+    kv_kind: str                    # 'f32' | 'f16' | 'bf16' | 'e5m2' | 'e4m3'
     k_scale: float = 1.0
     v_scale: float = 1.0
     num_splits: int = 16
@@ -84,15 +85,19 @@ class PagedCase:
         return int(self.block_tables.shape[1])
 
 
-def _fill_normal(dst, rng, chunk=1 << 24):
-    """Fill a contiguous CPU tensor with N(0,1) float32 draws rounded to its dtype."""
+_FP8_TORCH = {"e5m2": torch.float8_e5m2, "e4m3": torch.float8_e4m3fn}
+
+
+def _fill_normal(dst, rng, chunk=1 << 24, fp8="e5m2"):
+    """Fill a contiguous CPU tensor with N(0,1) float32 draws rounded to its dtype
+    (uint8 storage: the bytes of the fp8 format `fp8`)."""
     flat = dst.view(-1)
     n = flat.numel()
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         src = torch.from_numpy(rng.standard_normal(e - s, dtype=np.float32))
-        if dst.dtype == torch.uint8:  # fp8_e5m2 storage
-            flat[s:e] = src.to(torch.float8_e5m2).view(torch.uint8)
+        if dst.dtype == torch.uint8:  # fp8 storage
+            flat[s:e] = src.to(_FP8_TORCH[fp8]).view(torch.uint8)
         else:
             flat[s:e] = src.to(dst.dtype)
 
@@ -134,15 +139,15 @@ def make_case(name, q_lens, seq_lens, num_q_heads, num_kv_heads, head_dim, page_
     q = torch.empty((total_q, Hq, D), dtype=_TORCH_DTYPES[q_kind])
     _fill_normal(q, rng)
 
-    store_dtype = torch.uint8 if kv_kind == "e5m2" else _TORCH_DTYPES[kv_kind]
+    store_dtype = torch.uint8 if kv_kind in _FP8_TORCH else _TORCH_DTYPES[kv_kind]
     phys_shape = (num_pages, P, Hkv, D) if layout == "NHD" else (num_pages, Hkv, P, D)
     pools = []
     for _ in range(2):
         t = torch.empty(phys_shape, dtype=store_dtype)
-        _fill_normal(t, rng)
+        _fill_normal(t, rng, fp8=kv_kind if kv_kind in _FP8_TORCH else "e5m2")
         view = t if layout == "NHD" else t.permute(0, 2, 1, 3)
         if poison:
-            bad = E5M2_NAN_BYTE if kv_kind == "e5m2" else float("nan")
+            bad = FP8_NAN_BYTE if kv_kind in _FP8_TORCH else float("nan")
             view[torch.from_numpy(spare_ids.astype(np.int64))] = bad
             for b in range(B):
                 tail = int(seq_lens[b]) % P
@@ -249,7 +254,7 @@ def mixed_step(seed=5, kv_kind="f16"):
 
 def to_numpy64(t: torch.Tensor, kv_kind: Optional[str] = None):
     """Exact widening of a CPU tensor for the oracle (fp8 stays as raw bytes)."""
-    if kv_kind == "e5m2":
+    if kv_kind in _FP8_TORCH:
         return t.numpy()
     return t.to(torch.float64).numpy()
 
@@ -266,6 +271,8 @@ def to_device(case, device="cuda"):
         v = v.permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
     else:
         k, v = dev(k.contiguous()), dev(v.contiguous())
+    if case.kv_kind == "e4m3":  # the binding reads the fp8 format from the dtype (uint8 = E5M2)
+        k, v = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
     return dict(q=dev(case.q.contiguous()), k=k, v=v,
                 cu=torch.from_numpy(case.cu_seqlens_q.astype(np.int32)).to(device),
                 seq_lens=torch.from_numpy(case.seq_lens.astype(np.int32)).to(device),

@@ -19,12 +19,12 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA = \
     0, -1, -2, -3, -4, -5
-PA_F32, PA_F16, PA_BF16, PA_FP8_E5M2 = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_FP8_E5M2, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 DECODE_MAX_Q = 16
 SPLIT_TILE = 32
 
 _TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
-                torch.uint8: PA_FP8_E5M2, torch.float8_e5m2: PA_FP8_E5M2}
+                torch.uint8: PA_FP8_E5M2, torch.float8_e5m2: PA_FP8_E5M2, torch.float8_e4m3fn: PA_FP8_E4M3}
 _PA_TO_TORCH = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
 
 
@@ -230,7 +230,8 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
 def write_kv(k_new, v_new, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q, *, k_scale=1.0,
              v_scale=1.0, stream=None):
     """pa_write_kv: k_new / v_new [total_q, Hkv, D] into the pages at each sequence's
-    last q_len positions (uint8 pages: fp8_e5m2 of x / scale)."""
+    last q_len positions (uint8 / float8_e5m2 pages: E5M2 of x / scale;
+    float8_e4m3fn pages: E4M3 of x / scale)."""
     for t, name in ((k_new, "k_new"), (v_new, "v_new")):
         if not t.is_contiguous() or t.dim() != 3:
             raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous [total_q, Hkv, D] tensor")

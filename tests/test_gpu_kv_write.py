@@ -16,7 +16,8 @@ from paged_attention_prefill_amd import ops
 
 pytestmark = pytest.mark.gpu
 
-_BITS = {torch.float16: torch.int16, torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.uint8: torch.uint8}
+_BITS = {torch.float16: torch.int16, torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.uint8: torch.uint8,
+         torch.float8_e4m3fn: torch.uint8}
 
 
 def say(*a):
@@ -66,18 +67,19 @@ def test_kv_write_same_dtype_is_an_exact_copy(kind, layout):
     assert np.array_equal(raw(d["k"]), ko) and np.array_equal(raw(d["v"]), vo)
 
 
-@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.5, 3.0), (0.0078125, 1.7)])
-def test_kv_write_fp8_quantisation_is_bit_exact(k_scale, v_scale):
-    case = gen.make_case("kvw_fp8", q_kind="f16", kv_kind="e5m2", seed=63, k_scale=k_scale, v_scale=v_scale,
+@pytest.mark.parametrize("fmt,k_scale,v_scale", [("e5m2", 1.0, 1.0), ("e5m2", 0.5, 3.0), ("e5m2", 0.0078125, 1.7),
+                                                 ("e4m3", 1.0, 1.0), ("e4m3", 0.01, 250.0), ("e4m3", 0.3, 0.7)])
+def test_kv_write_fp8_quantisation_is_bit_exact(fmt, k_scale, v_scale):
+    case = gen.make_case(f"kvw_{fmt}", q_kind="f16", kv_kind=fmt, seed=63, k_scale=k_scale, v_scale=v_scale,
                          **dict(CASE, head_dim=256, page_size=64))
     kn, vn = new_rows(case, "f16", 64, specials=True)
     d = run_write(case, kn, vn)
     ko, vo = oracle.write_kv(raw(case.k_pool), raw(case.v_pool), kn.float().numpy(), vn.float().numpy(),
-                             case.cu_seqlens_q, case.seq_lens, case.block_tables, fp8=True, k_scale=k_scale,
+                             case.cu_seqlens_q, case.seq_lens, case.block_tables, fp8=fmt, k_scale=k_scale,
                              v_scale=v_scale)
     gk, gv = raw(d["k"]), raw(d["v"])
     bad = int((gk != ko).sum() + (gv != vo).sum())
-    say(f"  fp8 write: {bad} bytes differ of {gk.size + gv.size}")
+    say(f"  fp8 {fmt} write: {bad} bytes differ of {gk.size + gv.size}")
     assert bad == 0
 
 

@@ -1,7 +1,7 @@
 """Parity of the HIP path with the fp64 oracle, through the C ABI (needs an MI355X).
 
-Bars (max-abs error against the oracle): fp32 1e-5; fp16/bf16 2e-2; fp8_e5m2
-KV 5e-2 against the oracle fed the same dequantized values.  Besides the
+Bars (max-abs error against the oracle): fp32 1e-5; fp16/bf16 2e-2; fp8 KV
+(E5M2 or E4M3) 5e-2 against the oracle fed the same dequantized values.  Besides the
 max-abs bar every comparison also reports max|err| / max|ref| and
 rms(err) / rms(ref), with a self-imposed bar of 1e-2 on the rms ratio for
 16-bit inputs (at long contexts the outputs are small and the absolute bar
@@ -21,8 +21,8 @@ from paged_attention_prefill_amd import ops
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2}
-RMS_BAR = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e5m2": 2e-2}
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2, "e4m3": 5e-2}
+RMS_BAR = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e5m2": 2e-2, "e4m3": 2e-2}
 
 
 def say(*a):
@@ -39,7 +39,7 @@ def _gpu():
 
 
 def oracle_pools(case):
-    kind = "e5m2" if case.kv_kind == "e5m2" else "float"
+    kind = case.kv_kind if case.kv_kind in ("e5m2", "e4m3") else "float"
     k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, case.k_scale)
     v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
     return k, v
@@ -480,3 +480,31 @@ def test_mixed_step_sampled(kv_kind):
     ref, rl = run_oracle(chunk, rows=rows, pools=(k, v))
     compare(f"mixed chunk {kv_kind} (sampled {len(rows)})", kv_kind, out[rows[:, 0], rows[:, 1]], ref,
             lse[rows[:, 0], rows[:, 1]], rl)
+
+
+# ------------------------------------------------------------------ fp8 E4M3 KV
+
+@pytest.mark.parametrize("D,P", [(64, 16), (128, 48), (256, 16), (256, 64), (160, 32)])
+def test_e4m3_prefill_and_decode(D, P):
+    """E4M3 KV (fp16 q) against the oracle fed the same decoded values: prefill
+    with 1 and 3 parts, and the decode of the two last rows."""
+    c = gen.make_case(f"e4m3_D{D}_P{P}", q_lens=[70, 1, 5], seq_lens=[400, 333, 1200], num_q_heads=8,
+                      num_kv_heads=2, head_dim=D, page_size=P, q_kind="f16", kv_kind="e4m3", seed=D + 3 * P,
+                      k_scale=0.75, v_scale=1.5)
+    ref, rl = run_oracle(c)
+    for splits in (1, 3):
+        out, lse = gpu_prefill(c, splits=splits)
+        compare(f"e4m3 prefill D={D} P={P} S={splits}", "e4m3", out, ref, lse, rl)
+    dec = gen.select_seqs(c, [1, 2])
+    out, lse = gpu_decode(dec, splits=8, max_q=5)
+    compare(f"e4m3 decode D={D} P={P}", "e4m3", out.float().cpu().numpy(), ref[70:], lse.cpu().numpy(), rl[70:])
+
+
+def test_e4m3_verify_row_equals_serial_decode_bitwise():
+    case = gen.make_case("verify_e4m3", q_lens=[5, 1], seq_lens=[3000, 900], num_q_heads=24, num_kv_heads=4,
+                         head_dim=256, page_size=816, q_kind="f16", kv_kind="e4m3", seed=77)
+    ser = gen.expand_row(case, 0)
+    out_v, lse_v = gpu_decode_fixed(case, part_keys=512, parts=9, max_q=5)
+    out_s, lse_s = gpu_decode_fixed(ser, part_keys=512, parts=6, max_q=1)
+    assert torch.equal(bits(out_v[:5]), bits(out_s)) and torch.equal(lse_v[:5].view(torch.int32),
+                                                                       lse_s.view(torch.int32))

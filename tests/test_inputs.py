@@ -18,12 +18,12 @@ def _check_layout(case):
         seen |= set(pages)
         for j in range(L):
             k = case.k_pool[pages[j // P], j % P].float()
-            assert torch.isfinite(k).all() if case.kv_kind != "e5m2" else (
-                case.k_pool[pages[j // P], j % P] != gen.E5M2_NAN_BYTE).all()
+            assert torch.isfinite(k).all() if case.kv_kind not in ("e5m2", "e4m3") else (
+                (case.k_pool[pages[j // P], j % P] & 0x7F) != gen.FP8_NAN_BYTE).all()
         if n and L % P:
             tail = case.k_pool[pages[-1], L % P:]
-            if case.kv_kind == "e5m2":
-                assert (tail == gen.E5M2_NAN_BYTE).all()
+            if case.kv_kind in ("e5m2", "e4m3"):
+                assert (tail == gen.FP8_NAN_BYTE).all()
             else:
                 assert torch.isnan(tail.float()).all()
         # entries past the sequence's pages point at a poisoned spare page
@@ -52,6 +52,12 @@ def test_fp8_and_hnd_layouts():
     c = gen.make_case("f8", [2, 5], [33, 100], 6, 2, 64, 16, q_kind="f16", kv_kind="e5m2", seed=3)
     assert c.k_pool.dtype == torch.uint8
     _check_layout(c)
+    e = gen.make_case("e4", [2, 5], [33, 100], 6, 2, 64, 16, q_kind="f16", kv_kind="e4m3", seed=3)
+    assert e.k_pool.dtype == torch.uint8
+    _check_layout(e)
+    # E4M3 bytes of N(0, 1) draws: decoded values are the draws rounded to E4M3
+    vals = e.k_pool[e.block_tables[1, 0]].view(torch.float8_e4m3fn).float()
+    assert torch.isfinite(vals).all() and vals.abs().max() < 8
     h = gen.make_case("hnd", [2, 5], [33, 100], 6, 2, 64, 16, q_kind="f16", seed=3, layout="HND")
     assert h.k_pool.shape == (h.num_pages, 16, 2, 64)
     assert h.k_pool.stride(1) == 64 and h.k_pool.stride(2) == 16 * 64
