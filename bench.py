@@ -7,7 +7,8 @@ pages' D256 chunked-prefill measurement, at the full head count of the model),
 followed by the split-KV decode of a q=1 row over the same 152,048-token cache
 (pass 1 + merge).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_chunk|mixed_step|decode_batch|varlen]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload long_chunk|mixed_step|mixed_step_fp8|mixed_step_e4m3|decode_batch|varlen]
 
 Prints ONE JSON line.  `value` is the step's algorithmic FLOPs (causal-exact:
 4 * D * Hq per attended pair) divided by the step time; the prefill TFLOPS and
@@ -127,7 +128,8 @@ class Call:
 
 # The calls of one step of each workload, in launch order.
 WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "mixed_step": ["prefill", "decode"],
-                  "mixed_step_fp8": ["prefill", "decode"], "decode_batch": ["decode"], "varlen": ["prefill"]}
+                  "mixed_step_fp8": ["prefill", "decode"], "mixed_step_e4m3": ["prefill", "decode"],
+                  "decode_batch": ["decode"], "varlen": ["prefill"]}
 
 
 def build_workload(name):
@@ -156,6 +158,13 @@ def build_workload(name):
         desc = {"workload": "mixed step, fp8_e5m2 KV", "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256,
                 "page_size": 816, "kv_dtype": "e5m2"}
         return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
+    if name == "mixed_step_e4m3":
+        c = gen.mixed_step(kv_kind="e4m3")
+        ver = gen.select_seqs(c, [0], name="verify q=5 at 240000 (e4m3)")
+        chunk = gen.select_seqs(c, [1], name="prefill 784 after 104000 (e4m3)")
+        desc = {"workload": "mixed step, fp8 E4M3 KV", "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256,
+                "page_size": 816, "kv_dtype": "e4m3"}
+        return desc, [("prefill", chunk, "auto"), ("decode", ver, 64)]
     if name == "decode_batch":
         c = gen.decode_batch(kind="bf16")
         desc = {"workload": "split-KV decode batch: 32 rows q=1, lengths 0..10000, MHA 16 heads, D 128, page 16",
@@ -172,7 +181,7 @@ def build_workload(name):
 
 def prefill_kernel_name(desc):
     """Pass-1 kernel that serves the prefill of this workload."""
-    if desc.get("kv_dtype") == "e5m2":
+    if desc.get("kv_dtype") in ("e5m2", "e4m3") and desc.get("head_dim", 0) <= 128:
         return "attn_mfma_kernel"
     return "attn_prefill_w4_kernel" if desc.get("head_dim", 0) > 128 else "attn_mfma_dma_kernel"
 
@@ -193,7 +202,7 @@ def cpu_baseline(case, budget_rows, seed=0):
     rng = np.random.default_rng(seed)
     toks = np.sort(rng.choice(case.total_q, size=min(budget_rows, case.total_q), replace=False))
     rows = np.array([(t, h) for t in toks for h in range(case.num_q_heads)], dtype=np.int64)
-    kind = "e5m2" if case.kv_kind == "e5m2" else "float"
+    kind = case.kv_kind if case.kv_kind in ("e5m2", "e4m3") else "float"
     k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, case.k_scale)
     v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
     q64 = gen.to_numpy64(case.q)
@@ -441,7 +450,8 @@ def main():
             if s == 0:
                 s = ops.auto_splits(case.total_q, case.num_seqs, case.max_seqlen_q, case.num_q_heads,
                                     case.num_kv_heads, case.head_dim, ops._TORCH_TO_PA[case.q.dtype],
-                                    ops.PA_FP8_E5M2 if case.kv_kind == "e5m2" else ops._TORCH_TO_PA[case.q.dtype])
+                                    {"e5m2": ops.PA_FP8_E5M2, "e4m3": ops.PA_FP8_E4M3}.get(
+                                        case.kv_kind, ops._TORCH_TO_PA[case.q.dtype]))
         else:
             s = a.decode_splits or splits
         log(f"  {kind}: {case.name}, splits {s}")

@@ -13,7 +13,7 @@ read and the FP32 partial states written and read back by the merge.
 
 import numpy as np
 
-KV_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e5m2": 1}
+KV_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e5m2": 1, "e4m3": 1}
 Q_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
