@@ -72,7 +72,7 @@ extern "C" {
 #define PA_VERSION 1
 #define PA_DECODE_MAX_Q 16       /* largest q of a decode / verify row */
 #define PA_DECODE_SPLIT_TILE 32  /* keys per tile of the split partition */
-#define PA_PREFILL_MAX_AUTO_SPLITS 4
+#define PA_PREFILL_MAX_AUTO_SPLITS 16
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -115,12 +115,16 @@ typedef struct pa_kv_cache {
  *   scores, which commutes with a positive scale only.
  *   max_seqlen_q bounds every cu_seqlens_q[b+1] - cu_seqlens_q[b] (it sizes the
  *   static grid).  num_kv_splits: 1 = no key split; 2..64 = split every query
- *   tile's keys into that many whole-tile parts and merge; 0 = choose 1..4 by
- *   how many full waves of work groups fill the device (1CatAI/1Cat-vLLM
- *   PR #1279, commit 5), which depends on the device, not on the batch.
- *   With num_kv_splits != 1 the workspace must hold
+ *   tile's keys into that many whole-tile parts and merge; 0 = choose by how
+ *   many full waves of work groups fill the device (1CatAI/1Cat-vLLM PR #1279,
+ *   commit 5): up to 4 parts when the query tiles alone cover the device, up
+ *   to PA_PREFILL_MAX_AUTO_SPLITS when they do not, and never more than the
+ *   workspace holds (no workspace: 1).  The choice depends on the shape of the
+ *   call and the device, so num_kv_splits = 0 is not batch-invariant; any
+ *   fixed count is.  With num_kv_splits >= 2 the workspace must hold
  *   pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits)
- *   bytes of device memory (float-aligned); otherwise it may be NULL.
+ *   bytes of device memory (8-byte aligned); pa_prefill_workspace_bytes(...,
+ *   0) is the size that lets the automatic choice use every option.
  *   out (with lse) may be NULL when num_kv_splits >= 2: then only the first
  *   pass runs and the workspace holds the FP32 records [total_q, num_q_heads,
  *   num_kv_splits, head_dim + 2] for pa_merge_states (a caller that merges

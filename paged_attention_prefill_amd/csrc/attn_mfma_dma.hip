@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   const int split = w % p.num_splits;
   w /= p.num_splits;
   const int kvh = w % p.num_kv_heads;
-  const int seq = w / p.num_kv_heads;
+  const int seq = seq_by_rank(p, w / p.num_kv_heads, (int*)smem, tid, 64 * WAVES);
 
   const int q0 = p.cu_seqlens_q[seq];
   const int qlen = p.cu_seqlens_q[seq + 1] - q0;

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const int split = w % p.num_splits;
   w /= p.num_splits;
   const int kvh = w % p.num_kv_heads;
-  const int seq = w / p.num_kv_heads;
+  const int seq = seq_by_rank(p, w / p.num_kv_heads, (int*)smem, tid, 256);
 
   const int q0 = p.cu_seqlens_q[seq];
   const int qlen = p.cu_seqlens_q[seq + 1] - q0;

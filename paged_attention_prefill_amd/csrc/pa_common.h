@@ -69,6 +69,33 @@ __device__ __forceinline__ int xcd_remap(int bid) {
   return (row * 8 + ((xcd - row) & 7)) * kXcdGroup + (k % kXcdGroup);
 }
 
+// Sequence taken at position r of the grid's sequence order: longest first
+// (seq_lens descending, ties by index), so that the work groups of the longest
+// sequences, which set the end of a varlen call, are handed out before the
+// short ones.  Every thread of the group calls it (it holds two barriers);
+// `lds` is at least kRankMaxSeqs + 1 ints of LDS that the group does not
+// otherwise use yet.  Beyond kRankMaxSeqs sequences the order is the given one.
+constexpr int kRankMaxSeqs = 256;
+__device__ __forceinline__ int seq_by_rank(const AttnParams& p, int r, int* lds, int tid, int nthreads) {
+  const int B = p.num_seqs;
+  if (B <= 1 || B > kRankMaxSeqs) return r;
+  for (int b = tid; b < B; b += nthreads) lds[b] = p.seq_lens[b];
+  __syncthreads();
+  if (tid < B) {
+    const int L = lds[tid];
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int Lj = lds[j];
+      rank += (Lj > L) || (Lj == L && j < tid);
+    }
+    if (rank == r) lds[kRankMaxSeqs] = tid;
+  }
+  __syncthreads();
+  const int seq = lds[kRankMaxSeqs];
+  __syncthreads();  // the scratch is free again
+  return seq;
+}
+
 // Key range [lo, hi) of part `s` of a row with L keys.  part_keys == 0: S
 // parts of whole kSplitTile-key tiles cut from the row's own length,
 // per = ceil(ceil(L / T) / S) tiles each.  part_keys > 0 (a multiple of T):

@@ -148,14 +148,21 @@ int device_cus(int* cus) {
   return PA_OK;
 }
 
-// Split count in 1..4 that finishes the work groups in the fewest full waves on
-// this device (1CatAI/1Cat-vLLM PR #1279, commit 5); ties go to fewer splits.
-int auto_splits(int64_t active_groups, int slots) {
+// Split count for num_kv_splits = 0, by full waves of work groups on this
+// device (1CatAI/1Cat-vLLM PR #1279, commit 5, which picks <= 4 on Turing):
+// cost(S) = ceil(A S / slots) / S, the makespan in units of one unsplit group,
+// plus 0.2 % per extra part for the merge and the per-group start-up.  When
+// the A active groups already cover the slots, parts only trade granularity
+// and S stays <= 4; when they do not (a long chunk of few query tiles), up to
+// max_s parts fill the device (a 784-token chunk after 104K keys: 76 groups,
+// 10 parts run 8 % faster than 3).  Ties go to fewer parts.
+int auto_splits(int64_t active_groups, int slots, int max_s) {
+  const int cap = active_groups >= slots ? (max_s < 4 ? max_s : 4) : max_s;
   int best = 1;
   double best_cost = 1e300;
-  for (int s = 1; s <= PA_PREFILL_MAX_AUTO_SPLITS; ++s) {
+  for (int s = 1; s <= cap; ++s) {
     const int64_t waves = (active_groups * s + slots - 1) / slots;
-    const double cost = (double)waves / s;
+    const double cost = (double)waves / s + 0.002 * (s - 1);
     if (cost < best_cost - 1e-9) best_cost = cost, best = s;
   }
   return best;
@@ -271,7 +278,7 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   const int64_t tiles_grid = ceil_div((int64_t)max_seqlen_q * g, rows) * num_seqs;
   const int64_t tiles_est = ceil_div((int64_t)total_q * g, rows) + num_seqs - 1;
   const int64_t active = (tiles_grid < tiles_est ? tiles_grid : tiles_est) * num_kv_heads;
-  return auto_splits(active, cus * occ);
+  return auto_splits(active, cus * occ, PA_PREFILL_MAX_AUTO_SPLITS);
 }
 
 static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
@@ -364,16 +371,20 @@ int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, cons
     return fail(PA_ERR_INVALID_ARGUMENT, "out may be NULL only with num_kv_splits >= 2 and lse NULL");
   if (num_seqs == 0 || total_q == 0) return ok();
   int splits = num_kv_splits;
-  if (splits != 1) {
-    const size_t need = pa_prefill_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_kv_splits);
-    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u))
-      return fail(PA_ERR_WORKSPACE, "prefill with %d splits needs %zu bytes of 8-byte aligned workspace (got %zu)",
-                  num_kv_splits, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
-  }
   if (splits == 0) {
     splits = pa_prefill_auto_splits(total_q, num_seqs, max_seqlen_q, num_q_heads, kv->num_kv_heads,
                                     kv->head_dim, q_dtype, kv->dtype);
     if (splits < 0) return splits;
+    // at most the parts the workspace holds (records of one part: total_q * Hq * (D + 2) floats)
+    const size_t per = pa_prefill_workspace_bytes(total_q, num_q_heads, kv->head_dim, 2) / 2;
+    const size_t fit = (workspace == nullptr || ((uintptr_t)workspace & 7u)) ? 0 : workspace_bytes / per;
+    if ((size_t)splits > fit) splits = fit >= 2 ? (int)fit : 1;
+  }
+  if (splits != 1) {
+    const size_t need = pa_prefill_workspace_bytes(total_q, num_q_heads, kv->head_dim, splits);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u))
+      return fail(PA_ERR_WORKSPACE, "prefill with %d splits needs %zu bytes of 8-byte aligned workspace (got %zu)",
+                  splits, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
   }
   return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_seqs,
                        max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, 0, false,

@@ -44,7 +44,7 @@ def test_decode_workspace_matches_the_pages_record_size():
 def test_prefill_workspace_sizes():
     assert ops.prefill_workspace_bytes(100, 8, 128, 1) == 0
     assert ops.prefill_workspace_bytes(100, 8, 128, 3) == 100 * 8 * 3 * 130 * 4
-    assert ops.prefill_workspace_bytes(100, 8, 128, 0) == 100 * 8 * 4 * 130 * 4
+    assert ops.prefill_workspace_bytes(100, 8, 128, 0) == 100 * 8 * 16 * 130 * 4
 
 
 @pytest.mark.parametrize("args,status", [
