@@ -508,3 +508,83 @@ def test_e4m3_verify_row_equals_serial_decode_bitwise():
     out_s, lse_s = gpu_decode_fixed(ser, part_keys=512, parts=6, max_q=1)
     assert torch.equal(bits(out_v[:5]), bits(out_s)) and torch.equal(lse_v[:5].view(torch.int32),
                                                                        lse_s.view(torch.int32))
+
+
+# ------------------------------------------------------------------ graphs and prefill batch invariance
+
+def test_calls_replay_under_a_hip_graph():
+    """The grid depends on host scalars only, so a prefill (split, with merge),
+    a decode, an absolute-part decode and a KV write can be captured in one HIP
+    graph.  The graph is replayed several times with eager work and
+    synchronisations in between; every replay must equal the eager results bit
+    for bit (the pages keep the static grid for CUDA graphs: InferMatrixLab/
+    vllm-rlt PR #128, "Purpose", Decode)."""
+    c = gen.make_case("graph", q_lens=[300, 1, 5], seq_lens=[1000, 700, 2000], num_q_heads=16, num_kv_heads=4,
+                      head_dim=128, page_size=32, q_kind="bf16", seed=91)
+    d = gen.to_device(c)
+    pre = gen.select_seqs(c, [0])
+    dec = gen.select_seqs(c, [1, 2])
+    dp, dd = gen.to_device(pre), gen.to_device(dec)
+    dp["k"], dp["v"], dd["k"], dd["v"] = d["k"], d["v"], d["k"], d["v"]
+    kn = torch.randn((5, 4, 128), device="cuda").to(torch.bfloat16)
+    vn = torch.randn((5, 4, 128), device="cuda").to(torch.bfloat16)
+    ws_p = torch.empty(ops.prefill_workspace_bytes(pre.total_q, 16, 128, 3) // 4, dtype=torch.float32, device="cuda")
+    ws_d = torch.empty(ops.decode_workspace_bytes(dec.total_q, 16, 128, 8) // 4, dtype=torch.float32, device="cuda")
+    ws_f = torch.empty_like(ws_d)
+    outs = [torch.empty_like(dp["q"]), torch.empty_like(dd["q"]), torch.empty_like(dd["q"])]
+    lses = [torch.empty(dp["q"].shape[:2], dtype=torch.float32, device="cuda") for _ in range(1)]
+    kv_copy = [d["k"].clone(), d["v"].clone()]
+    bt_w = torch.from_numpy(np.ascontiguousarray(c.block_tables[2:3])).cuda()
+    cu_w = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    sl_w = torch.tensor([int(c.seq_lens[2])], dtype=torch.int32, device="cuda")
+
+    def step(stream):
+        ops.paged_prefill(dp["q"], dp["k"], dp["v"], dp["cu"], dp["seq_lens"], dp["bt"], pre.max_seqlen_q, c.scale,
+                          num_kv_splits=3, out=outs[0], lse=lses[0], workspace=ws_p, stream=stream)
+        ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 5, c.scale, num_splits=8,
+                            out=outs[1], workspace=ws_d, stream=stream)
+        ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 5, c.scale, num_splits=8,
+                            part_keys=256, out=outs[2], workspace=ws_f, stream=stream)
+        ops.write_kv(kn, vn, kv_copy[0], kv_copy[1], cu_w, sl_w, bt_w, 5, stream=stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs] + [lses[0].clone(), kv_copy[0].clone(), kv_copy[1].clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        lses[0].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(outs) + [lses[0], kv_copy[0], kv_copy[1]]
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert torch.equal(bits(a), bits(b)), f"replay {rep}, output {i}"
+        _ = torch.ones(1 << 20, device="cuda").sum().item()  # eager work between replays
+    ref, rl = run_oracle(c)
+    compare("graph prefill", "bf16", outs[0].float().cpu().numpy(), ref[:300])
+    compare("graph decode", "bf16", outs[1].float().cpu().numpy(), ref[300:])
+
+
+def test_prefill_with_fixed_splits_is_batch_invariant_bitwise(varlen_bf16):
+    """A sequence's prefill output does not depend on the other sequences of the
+    call when num_kv_splits is fixed (the grid order only changes which work
+    group runs when)."""
+    c, d, _ = varlen_bf16
+    for splits in (1, 3):
+        out_b, lse_b = gpu_prefill(c, d, splits=splits)
+        cu = c.cu_seqlens_q
+        for b in (3, 1):
+            one, lo = gpu_prefill(gen.select_seqs(c, [b]), splits=splits)
+            assert np.array_equal(one.view(np.uint64), out_b[cu[b]:cu[b + 1]].view(np.uint64)), (splits, b)
+            assert np.array_equal(lo.view(np.uint64), lse_b[cu[b]:cu[b + 1]].view(np.uint64)), (splits, b)
+        sub = gen.select_seqs(c, [2, 0])
+        two, _ = gpu_prefill(sub, splits=splits)
+        assert np.array_equal(two[:cu[3] - cu[2]].view(np.uint64), out_b[cu[2]:cu[3]].view(np.uint64))
