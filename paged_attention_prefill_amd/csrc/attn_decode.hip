@@ -52,14 +52,10 @@ void attn_decode_kernel(const AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, r32 = lane & 31;
 
-  int w = xcd_remap(blockIdx.x);
-  if (w >= p.num_work) return;
-  const int qtile = w % p.qtiles;
-  w /= p.qtiles;
-  const int split = w % p.num_splits;
-  w /= p.num_splits;
-  const int kvh = w % p.num_kv_heads;
-  const int seq = w / p.num_kv_heads;
+  WorkItem wi;
+  if (!work_of_block(p, blockIdx.x, false, wi)) return;
+  const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const int seq = wi.seqpos;
 
   const int q0 = p.cu_seqlens_q[seq];
   const int qlen = p.cu_seqlens_q[seq + 1] - q0;

@@ -48,15 +48,11 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, r32 = lane & 31;
 
-  int w = xcd_remap(blockIdx.x);
-  if (w >= p.num_work) return;
+  WorkItem wi;
+  if (!work_of_block(p, blockIdx.x, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
-  const int qtile = p.qtiles - 1 - w % p.qtiles;
-  w /= p.qtiles;
-  const int split = w % p.num_splits;
-  w /= p.num_splits;
-  const int kvh = w % p.num_kv_heads;
-  const int seq = seq_by_rank(p, w / p.num_kv_heads, (int*)smem, tid, 64 * WAVES);
+  const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 64 * WAVES);
 
   const int q0 = p.cu_seqlens_q[seq];
   const int qlen = p.cu_seqlens_q[seq + 1] - q0;

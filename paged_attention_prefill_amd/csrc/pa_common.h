@@ -33,8 +33,10 @@ struct AttnParams {
   int num_splits;
   int part_keys;           // 0: parts cut from each row's own length; > 0: absolute parts of this many keys
   int write_partial;       // 1: records to `partial`; 0: final out/lse
-  int qtiles;              // q tiles per (sequence, kv head) in the grid
-  int num_work;            // work items (the grid is padded beyond it)
+  int qtiles;              // q tiles per (sequence, kv head, key part) in the grid
+  int chunks;              // runs per group of q tiles (see work_of_block)
+  int run_len;             // q tiles per run
+  int num_runs;            // groups * chunks
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;
 };
@@ -53,20 +55,37 @@ struct KvWriteParams {
   float k_scale, v_scale;  // fp8 cache: byte = E5M2(x / scale)
 };
 
-// Block index -> work index.  Work groups are handed to the 8 XCDs round
-// robin; runs of kXcdGroup consecutive work items (neighbouring query tiles of
-// one sequence, kv head and key part, which read the same K/V) are kept on one
-// XCD so that they share its L2.  Row r of 8 runs goes to the 8 XCDs rotated
-// by r, so that a pattern of busy and empty runs that repeats every 2, 4 or 8
-// runs (a static grid sized for the longest sequence leaves such holes behind
-// the shorter ones) is spread over all XCDs instead of piling on some.  The
-// grid is padded to a multiple of 8 * kXcdGroup; the mapping is a bijection on
-// the padded range, so it only affects locality and balance.
-constexpr int kXcdGroup = 16;
-__device__ __forceinline__ int xcd_remap(int bid) {
+// Block index -> work item.  A group is the query tiles of one (sequence
+// position, kv head, key part): they all read the same K/V.  Its qtiles tiles
+// are cut into `chunks` runs of run_len consecutive tiles, and every run stays
+// on one XCD, so each XCD's L2 fetches a group's K/V once per run it holds
+// (the host makes whole groups one run where that keeps the 8 XCDs evenly
+// loaded).  Work groups go to the 8 XCDs round robin (block b to XCD b % 8);
+// row r of 8 runs is dealt to the XCDs rotated by r, so a pattern of busy and
+// empty runs that repeats every 2, 4 or 8 runs (a static grid sized for the
+// longest sequence leaves such holes behind the shorter ones) is spread over
+// all XCDs.  Within a run the tiles come in order; `reverse` hands out a
+// group's last tiles (the ones that see the most keys) first.  Returns false
+// for a padding block.  The mapping is a bijection on the padded grid, so it
+// only affects locality and balance.
+struct WorkItem {
+  int qtile, split, kvh, seqpos;  // seqpos: position in the grid's sequence order
+};
+__device__ __forceinline__ bool work_of_block(const AttnParams& p, int bid, bool reverse, WorkItem& wi) {
+  const int R = p.run_len;
   const int xcd = bid & 7, k = bid >> 3;
-  const int row = k / kXcdGroup;
-  return (row * 8 + ((xcd - row) & 7)) * kXcdGroup + (k % kXcdGroup);
+  const int row = k / R, pos = k - row * R;
+  const int run = row * 8 + ((xcd - row) & 7);
+  if (run >= p.num_runs) return false;
+  int grp = run / p.chunks;
+  const int qi = (run - grp * p.chunks) * R + pos;
+  if (qi >= p.qtiles) return false;
+  wi.qtile = reverse ? p.qtiles - 1 - qi : qi;
+  wi.split = grp % p.num_splits;
+  grp /= p.num_splits;
+  wi.kvh = grp % p.num_kv_heads;
+  wi.seqpos = grp / p.num_kv_heads;
+  return true;
 }
 
 // Sequence taken at position r of the grid's sequence order: longest first

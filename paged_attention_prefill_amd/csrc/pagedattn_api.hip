@@ -170,6 +170,9 @@ int auto_splits(int64_t active_groups, int slots, int max_s) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// gcd(n, 8) for n >= 1
+int64_t gcd8(int64_t n) { return (n & 7) == 0 ? 8 : (n & 3) == 0 ? 4 : (n & 1) == 0 ? 2 : 1; }
+
 // Which pass-1 kernel serves a call: fp32 -> exact-product VALU kernel;
 // fp16/bf16 with same-dtype KV -> MFMA kernels with the LDS DMA pipeline;
 // fp16 q with fp8_e5m2 KV -> the DMA kernels (8-bit tiles widened at the
@@ -290,11 +293,19 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
   const int rows = rows_for(kind, dpad_of(kv->head_dim), is_decode);
   const int qtiles = (int)ceil_div((int64_t)max_q * g, rows);
-  const int64_t nwork = (int64_t)qtiles * num_seqs * kv->num_kv_heads * splits;
-  const int64_t pad = 8 * pa::kXcdGroup;
-  const int64_t nblocks = (nwork + pad - 1) / pad * pad;
-  if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nwork);
-  if (nwork == 0 || total_q == 0) return ok();
+  // Groups (sequence, kv head, part) of qtiles query tiles each, cut into runs
+  // that stay on one XCD: whole groups when the group count spreads evenly over
+  // the 8 XCDs, otherwise the fewest cuts that make the run count a multiple of
+  // 8, and runs of at most 64 tiles (two waves of one XCD's compute units).
+  const int64_t groups = (int64_t)num_seqs * kv->num_kv_heads * splits;
+  int64_t chunks = 8 / gcd8(groups);
+  if (chunks > qtiles) chunks = qtiles;
+  while (ceil_div(qtiles, chunks) > 64) chunks *= 2;
+  const int64_t run_len = ceil_div(qtiles, chunks);
+  const int64_t runs = groups * chunks;
+  const int64_t nblocks = ceil_div(runs, 8) * 8 * run_len;
+  if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nblocks);
+  if (groups == 0 || total_q == 0) return ok();
   const bool partial = is_decode || splits > 1;
 
   pa::AttnParams p;
@@ -321,7 +332,9 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.part_keys = part_keys;
   p.write_partial = partial ? 1 : 0;
   p.qtiles = qtiles;
-  p.num_work = (int)nwork;
+  p.chunks = (int)chunks;
+  p.run_len = (int)run_len;
+  p.num_runs = (int)runs;
   p.scale_log2 = scale * (is_fp8(kv->dtype) ? kv->k_scale : 1.0f) * 1.4426950408889634f;
   p.v_scale = is_fp8(kv->dtype) ? kv->v_scale : 1.0f;
 
