@@ -41,15 +41,18 @@ def dequantize_pool(pool, kind, scale=1.0):
 
     ``kind`` is 'float' for any IEEE float storage (fp32, fp16, or bf16 already
     widened by the caller), 'e5m2' or 'e4m3' for a uint8 array of fp8 bytes, whose
-    values are decode(byte) * scale (per-tensor scale; 1CatAI/1Cat-vLLM PR #616,
+    values are decode(byte) * scale; ``scale`` is one number or one per kv head (per-tensor scale; 1CatAI/1Cat-vLLM PR #616,
     fp8_e5m2 KV paragraph of "Test Result").
     """
     if kind == "float":
         return np.asarray(pool, dtype=np.float64)
+    sc = np.asarray(scale, dtype=np.float64)
+    if sc.ndim == 1:  # one factor per kv head (axis 2 of [pages, page_size, Hkv, D])
+        sc = sc[None, None, :, None]
     if kind == "e5m2":
-        return e5m2_to_float64(np.asarray(pool)) * float(scale)
+        return e5m2_to_float64(np.asarray(pool)) * sc
     if kind == "e4m3":
-        return e4m3_to_float64(np.asarray(pool)) * float(scale)
+        return e4m3_to_float64(np.asarray(pool)) * sc
     raise ValueError(f"unknown pool kind {kind!r}")
 
 

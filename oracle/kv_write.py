@@ -74,15 +74,21 @@ def quantize_e5m2(x, scale):
 
 
 def write_kv(k_pool, v_pool, k_new, v_new, cu_seqlens_q, seq_lens, block_tables, fp8=False,
-             k_scale=1.0, v_scale=1.0):
+             k_scale=1.0, v_scale=1.0, k_head_scales=None, v_head_scales=None):
     """Copies of the pools [num_pages, P, Hkv, D] with the new tokens written.
 
     k_new, v_new [total_q, Hkv, D] (float values); fp8 pools are uint8 byte
     arrays, fp8 = True or "e5m2" for E5M2 bytes, "e4m3" for E4M3 bytes.
     """
     fmt = "e5m2" if fp8 is True else fp8
+
+    def head_scales(scale, per_head):
+        # the per-tensor factor times the head's own, the product rounded to float32
+        ph = np.ones(H, dtype=np.float32) if per_head is None else np.asarray(per_head, dtype=np.float32)
+        return np.float32(scale) * ph
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
+    H = k_out.shape[2]
     P = k_out.shape[1]
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     for b in range(len(seq_lens)):
@@ -95,8 +101,10 @@ def write_kv(k_pool, v_pool, k_new, v_new, cu_seqlens_q, seq_lens, block_tables,
             page = int(block_tables[b][pos // P])
             row = int(cu[b]) + t
             if fp8:
-                k_out[page, pos % P] = quantize_fp8(k_new[row], k_scale, fmt)
-                v_out[page, pos % P] = quantize_fp8(v_new[row], v_scale, fmt)
+                ks, vs = head_scales(k_scale, k_head_scales), head_scales(v_scale, v_head_scales)
+                for h in range(H):
+                    k_out[page, pos % P, h] = quantize_fp8(k_new[row, h], ks[h], fmt)
+                    v_out[page, pos % P, h] = quantize_fp8(v_new[row, h], vs[h], fmt)
             else:
                 k_out[page, pos % P] = k_new[row]
                 v_out[page, pos % P] = v_new[row]

@@ -116,3 +116,24 @@ def test_e4m3_encoder_specials_and_round_trip():
     assert list(oracle.e4m3_encode(np.array([np.nan, -np.nan]))) == [0x7F, 0xFF]
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
     assert (oracle.e4m3_encode(oracle.e4m3_to_float64(codes)) == codes).all()
+
+
+
+def test_per_head_scales_in_dequantisation_and_write():
+    """A per-head factor multiplies head h only (axis 2 of the pool), and the
+    write divides by the float32 product of the two factors."""
+    rng = np.random.default_rng(3)
+    pool = rng.integers(0, 0x7B, size=(3, 16, 4, 8), dtype=np.uint8)
+    hs = np.array([0.5, 2.0, 1.0, 3.0], dtype=np.float32)
+    got = oracle.dequantize_pool(pool, "e5m2", 0.25 * hs.astype(np.float64))
+    for h in range(4):
+        np.testing.assert_array_equal(got[:, :, h], oracle.e5m2_to_float64(pool[:, :, h]) * 0.25 * float(hs[h]))
+    case = gen.make_case("hs", q_lens=[3], seq_lens=[20], num_q_heads=4, num_kv_heads=4, head_dim=16,
+                         page_size=16, q_kind="f16", kv_kind="e4m3", seed=5, poison=False)
+    kn = rng.standard_normal((3, 4, 16))
+    ko, _ = oracle.write_kv(case.k_pool.numpy(), case.v_pool.numpy(), kn, kn, case.cu_seqlens_q, case.seq_lens,
+                            case.block_tables, fp8="e4m3", k_scale=0.3, k_head_scales=hs)
+    for h in range(4):
+        want = oracle.quantize_fp8(kn[:, h], np.float32(0.3) * hs[h], "e4m3")
+        K = oracle.gather_dense_kv(ko, case.block_tables[0], 20, h)
+        np.testing.assert_array_equal(K[17:20], want)
