@@ -105,6 +105,11 @@ typedef struct pa_kv_cache {
   int32_t dtype;         /* pa_dtype */
   float k_scale;         /* fp8 KV only (must be 1 otherwise): value = decode(byte) * scale */
   float v_scale;
+  /* fp8 KV only, nullable: device float[num_kv_heads] per-head factors, value =
+   * decode(byte) * k_scale * k_head_scales[h] (V likewise).  Trusted like the
+   * other device data: positive and finite. */
+  const float *k_head_scales;
+  const float *v_head_scales;
 } pa_kv_cache;
 
 /*
@@ -222,7 +227,8 @@ int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_token
  *   The cache (kv->k_pages, kv->v_pages: written through, despite the const of
  *   the descriptor) has src_dtype, which is copied exactly, or FP8_E5M2 (with
  *   F16 src) or FP8_E4M3 (with F16 src), byte = the fp8 code of (x / scale)
- *   computed in fp32 (k_scale for K, v_scale for V, both positive), rounded to
+ *   computed in fp32, scale = k_scale (v_scale for V, both positive) times the
+ *   head's k_head_scales[h] when given (the product rounded to fp32), rounded to
  *   nearest with ties to even and saturated to the largest finite magnitude
  *   (57344 for E5M2, 448 for E4M3); NaN stays NaN (0x7F with its sign).  Nothing else in
  *   the cache is touched.  Device metadata is trusted (pa_validate_metadata

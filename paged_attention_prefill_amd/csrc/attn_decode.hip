@@ -55,6 +55,7 @@ void attn_decode_kernel(const AttnParams p) {
   WorkItem wi;
   if (!work_of_block(p, blockIdx.x, false, wi)) return;
   const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = wi.seqpos;
 
   const int q0 = p.cu_seqlens_q[seq];
@@ -216,7 +217,7 @@ void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = key < lim ? s[r] * p.scale_log2 : kNegInf;
+      const float v = key < lim ? s[r] * score_scale : kNegInf;
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -297,7 +298,7 @@ void attn_decode_kernel(const AttnParams p) {
   }
   if (!valid) return;
   const bool empty = (mall == kNegInf) || !(lall > 0.0f);
-  const float inv = empty ? 0.0f : p.v_scale / lall;
+  const float inv = empty ? 0.0f : out_scale / lall;
   const float lse_nat = empty ? kNegInf : (mall + __log2f(lall)) * 0.69314718055994530942f;
   const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
   float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   if (!work_of_block(p, blockIdx.x, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
   const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = wi.seqpos;
 
   const int q0 = p.cu_seqlens_q[seq];
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = key < lim ? s[r] * p.scale_log2 : kNegInf;
+      const float v = key < lim ? s[r] * score_scale : kNegInf;
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!valid) return;
   const bool empty = (m == kNegInf) || !(ltot > 0.0f);
-  const float inv = empty ? 0.0f : p.v_scale / ltot;
+  const float inv = empty ? 0.0f : out_scale / ltot;
   const float lse_nat = empty ? kNegInf : (m + __log2f(ltot)) * 0.69314718055994530942f;
   const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
   if (p.write_partial) {

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   if (!work_of_block(p, blockIdx.x, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
   const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 64 * WAVES);
 
   const int q0 = p.cu_seqlens_q[seq];
@@ -144,14 +145,14 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float v = key < lim[rb] ? s[rb][r] * p.scale_log2 : kNegInf;
+          const float v = key < lim[rb] ? s[rb][r] * score_scale : kNegInf;
           s[rb][r] = v;
           tmax = fmaxf(tmax, v);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float v = s[rb][r] * p.scale_log2;
+          const float v = s[rb][r] * score_scale;
           s[rb][r] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
     if (!valid[rb]) continue;
     const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
-    const float inv = empty ? 0.0f : p.v_scale / ltot;
+    const float inv = empty ? 0.0f : out_scale / ltot;
     const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
     const int64_t rowidx = (int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb];
     if (p.write_partial) {

@@ -116,6 +116,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   if (!work_of_block(p, blockIdx.x, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
   const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 256);
 
   const int q0 = p.cu_seqlens_q[seq];
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const uint32_t vlane = KV8 ? TILE_BYTES + (8 * (kr >> 2) + 4 * (tg >> 1) + (kr & 3)) * ROWB + 16 * (tg & 1) +
                                    8 * (tk & 1) + 32 * kr
                               : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
-  const float c = p.scale_log2;
+  const float c = score_scale;
 
   f32x16_t s[RB];
   uint4 pcur[RB][2], pnew[RB][2];
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     const int tok = prow / g;
     const int hq = kvh * g + (prow - tok * g);
     const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
-    const float inv = empty ? 0.0f : p.v_scale / ltot;
+    const float inv = empty ? 0.0f : out_scale / ltot;
     const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
     const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
     if (p.write_partial) {

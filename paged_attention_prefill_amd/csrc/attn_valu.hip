@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
   if (!work_of_block(p, blockIdx.x, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
   const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = wi.seqpos;
 
   const int q0 = p.cu_seqlens_q[seq];
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 #pragma unroll 8
       for (int d = 0; d < HALF; ++d) dot = fmaf(qr[d], kr[d], dot);
       dot += __shfl_xor(dot, 32);
-      const float s = (j0 + key < lim[i]) ? dot * p.scale_log2 : kNegInfV;
+      const float s = (j0 + key < lim[i]) ? dot * score_scale : kNegInfV;
       const float tmax = wave_max32(s);
       const float mnew = fmaxf(m[i], tmax);
       const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m[i] - mnew);
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
   for (int i = 0; i < 4; ++i) {
     if (!rvalid[i]) continue;
     const bool empty = m[i] == kNegInfV || !(l[i] > 0.0f);
-    const float inv = empty ? 0.0f : p.v_scale / l[i];
+    const float inv = empty ? 0.0f : out_scale / l[i];
     const float lse_nat = empty ? kNegInfV : (m[i] + log2f(l[i])) * 0.69314718055994530942f;
     const int64_t rowidx = (int64_t)(q0 + rowtok[i]) * p.num_q_heads + rowhq[i];
     if (p.write_partial) {

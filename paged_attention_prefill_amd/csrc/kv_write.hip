@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_
                                                        int64_t stride_page, int64_t stride_token,
                                                        int64_t stride_head, int page_size, int num_kv_heads,
                                                        int head_dim, int blocks_per_seq, float k_scale,
-                                                       float v_scale) {
+                                                       float v_scale, const float* __restrict__ k_head_scale,
+                                                       const float* __restrict__ v_head_scale) {
   const int seq = blockIdx.x / blocks_per_seq;
   const int chunks = head_dim >> 3;  // 8 elements each
   const int64_t item = (int64_t)(blockIdx.x - seq * blocks_per_seq) * 256 + threadIdx.x;
@@ -98,7 +99,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const ST* __restrict__ k_
     const ST* s = (kvi == 0 ? k_new : v_new) + src;
     char* base = kvi == 0 ? k_pages : v_pages;
     if constexpr (F8 != 0) {
-      const float sc = kvi == 0 ? k_scale : v_scale;
+      // the head's scale: the per-tensor factor times the per-head one (rounded to fp32)
+      const float* hs = kvi == 0 ? k_head_scale : v_head_scale;
+      const float sc = (kvi == 0 ? k_scale : v_scale) * (hs ? hs[h] : 1.0f);
       float x[8];
       if constexpr (sizeof(ST) == 4) {
         const float4 a = ((const float4*)s)[0], b = ((const float4*)s)[1];
@@ -136,7 +139,7 @@ hipError_t launch_kv_f(const KvWriteParams& w, hipStream_t stream) {
   hipLaunchKernelGGL((kv_write_kernel<ST, F8>), grid, dim3(256), 0, stream, (const ST*)w.k_new, (const ST*)w.v_new,
                      w.cu_seqlens_q, w.seq_lens, w.block_tables, w.max_pages, (char*)w.k_pages, (char*)w.v_pages,
                      w.stride_page, w.stride_token, w.stride_head, w.page_size, w.num_kv_heads, w.head_dim, bps,
-                     w.k_scale, w.v_scale);
+                     w.k_scale, w.v_scale, w.k_head_scale, w.v_head_scale);
   return hipGetLastError();
 }
 

@@ -39,7 +39,18 @@ struct AttnParams {
   int num_runs;            // groups * chunks
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;
+  const float* k_head_scale;  // [Hkv] or null: fp8 K of head h is decode(byte) * k_scale * k_head_scale[h]
+  const float* v_head_scale;  // [Hkv] or null
 };
+
+// The score factor (scale * k_scale * log2 e, times the head's K scale) and the
+// output factor (v_scale times the head's V scale) of kv head h.
+__device__ __forceinline__ float head_score_scale(const AttnParams& p, int h) {
+  return p.k_head_scale ? p.scale_log2 * p.k_head_scale[h] : p.scale_log2;
+}
+__device__ __forceinline__ float head_v_scale(const AttnParams& p, int h) {
+  return p.v_head_scale ? p.v_scale * p.v_head_scale[h] : p.v_scale;
+}
 
 // Arguments of the KV write (new tokens' K and V into their cache pages).
 struct KvWriteParams {
@@ -52,7 +63,9 @@ struct KvWriteParams {
   void* v_pages;
   int64_t stride_page, stride_token, stride_head;  // elements of the cache dtype
   int num_seqs, max_pages, max_q, num_kv_heads, head_dim, page_size;
-  float k_scale, v_scale;  // fp8 cache: byte = E5M2(x / scale)
+  float k_scale, v_scale;  // fp8 cache: byte = fp8(x / scale), scale = k_scale * k_head_scale[h]
+  const float* k_head_scale;  // [Hkv] or null
+  const float* v_head_scale;
 };
 
 // Block index -> work item.  A group is the query tiles of one (sequence

@@ -125,6 +125,10 @@ int check_kv(const pa_kv_cache* kv, int q_dtype, int hq) {
   if (!(kv->k_scale > 0.0f)) return fail(PA_ERR_INVALID_ARGUMENT, "k_scale must be positive");
   if (!is_fp8(kv->dtype) && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
     return fail(PA_ERR_UNSUPPORTED, "k_scale / v_scale apply to fp8 KV only (must be 1)");
+  if (!is_fp8(kv->dtype) && (kv->k_head_scales != nullptr || kv->v_head_scales != nullptr))
+    return fail(PA_ERR_UNSUPPORTED, "per-head scales apply to fp8 KV only");
+  if (((uintptr_t)kv->k_head_scales & 3u) || ((uintptr_t)kv->v_head_scales & 3u))
+    return fail(PA_ERR_INVALID_ARGUMENT, "per-head scales must be 4-byte aligned");
   return PA_OK;
 }
 
@@ -337,6 +341,8 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.num_runs = (int)runs;
   p.scale_log2 = scale * (is_fp8(kv->dtype) ? kv->k_scale : 1.0f) * 1.4426950408889634f;
   p.v_scale = is_fp8(kv->dtype) ? kv->v_scale : 1.0f;
+  p.k_head_scale = kv->k_head_scales;
+  p.v_head_scale = kv->v_head_scales;
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
@@ -487,6 +493,8 @@ int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const i
   w.page_size = kv->page_size;
   w.k_scale = kv->k_scale;
   w.v_scale = kv->v_scale;
+  w.k_head_scale = kv->k_head_scales;
+  w.v_head_scale = kv->v_head_scales;
   hipError_t e = pa::launch_kv_write(w, kind_of(src_dtype), is_fp8(kv->dtype) ? kind_of(kv->dtype) : 0,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "KV write launch failed: %s", hipGetErrorString(e));

@@ -58,6 +58,8 @@ class PagedCase:
     v_scale: float = 1.0
     num_splits: int = 16
     layout: str = "NHD"
+    k_head_scales: Optional[np.ndarray] = None  # fp8 only: float32 [Hkv] per-head factors
+    v_head_scales: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -273,7 +275,12 @@ def to_device(case, device="cuda"):
         k, v = dev(k.contiguous()), dev(v.contiguous())
     if case.kv_kind == "e4m3":  # the binding reads the fp8 format from the dtype (uint8 = E5M2)
         k, v = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
-    return dict(q=dev(case.q.contiguous()), k=k, v=v,
+    extra = {}
+    for name in ("k_head_scales", "v_head_scales"):
+        val = getattr(case, name)
+        if val is not None:
+            extra[name] = torch.from_numpy(np.asarray(val, dtype=np.float32)).to(device)
+    return dict(q=dev(case.q.contiguous()), k=k, v=v, **extra,
                 cu=torch.from_numpy(case.cu_seqlens_q.astype(np.int32)).to(device),
                 seq_lens=torch.from_numpy(case.seq_lens.astype(np.int32)).to(device),
                 bt=torch.from_numpy(np.ascontiguousarray(case.block_tables, dtype=np.int32)).to(device))

@@ -40,7 +40,8 @@ class KvCache(ctypes.Structure):
                 ("stride_head", ctypes.c_int64), ("num_pages", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("k_head_scales", ctypes.c_void_p), ("v_head_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -119,8 +120,9 @@ def _dtype(t):
         raise PagedAttentionError(PA_ERR_UNSUPPORTED, f"unsupported dtype {t.dtype}") from None
 
 
-def kv_cache(k_pages, v_pages, k_scale=1.0, v_scale=1.0):
-    """Describe logical [num_pages, page_size, Hkv, D] K/V page tensors (D contiguous)."""
+def kv_cache(k_pages, v_pages, k_scale=1.0, v_scale=1.0, k_head_scales=None, v_head_scales=None):
+    """Describe logical [num_pages, page_size, Hkv, D] K/V page tensors (D contiguous);
+    fp8 pages may carry per-head scale tensors (float32 [Hkv] on the device)."""
     if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "K and V pages must share shape and strides")
     if k_pages.dtype != v_pages.dtype:
@@ -129,8 +131,13 @@ def kv_cache(k_pages, v_pages, k_scale=1.0, v_scale=1.0):
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "pages must be 4-D with a contiguous head dim")
     n, P, H, D = k_pages.shape
     s = k_pages.stride()
+    for t, name in ((k_head_scales, "k_head_scales"), (v_head_scales, "v_head_scales")):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != H or not t.is_contiguous()):
+            raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous float32 [Hkv] tensor")
     return KvCache(k_pages.data_ptr(), v_pages.data_ptr(), s[0], s[1], s[2], n, P, H, D,
-                   _dtype(k_pages), float(k_scale), float(v_scale))
+                   _dtype(k_pages), float(k_scale), float(v_scale),
+                   None if k_head_scales is None else k_head_scales.data_ptr(),
+                   None if v_head_scales is None else v_head_scales.data_ptr())
 
 
 def _i32(t, name):
@@ -162,7 +169,8 @@ def _partials_view(workspace, total_q, Hq, D, splits):
 
 def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_seqlen_q, scale,
                   *, k_scale=1.0, v_scale=1.0, num_kv_splits=1, out=None, lse=None,
-                  return_lse=False, workspace=None, stream=None, merge=True):
+                  return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
+                  v_head_scales=None):
     """pa_paged_prefill on torch tensors; returns out (and lse).
 
     merge=False (num_kv_splits >= 2): runs the first pass only and returns the
@@ -170,7 +178,7 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
     total_q, Hq, D = q.shape
     if not q.is_contiguous():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
-    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale, k_head_scales, v_head_scales)
     if merge:
         out = torch.empty_like(q) if out is None else out
         if return_lse and lse is None:
@@ -193,7 +201,8 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
 
 def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
                     *, num_splits=16, part_keys=0, k_scale=1.0, v_scale=1.0, out=None, lse=None,
-                    return_lse=False, workspace=None, stream=None, merge=True):
+                    return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
+                    v_head_scales=None):
     """pa_split_kv_decode on torch tensors; returns out (and lse).
 
     part_keys > 0: pa_split_kv_decode_fixed, num_splits absolute parts of
@@ -203,7 +212,7 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     total_q, Hq, D = q.shape
     if not q.is_contiguous():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
-    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale, k_head_scales, v_head_scales)
     if merge:
         out = torch.empty_like(q) if out is None else out
         if return_lse and lse is None:
@@ -228,7 +237,7 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
 
 
 def write_kv(k_new, v_new, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q, *, k_scale=1.0,
-             v_scale=1.0, stream=None):
+             v_scale=1.0, stream=None, k_head_scales=None, v_head_scales=None):
     """pa_write_kv: k_new / v_new [total_q, Hkv, D] into the pages at each sequence's
     last q_len positions (uint8 / float8_e5m2 pages: E5M2 of x / scale;
     float8_e4m3fn pages: E4M3 of x / scale)."""
@@ -237,7 +246,7 @@ def write_kv(k_new, v_new, k_pages, v_pages, cu_seqlens_q, seq_lens, block_table
             raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous [total_q, Hkv, D] tensor")
     if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "k_new and v_new must share shape and dtype")
-    kv = kv_cache(k_pages, v_pages, k_scale, v_scale)
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale, k_head_scales, v_head_scales)
     B = int(seq_lens.numel())
     _check(lib().pa_write_kv(_ptr(k_new), _ptr(v_new), _dtype(k_new), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
                              _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B,

@@ -48,7 +48,8 @@ def run_write(case, kn, vn):
     say(f"  write {case.name}: seqs={case.num_seqs} total_q={case.total_q} Hkv={case.num_kv_heads} "
         f"D={case.head_dim} P={case.page_size} kv={case.kv_kind} layout={case.layout}")
     ops.write_kv(kn.cuda(), vn.cuda(), d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], max(1, case.max_seqlen_q),
-                 k_scale=case.k_scale, v_scale=case.v_scale)
+                 k_scale=case.k_scale, v_scale=case.v_scale, k_head_scales=d.get("k_head_scales"),
+                 v_head_scales=d.get("v_head_scales"))
     torch.cuda.synchronize()
     return d
 
@@ -99,3 +100,17 @@ def test_attention_over_the_written_cache():
     err = float(np.abs(out.float().cpu().numpy() - ref).max())
     say(f"  prefill over the written cache: max|err| {err:.3e}")
     assert err < 2e-2
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+def test_kv_write_fp8_per_head_scales(fmt):
+    case = gen.make_case(f"kvw_heads_{fmt}", q_kind="f16", kv_kind=fmt, seed=67, k_scale=0.5, v_scale=1.25,
+                         **dict(CASE, head_dim=256, page_size=64))
+    case.k_head_scales = np.array([0.1, 3.0], dtype=np.float32)
+    case.v_head_scales = np.array([7.0, 0.3], dtype=np.float32)
+    kn, vn = new_rows(case, "f16", 68, specials=True)
+    d = run_write(case, kn, vn)
+    ko, vo = oracle.write_kv(raw(case.k_pool), raw(case.v_pool), kn.float().numpy(), vn.float().numpy(),
+                             case.cu_seqlens_q, case.seq_lens, case.block_tables, fp8=fmt, k_scale=0.5, v_scale=1.25,
+                             k_head_scales=case.k_head_scales, v_head_scales=case.v_head_scales)
+    assert np.array_equal(raw(d["k"]), ko) and np.array_equal(raw(d["v"]), vo)

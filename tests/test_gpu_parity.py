@@ -40,8 +40,10 @@ def _gpu():
 
 def oracle_pools(case):
     kind = case.kv_kind if case.kv_kind in ("e5m2", "e4m3") else "float"
-    k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, case.k_scale)
-    v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
+    ks = case.k_scale if case.k_head_scales is None else case.k_scale * np.asarray(case.k_head_scales, np.float64)
+    vs = case.v_scale if case.v_head_scales is None else case.v_scale * np.asarray(case.v_head_scales, np.float64)
+    k = oracle.dequantize_pool(gen.to_numpy64(case.k_pool, case.kv_kind), kind, ks)
+    v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, vs)
     return k, v
 
 
@@ -57,7 +59,8 @@ def gpu_prefill(case, d=None, splits=1):
         f"D={case.head_dim} P={case.page_size} splits={splits}")
     out, lse = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], case.max_seqlen_q,
                                  case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
-                                 num_kv_splits=splits, return_lse=True)
+                                 num_kv_splits=splits, return_lse=True, k_head_scales=d.get("k_head_scales"),
+                                 v_head_scales=d.get("v_head_scales"))
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -70,7 +73,8 @@ def gpu_decode(case, d=None, splits=None, max_q=None):
         f"Hkv={case.num_kv_heads} D={case.head_dim} P={case.page_size} S={splits} max_q={max_q}")
     out, lse = ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], max_q, case.scale,
                                    num_splits=splits, k_scale=case.k_scale, v_scale=case.v_scale,
-                                   return_lse=True)
+                                   return_lse=True, k_head_scales=d.get("k_head_scales"),
+                                   v_head_scales=d.get("v_head_scales"))
     torch.cuda.synchronize()
     return out, lse
 
@@ -588,3 +592,23 @@ def test_prefill_with_fixed_splits_is_batch_invariant_bitwise(varlen_bf16):
         sub = gen.select_seqs(c, [2, 0])
         two, _ = gpu_prefill(sub, splits=splits)
         assert np.array_equal(two[:cu[3] - cu[2]].view(np.uint64), out_b[cu[2]:cu[3]].view(np.uint64))
+
+
+@pytest.mark.parametrize("fmt,D,P", [("e5m2", 256, 64), ("e4m3", 256, 816), ("e4m3", 128, 32), ("e5m2", 64, 16)])
+def test_fp8_per_head_scales(fmt, D, P):
+    """fp8 KV with a factor per kv head on top of the per-tensor one, prefill
+    (1 and 2 parts) and decode, against the oracle fed decode(byte) * k_scale *
+    k_head_scales[h]."""
+    c = gen.make_case(f"headscale_{fmt}_D{D}", q_lens=[90, 1, 4], seq_lens=[700, 500, 1500], num_q_heads=12,
+                      num_kv_heads=4, head_dim=D, page_size=P, q_kind="f16", kv_kind=fmt, seed=7 * D + P,
+                      k_scale=0.5, v_scale=2.0)
+    c.k_head_scales = np.array([1.0, 0.25, 3.0, 0.7], dtype=np.float32)
+    c.v_head_scales = np.array([0.5, 1.5, 1.0, 4.0], dtype=np.float32)
+    ref, rl = run_oracle(c)
+    d = gen.to_device(c)
+    for splits in (1, 2):
+        out, lse = gpu_prefill(c, d, splits=splits)
+        compare(f"{fmt} per-head prefill D={D} S={splits}", fmt, out, ref, lse, rl)
+    dec = gen.select_seqs(c, [1, 2])
+    out, lse = gpu_decode(dec, splits=8, max_q=4)
+    compare(f"{fmt} per-head decode D={D}", fmt, out.float().cpu().numpy(), ref[90:], lse.cpu().numpy(), rl[90:])
