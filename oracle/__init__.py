@@ -38,6 +38,8 @@ from .attention import (  # noqa: F401
     dequantize_pool,
     gather_dense_kv,
     visible_key_count,
+    window_start,
+    add_sink,
     attention_rows,
     paged_attention,
     split_ranges,

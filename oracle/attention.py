@@ -74,15 +74,34 @@ def visible_key_count(seq_len, q_len, i):
     return seq_len - q_len + i + 1
 
 
-def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128):
+def window_start(seq_len, q_len, i, window_left):
+    """First key visible to query token i under a left window: the token sits
+    at key L - Q + i and sees keys j >= L - Q + i - window_left (window_left < 0:
+    no window, start 0)."""
+    i = np.asarray(i, dtype=np.int64)
+    if window_left is None or window_left < 0:
+        return np.zeros_like(i)
+    return np.maximum(0, seq_len - q_len + i - int(window_left))
+
+
+def add_sink(o, lse, sink):
+    """The softmax with one more logit `sink` in its denominator and no value:
+    o * sum_j e^s_j / (sum_j e^s_j + e^sink), lse = log(sum_j e^s_j + e^sink)."""
+    new = np.logaddexp(lse, sink)
+    f = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)
+    return o * f[..., None], new
+
+
+def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128, starts=None):
     """Softmax attention of query rows over a key range.
 
-    Row r attends to keys j with key_lo <= j < min(counts[r], key_hi, len(K)).
-    Returns (o [n, D], lse [n]); a row with no key in range gets o = 0 and
-    lse = -inf.
+    Row r attends to keys j with max(key_lo, starts[r]) <= j < min(counts[r],
+    key_hi, len(K)).  Returns (o [n, D], lse [n]); a row with no key in range
+    gets o = 0 and lse = -inf.
     """
     qrows = np.asarray(qrows, dtype=np.float64)
     counts = np.asarray(counts, dtype=np.int64)
+    starts = np.zeros_like(counts) if starts is None else np.asarray(starts, dtype=np.int64)
     n, D = qrows.shape
     L = K.shape[0]
     hi = L if key_hi is None else min(int(key_hi), L)
@@ -98,7 +117,7 @@ def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128)
         Vb = V[key_lo:emax]
         s = scale * (qb @ Kb.T)
         j = np.arange(key_lo, emax)
-        vis = j[None, :] < end[:, None]
+        vis = (j[None, :] < end[:, None]) & (j[None, :] >= starts[r0:r0 + block][:, None])
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
         has = np.isfinite(m)
@@ -116,13 +135,16 @@ def _token_to_seq(cu):
     return np.searchsorted(cu, np.arange(total), side="right") - 1
 
 
-def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, rows=None):
+def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, rows=None,
+                    window_left=-1, sinks=None):
     """Varlen paged attention in float64.
 
     q            [total_q, Hq, D]
     k_pool/v_pool [num_pages, page_size, Hkv, D] (float64 values; see dequantize_pool)
     cu_seqlens_q [B + 1], seq_lens [B], block_tables [B, max_pages]
     rows         optional [n, 2] array of (token, q head) pairs to compute.
+    window_left  >= 0: token i also needs j >= L - Q + i - window_left (see window_start).
+    sinks        optional [Hq] logits, one more term in each head's softmax denominator.
 
     Returns (out [total_q, Hq, D], lse [total_q, Hq]) or, with ``rows``,
     (out [n, D], lse [n]) in the order given.
@@ -165,15 +187,21 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
             if want is None:
                 i = np.arange(Qb)
                 counts = visible_key_count(Lb, Qb, i)
+                starts = window_start(Lb, Qb, i, window_left)
                 for qh in heads:
-                    o, s = attention_rows(q[t0:t1, qh, :], K, V, counts, scale)
+                    o, s = attention_rows(q[t0:t1, qh, :], K, V, counts, scale, starts=starts)
+                    if sinks is not None:
+                        o, s = add_sink(o, s, float(sinks[qh]))
                     out[t0:t1, qh, :] = o
                     lse[t0:t1, qh] = s
             else:
                 toks = want[sel, 0]
                 qrows = q[toks, want[sel, 1], :]
                 counts = visible_key_count(Lb, Qb, toks - t0)
-                o, s = attention_rows(qrows, K, V, counts, scale)
+                starts = window_start(Lb, Qb, toks - t0, window_left)
+                o, s = attention_rows(qrows, K, V, counts, scale, starts=starts)
+                if sinks is not None:
+                    o, s = add_sink(o, s, np.asarray(sinks, dtype=np.float64)[want[sel, 1]])
                 out[sel] = o
                 lse[sel] = s
     return out, lse
@@ -197,12 +225,12 @@ def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0):
     return [(min(s * per * tile, L), min((s + 1) * per * tile, L)) for s in range(num_splits)]
 
 
-def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0):
+def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0, starts=None):
     """Per-part partial states of rows over one sequence: (o_s [S, n, D], lse_s [S, n])."""
     ranges = split_ranges(K.shape[0], num_splits, tile, part_keys)
     os_, ls_ = [], []
     for lo, hi in ranges:
-        o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi)
+        o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi, starts=starts)
         os_.append(o)
         ls_.append(s)
     return np.stack(os_), np.stack(ls_)

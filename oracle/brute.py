@@ -15,8 +15,11 @@ def _f(x):
     return float(x)
 
 
-def brute_paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale):
+def brute_paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, window_left=-1,
+                          sinks=None):
     """q [total_q][Hq][D]; pools [num_pages][page_size][Hkv][D] (float values).
+    window_left >= 0: the token at key position p sees keys p - window_left .. p;
+    sinks[h]: a logit with no value added to head h's softmax denominator.
 
     Returns (out, lse) as nested Python lists: out[t][h][d], lse[t][h].
     """
@@ -35,23 +38,27 @@ def brute_paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_table
         L = int(seq_lens[b])
         for i in range(Q):
             n_vis = L - Q + i + 1
+            first = 0 if window_left is None or window_left < 0 else max(0, n_vis - 1 - window_left)
             for h in range(Hq):
                 kvh = h // g
-                if n_vis <= 0:
+                sink = None if sinks is None else _f(sinks[h])
+                if n_vis <= first:
+                    if sink is not None:
+                        lse[t0 + i][h] = sink  # only the sink: zeros and lse = sink
                     continue  # no visible key: zeros and -inf
                 qv = [_f(x) for x in q[t0 + i][h]]
                 scores = []
                 vals = []
-                for j in range(n_vis):
+                for j in range(first, n_vis):
                     page = int(block_tables[b][j // page_size])
                     slot = j % page_size
                     kj = k_pool[page][slot][kvh]
                     scores.append(scale * math.fsum(qv[d] * _f(kj[d]) for d in range(D)))
                     vals.append([_f(x) for x in v_pool[page][slot][kvh]])
-                m = max(scores)
+                m = max(scores) if sink is None else max(max(scores), sink)
                 w = [math.exp(s - m) for s in scores]
-                den = math.fsum(w)
-                out[t0 + i][h] = [math.fsum(w[j] * vals[j][d] for j in range(n_vis)) / den
+                den = math.fsum(w + ([math.exp(sink - m)] if sink is not None else []))
+                out[t0 + i][h] = [math.fsum(w[j] * vals[j][d] for j in range(len(w))) / den
                                   for d in range(D)]
                 lse[t0 + i][h] = m + math.log(den)
     return out, lse

@@ -404,11 +404,11 @@ MUTATIONS = {
                           lambda pool, bt, L, h: np.asarray(pool[np.asarray(bt)[np.arange(L) % pool.shape[1] % len(bt)],
                                                                  np.arange(L) // pool.shape[1] % pool.shape[1], h, :], np.float64)),
     "scale_dropped": ("attention_rows",
-                      lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, _f=oa.attention_rows:
-                      _f(q, K, V, c, 1.0, key_lo, key_hi, block)),
+                      lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows:
+                      _f(q, K, V, c, 1.0, key_lo, key_hi, block, starts)),
     "lse_base2": ("attention_rows",
-                  lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, _f=oa.attention_rows:
-                  (lambda r: (r[0], r[1] / math.log(2)))(_f(q, K, V, c, scale, key_lo, key_hi, block))),
+                  lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows:
+                  (lambda r: (r[0], r[1] / math.log(2)))(_f(q, K, V, c, scale, key_lo, key_hi, block, starts))),
     "merge_unweighted": ("merge_partials",
                          lambda o, l: (np.asarray(o).mean(0), np.asarray(l).max(0))),
 }
@@ -421,3 +421,93 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(oa, attr, fn)
     monkeypatch.setattr(oracle, attr, fn, raising=False)
     assert not _pin_suite_passes(), f"mutation {name} survived every pin"
+
+
+# ---------------------------------------------------------------- window and sinks
+
+def _dense(case):
+    k = gen.to_numpy64(case.k_pool)
+    v = gen.to_numpy64(case.v_pool)
+    return k, v
+
+
+@pytest.mark.parametrize("window,sinks", [(0, None), (3, None), (7, [0.5, -1.0, 2.0, 0.0, 1.0, -3.0]),
+                                          (-1, [0.5, -1.0, 2.0, 0.0, 1.0, -3.0]), (100, None)])
+def test_window_and_sinks_match_brute_force(window, sinks):
+    case = small_gqa_case(seed=13)
+    k, v = _dense(case)
+    o, l = oracle.paged_attention(gen.to_numpy64(case.q), k, v, case.cu_seqlens_q, case.seq_lens,
+                                  case.block_tables, case.scale, window_left=window, sinks=sinks)
+    bo, bl = oracle.brute_paged_attention(gen.to_numpy64(case.q).tolist(), k.tolist(), v.tolist(),
+                                          case.cu_seqlens_q.tolist(), case.seq_lens.tolist(),
+                                          case.block_tables.tolist(), case.scale, window_left=window, sinks=sinks)
+    bo, bl = np.array(bo), np.array(bl)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert (fin == np.isfinite(l)).all()
+    np.testing.assert_allclose(l[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+def test_window_special_cases():
+    case = small_gqa_case(seed=14)
+    k, v = _dense(case)
+    q = gen.to_numpy64(case.q)
+    args = (case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale)
+    full, fl = oracle.paged_attention(q, k, v, *args)
+    wide, wl = oracle.paged_attention(q, k, v, *args, window_left=int(case.seq_lens.max()))
+    np.testing.assert_array_equal(wide, full)
+    np.testing.assert_array_equal(wl, fl)
+    # window 0: each token sees only its own key: o = v at that key, lse = its score
+    o0, l0 = oracle.paged_attention(q, k, v, *args, window_left=0)
+    g = case.num_q_heads // case.num_kv_heads
+    for b in range(case.num_seqs):
+        L, Q = int(case.seq_lens[b]), int(case.q_lens[b])
+        for i in range(Q):
+            t, p = int(case.cu_seqlens_q[b]) + i, L - Q + i
+            for h in range(case.num_q_heads):
+                if p < 0:
+                    assert not o0[t, h].any() and l0[t, h] == -np.inf
+                    continue
+                page, slot = int(case.block_tables[b][p // case.page_size]), p % case.page_size
+                np.testing.assert_allclose(o0[t, h], v[page, slot, h // g], atol=1e-15)
+                np.testing.assert_allclose(l0[t, h], case.scale * q[t, h] @ k[page, slot, h // g], atol=1e-13)
+
+
+def test_sink_closed_forms():
+    case = small_gqa_case(seed=15)
+    k, v = _dense(case)
+    q = gen.to_numpy64(case.q)
+    args = (case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale)
+    base, bl = oracle.paged_attention(q, k, v, *args)
+    none, nl = oracle.paged_attention(q, k, v, *args, sinks=[-np.inf] * case.num_q_heads)
+    np.testing.assert_array_equal(none, base)
+    np.testing.assert_array_equal(nl, bl)
+    # zero queries: n visible keys of weight 1 and a sink of weight e^s: o = sum v / (n + e^s)
+    z, zl = oracle.paged_attention(np.zeros_like(q), k, v, *args, sinks=[0.7] * case.num_q_heads)
+    g = case.num_q_heads // case.num_kv_heads
+    for b in range(case.num_seqs):
+        L, Q = int(case.seq_lens[b]), int(case.q_lens[b])
+        for i in range(Q):
+            t, n = int(case.cu_seqlens_q[b]) + i, L - Q + i + 1
+            for h in range(case.num_q_heads):
+                V = oracle.gather_dense_kv(v, case.block_tables[b], L, h // g)[:max(n, 0)]
+                want = V.sum(axis=0) / (max(n, 0) + np.exp(0.7))
+                np.testing.assert_allclose(z[t, h], want, atol=1e-14)
+                np.testing.assert_allclose(zl[t, h], np.log(max(n, 0) + np.exp(0.7)), atol=1e-13)
+
+
+@pytest.mark.parametrize("S,window", [(3, 5), (4, 0), (2, 12)])
+def test_window_split_merge_equals_unsplit(S, window):
+    case = gen.make_case("wsplit", q_lens=[6], seq_lens=[300], num_q_heads=2, num_kv_heads=1, head_dim=16,
+                         page_size=16, q_kind="f32", seed=33)
+    q = gen.to_numpy64(case.q)[:, 0, :]
+    K = oracle.gather_dense_kv(gen.to_numpy64(case.k_pool), case.block_tables[0], 300, 0)
+    V = oracle.gather_dense_kv(gen.to_numpy64(case.v_pool), case.block_tables[0], 300, 0)
+    i = np.arange(6)
+    counts = oracle.visible_key_count(300, 6, i)
+    starts = oracle.window_start(300, 6, i, window)
+    o, l = oracle.attention_rows(q, K, V, counts, case.scale, starts=starts)
+    os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S, starts=starts)
+    om, lm = oracle.merge_partials(os_, ls_)
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, l, atol=1e-13)
