@@ -113,6 +113,26 @@ typedef struct pa_kv_cache {
 } pa_kv_cache;
 
 /*
+ * Optional variants of the attention calls (the *_ex entry points).  The
+ * pages' Turing prefill gate lists sinks and sliding windows among what it
+ * does not take (1CatAI/1Cat-vLLM PR #1279, commit 1, the selection rule);
+ * here they are options of every kernel.
+ *   sinks: device float[num_q_heads] or NULL.  Head h's softmax gets one more
+ *     logit sinks[h] (natural units, compared with scale * q.k) that carries
+ *     no value: o = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sinks[h]}), lse =
+ *     log(sum_j e^{s_j} + e^{sinks[h]}); a row with no visible key gets o = 0,
+ *     lse = sinks[h].  Applied once per row, in the unsplit epilogue or in the
+ *     merge; the FP32 records of pass 1 (out = NULL) stay sink-free.
+ *   window_left: < 0 for none; otherwise the token at key position p (p =
+ *     seq_len - q_len + i) sees keys p - window_left .. p only.
+ */
+typedef struct pa_attn_options {
+  const float *sinks;
+  int32_t window_left;
+  int32_t reserved;     /* must be 0 */
+} pa_attn_options;
+
+/*
  * Varlen paged prefill (InferMatrixLab/vllm-rlt PR #128, "Purpose", Prefill).
  *   q [total_q, num_q_heads, head_dim] (q_dtype); out same shape and dtype;
  *   lse nullable; scale (positive, finite) multiplies q.k (k_scale, also
@@ -141,6 +161,14 @@ int pa_paged_prefill(const void *q, int32_t q_dtype, void *out, float *lse,
                      int32_t total_q, int32_t max_seqlen_q, int32_t num_q_heads,
                      const pa_kv_cache *kv, float scale, int32_t num_kv_splits,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_paged_prefill with options (opts may be NULL: none). */
+int pa_paged_prefill_ex(const void *q, int32_t q_dtype, void *out, float *lse,
+                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
+                        int32_t total_q, int32_t max_seqlen_q, int32_t num_q_heads,
+                        const pa_kv_cache *kv, float scale, int32_t num_kv_splits,
+                        const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Split-KV decode / verify (InferMatrixLab/vllm-rlt PR #128, "Purpose", Decode).
@@ -194,6 +222,19 @@ int pa_split_kv_decode_fixed(const void *q, int32_t q_dtype, void *out, float *l
                              int32_t total_q, int32_t max_q_per_row, int32_t num_q_heads,
                              const pa_kv_cache *kv, float scale, int32_t part_keys, int32_t num_parts,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Split-KV decode with options: part_keys = 0 is pa_split_kv_decode (parts cut
+ * from each row's own length, num_splits of them), part_keys > 0 is
+ * pa_split_kv_decode_fixed (num_splits absolute parts of part_keys keys);
+ * opts may be NULL.
+ */
+int pa_split_kv_decode_ex(const void *q, int32_t q_dtype, void *out, float *lse,
+                          const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                          const int32_t *block_tables, int32_t num_rows, int32_t max_pages_per_seq,
+                          int32_t total_q, int32_t max_q_per_row, int32_t num_q_heads,
+                          const pa_kv_cache *kv, float scale, int32_t num_splits, int32_t part_keys,
+                          const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Merge of FP32 partial softmax states (InferMatrixLab/vllm-rlt PR #128,

@@ -88,7 +88,8 @@ def add_sink(o, lse, sink):
     """The softmax with one more logit `sink` in its denominator and no value:
     o * sum_j e^s_j / (sum_j e^s_j + e^sink), lse = log(sum_j e^s_j + e^sink)."""
     new = np.logaddexp(lse, sink)
-    f = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)
+    with np.errstate(invalid="ignore"):
+        f = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)
     return o * f[..., None], new
 
 

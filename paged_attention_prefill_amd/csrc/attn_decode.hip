@@ -75,6 +75,7 @@ void attn_decode_kernel(const AttnParams p) {
   const int tok = valid ? prow / g : 0;
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
+  const int lo = window_lo(p, L - qlen + tok);
 
   // Q^T (B operand) over the whole head dimension: k-step kk holds d = 16 kk + 8 hi .. +7
   // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half)
@@ -94,10 +95,17 @@ void attn_decode_kernel(const AttnParams p) {
   float m = kNegInf, lsum = 0.0f;
 
   const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
-  const int nt_w = ntiles > wave ? (ntiles - wave + WAVES - 1) / WAVES : 0;
+  // Tile t of the part (keys klo + 32 t ..) belongs to wave t % 4 whatever the
+  // window: tiles before the earliest window start of the group's rows are
+  // skipped, so each wave starts at its first tile at or after t0.  Anchoring
+  // the assignment at the part's start keeps a row's bits independent of the
+  // rows packed with it (the extra tiles of a verify row are masked no-ops).
+  const int t0 = (window_klo(p, klo, khi, L - qlen + row0 / g) - klo) / kKT;
+  const int tw = wave + WAVES * ((max(t0 - wave, 0) + WAVES - 1) / WAVES);
+  const int nt_w = ntiles > tw ? (ntiles - tw + WAVES - 1) / WAVES : 0;
   const uint32_t wbase = wave * NSW * STAGE_BYTES;
   TL tl;
-  tl.init(p, seq, kvh, 0, lane, klo + wave * kKT, kend, (uint32_t)(uintptr_t)(&smem[0]) + wbase);
+  tl.init(p, seq, kvh, 0, lane, klo + tw * kKT, kend, (uint32_t)(uintptr_t)(&smem[0]) + wbase);
   tl.set_stride(WAVES * kKT);
 
   const uint32_t klane = k_frag_lane(r32, hi);
@@ -185,7 +193,7 @@ void attn_decode_kernel(const AttnParams p) {
 
   for (int i = 0; i < nt_w; ++i) {
     const int st = NSW == 1 ? 0 : (i & 1);
-    const int j0 = klo + (wave + WAVES * i) * kKT;
+    const int j0 = klo + (tw + WAVES * i) * kKT;
     const uint32_t sb = wbase + st * STAGE_BYTES;
     const bool more = i + NSW < nt_w;
 
@@ -217,7 +225,7 @@ void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = key < lim ? s[r] * score_scale : kNegInf;
+      const float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }

@@ -129,12 +129,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   const int L = p.seq_lens[seq];
   int klo, khi;
   split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  klo = window_klo(p, klo, khi, L - qlen + row0 / g);  // first tile: the earliest window start
 
   const int prow = row0 + wave * 32 + r32;
   const bool valid = prow < nrows;
   const int tok = valid ? prow / g : 0;
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
+  const int lo = window_lo(p, L - qlen + tok);
   const int last_tok = (min(row0 + kRows, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow_first = row0 + wave * 32;
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = key < lim ? s[r] * score_scale : kNegInf;
+      const float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -287,9 +289,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   // ---- epilogue
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!valid) return;
-  const bool empty = (m == kNegInf) || !(ltot > 0.0f);
-  const float inv = empty ? 0.0f : out_scale / ltot;
-  const float lse_nat = empty ? kNegInf : (m + __log2f(ltot)) * 0.69314718055994530942f;
+  float inv, lse_nat;
+  final_row(p.write_partial ? nullptr : p.sinks, hq, m, ltot, out_scale, inv, lse_nat);
   const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
   if (p.write_partial) {
     float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);

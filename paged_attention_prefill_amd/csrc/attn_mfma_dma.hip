@@ -70,11 +70,13 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   const int wrow0 = row0 + wave * WROWS;
   const bool wave_active = wrow0 < nrows;
   const int wave_kend = wave_active ? min(khi, L - qlen + (min(wrow0 + WROWS, nrows) - 1) / g + 1) : 0;
+  // first tile: the part's start, or the tile of the earliest window start
+  const int kfirst = window_klo(p, klo, khi, L - qlen + row0 / g);
 
   // ---- this lane's rows (one per block) and their Q^T fragments (B operand):
   // lane holds row r32 of each block, d = 16 kk + 8 hi .. +7
   bool valid[RB], rb_on[RB];
-  int tok[RB], hq[RB], lim[RB];
+  int tok[RB], hq[RB], lim[RB], lo[RB];
   uint4 qf[RB][NKK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     tok[rb] = valid[rb] ? prow / g : 0;
     hq[rb] = kvh * g + (valid[rb] ? prow - (prow / g) * g : 0);
     lim[rb] = valid[rb] ? min(L - qlen + tok[rb] + 1, khi) : 0;
+    lo[rb] = window_lo(p, L - qlen + tok[rb]);
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb]) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -102,10 +105,10 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     for (int db = 0; db < NDB; ++db) oacc[rb][db] = (f32x16_t)(0.0f);
   }
 
-  const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
+  const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
 
   TileLoader<DPAD, WAVES> tl;
-  tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  tl.init(p, seq, kvh, wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
   auto issue = [&](int it, int stage) { tl.issue(it, stage); };
 
   // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
@@ -141,11 +144,11 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float tmax = kNegInf;
-      if (__any(j0 + kKT > lim[rb])) {  // causal diagonal / key-range end inside this tile
+      if (__any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float v = key < lim[rb] ? s[rb][r] * score_scale : kNegInf;
+          const float v = (key < lim[rb] && key >= lo[rb]) ? s[rb][r] * score_scale : kNegInf;
           s[rb][r] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -219,22 +222,21 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     wait_tiles<LPW, DIST - 1>(issued - it - 1);  // this tile's own loads have landed
     lds_barrier();
     if (issued < ntiles) issue(issued, issued % NST), ++issued;
-    const int j0 = klo + it * kKT;
+    const int j0 = kfirst + it * kKT;
     const bool live = wave_active && j0 < wave_kend;
     if (late && it > 0 && wave_active && j0 - kKT < wave_kend) pv((it - 1) % NST);
     if (live) qk_softmax(it % NST, j0);
     if (!late && live) pv(it % NST);
   }
-  if (late && ntiles > 0 && wave_active && klo + (ntiles - 1) * kKT < wave_kend) pv((ntiles - 1) % NST);
+  if (late && ntiles > 0 && wave_active && kfirst + (ntiles - 1) * kKT < wave_kend) pv((ntiles - 1) % NST);
 
   // ---- epilogue
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
     if (!valid[rb]) continue;
-    const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
-    const float inv = empty ? 0.0f : out_scale / ltot;
-    const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
+    float inv, lse_nat;
+    final_row(p.write_partial ? nullptr : p.sinks, hq[rb], m[rb], ltot, out_scale, inv, lse_nat);
     const int64_t rowidx = (int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb];
     if (p.write_partial) {
       float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);

@@ -131,9 +131,11 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow0 = row0 + wave * WROWS;
+  // first tile: the part's start, or the tile of the earliest window start
+  const int kfirst = window_klo(p, klo, khi, L - qlen + row0 / g);
 
   // this lane's rows (one per block) and their Q^T fragments (B operand)
-  int lim[RB];
+  int lim[RB], lo[RB];
   uint4 qf[RB][NKK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     const int tok = valid ? prow / g : 0;
     const int hq = kvh * g + (valid ? prow - tok * g : 0);
     lim[rb] = valid ? min(L - qlen + tok + 1, khi) : 0;
+    lo[rb] = window_lo(p, L - qlen + tok);
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -163,9 +166,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     acc_fence<NDB>(oacc[rb]);
   }
 
-  const int ntiles = kend > klo ? (kend - klo + kKT - 1) / kKT : 0;
+  const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
   TL tl;
-  tl.init(p, seq, kvh, wave, lane, klo, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  tl.init(p, seq, kvh, wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
 
   const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
@@ -220,16 +223,20 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     scores_ready(s[0], s[1]);
   };
 
-  // Causal / key-range mask on the scores of the tile starting at key j0;
-  // only tiles that reach some row's last key need it.
+  // Causal / key-range / window mask on the scores of the tile starting at
+  // key j0; only tiles that reach some row's last key or start before some
+  // row's window need it.
   auto mask_scores = [&](int j0) {
-    if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1])) {
+    if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1] || j0 < lo[0] || j0 < lo[1])) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
-        const int t = lim[rb] - j0 - 4 * hi;
+        const int t = lim[rb] - j0 - 4 * hi, u = lo[rb] - j0 - 4 * hi;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          s[rb][r] = (c < t && c >= u) ? s[rb][r] : kNegInf;
+        }
       }
     }
   };
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     wait_tiles<LPW, DIST - 1>(issued - 1);
     lds_barrier();
     qk_issue(0);
-    mask_scores(klo);
+    mask_scores(kfirst);
     softmax();
     if (issued < ntiles) tl.fetch(issued);
     // alpha of the first tile multiplies zero accumulators: nothing to rescale
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     for (int it = 1; it < ntiles; ++it) {
       wait_tiles<LPW, DIST - 1>(issued - it - 1);
       lds_barrier();
-      const int j0 = klo + it * kKT;
+      const int j0 = kfirst + it * kKT;
       qk_issue(it % NST);
       mask_scores(j0);
       pv_softmax((it - 1) % NST);
@@ -413,9 +420,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     if (prow >= nrows) continue;
     const int tok = prow / g;
     const int hq = kvh * g + (prow - tok * g);
-    const bool empty = (m[rb] == kNegInf) || !(ltot > 0.0f);
-    const float inv = empty ? 0.0f : out_scale / ltot;
-    const float lse_nat = empty ? kNegInf : (m[rb] + __log2f(ltot)) * 0.69314718055994530942f;
+    float inv, lse_nat;
+    final_row(p.write_partial ? nullptr : p.sinks, hq, m[rb], ltot, out_scale, inv, lse_nat);
     const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
     if (p.write_partial) {
       float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
   const int L = p.seq_lens[seq];
   int klo, khi;
   split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  klo = window_klo(p, klo, khi, L - qlen + row0 / g);  // first tile: the earliest window start
   const int last_tok = (min(row0 + kRowsV, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
 
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
   }
 
   // this wave's 4 rows
-  int lim[4], rowtok[4], rowhq[4];
+  int lim[4], lo[4], rowtok[4], rowhq[4];
   bool rvalid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
     rowtok[i] = rvalid[i] ? prow / g : 0;
     rowhq[i] = kvh * g + (rvalid[i] ? prow % g : 0);
     lim[i] = rvalid[i] ? min(L - qlen + rowtok[i] + 1, khi) : 0;
+    lo[i] = window_lo(p, L - qlen + rowtok[i]);
   }
   float m[4], l[4], o[4][NC];
 #pragma unroll
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 #pragma unroll 8
       for (int d = 0; d < HALF; ++d) dot = fmaf(qr[d], kr[d], dot);
       dot += __shfl_xor(dot, 32);
-      const float s = (j0 + key < lim[i]) ? dot * score_scale : kNegInfV;
+      const float s = (j0 + key < lim[i] && j0 + key >= lo[i]) ? dot * score_scale : kNegInfV;
       const float tmax = wave_max32(s);
       const float mnew = fmaxf(m[i], tmax);
       const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m[i] - mnew);
@@ -196,9 +198,8 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!rvalid[i]) continue;
-    const bool empty = m[i] == kNegInfV || !(l[i] > 0.0f);
-    const float inv = empty ? 0.0f : out_scale / l[i];
-    const float lse_nat = empty ? kNegInfV : (m[i] + log2f(l[i])) * 0.69314718055994530942f;
+    float inv, lse_nat;
+    final_row(p.write_partial ? nullptr : p.sinks, rowhq[i], m[i], l[i], out_scale, inv, lse_nat);
     const int64_t rowidx = (int64_t)(q0 + rowtok[i]) * p.num_q_heads + rowhq[i];
     if (p.write_partial) {
       float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);

@@ -8,7 +8,9 @@
 // (merge_rows_kernel below).  Record s = (o_s[0..D),
 // lse_s, pad) with o_s normalised.  M = max_s lse_s; w_s = exp(lse_s - M);
 // o = sum_s w_s o_s / sum_s w_s; lse = M + log sum_s w_s.  All parts empty ->
-// o = 0, lse = -inf; an empty part's o_s is never read into the sum.
+// o = 0, lse = -inf; an empty part's o_s is never read into the sum.  With
+// sinks, head h's sinks[h] joins as a logit with no value: M includes it and
+// the denominator gains exp(sinks[h] - M), once per row.
 //
 // Thread t owns a pair of output columns (t % (D/2)) and a run of parts
 // (t / (D/2)): a contiguous run, or every SG-th part for absolute parts; each
@@ -38,7 +40,8 @@ template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, floa
 // same bits whatever the part count of the call.
 template <typename OT, int kMT, bool STRIDED>
 __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ partials, int S, int D,
-                                                    OT* __restrict__ out, float* __restrict__ out_lse) {
+                                                    OT* __restrict__ out, float* __restrict__ out_lse,
+                                                    const float* __restrict__ sinks, int H) {
   constexpr int NW = kMT / 64;
   __shared__ float red[NW];
   __shared__ float2 part[kMT];
@@ -58,6 +61,9 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
   M = red[0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
+  // a sink is one more logit with no value, counted once per row
+  const float sk = sinks ? sinks[row % H] : kNegInfM;
+  M = fmaxf(M, sk);
 
   const int DC = D >> 1;                 // float2 column pairs
   const int SG = kMT / DC;               // runs of parts (>= 2 since D / 2 <= 128)
@@ -89,6 +95,7 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
       sy += v.y;
       sd += dpart[gI * DC];  // every thread of a run holds the same den
     }
+    if (sk != kNegInfM) sd += exp2f((sk - M) * kLog2e);
     const bool empty = M == kNegInfM || !(sd > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / sd;
     put2<OT>(out + row * D + 2 * t, sx * inv, sy * inv);
@@ -104,7 +111,8 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
 template <typename OT>
 __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict__ partials, int S, int D,
                                                          int64_t rows, OT* __restrict__ out,
-                                                         float* __restrict__ out_lse) {
+                                                         float* __restrict__ out_lse,
+                                                         const float* __restrict__ sinks, int H) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -113,6 +121,8 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
   float M = kNegInfM;
 #pragma unroll 4
   for (int s = 0; s < S; ++s) M = fmaxf(M, rec[(int64_t)s * R + D]);
+  const float sk = sinks ? sinks[row % H] : kNegInfM;  // one more logit with no value
+  M = fmaxf(M, sk);
   const int DC = D >> 1;
   for (int dc = lane; dc < DC; dc += 64) {
     float ax = 0.0f, ay = 0.0f, den = 0.0f;
@@ -128,6 +138,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
         ay = live ? fmaf(ws, v.y, ay) : ay;
         den += ws;
       }
+      if (sk != kNegInfM) den += exp2f((sk - M) * kLog2e);
     }
     const bool empty = M == kNegInfM || !(den > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / den;
@@ -138,27 +149,27 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
 
 template <typename OT>
 static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out, float* out_lse,
-                           bool strided, hipStream_t stream) {
+                           bool strided, const float* sinks, hipStream_t stream) {
   const int64_t rows = (int64_t)ntok * H;
   if (rows == 0) return hipSuccess;
   if (strided)
     hipLaunchKernelGGL((merge_kernel<OT, 1024, true>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
-                       (OT*)out, out_lse);
+                       (OT*)out, out_lse, sinks, H);
   else if (S >= 16)
     hipLaunchKernelGGL((merge_kernel<OT, 1024, false>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
-                       (OT*)out, out_lse);
+                       (OT*)out, out_lse, sinks, H);
   else
     hipLaunchKernelGGL((merge_rows_kernel<OT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, partials, S,
-                       D, rows, (OT*)out, out_lse);
+                       D, rows, (OT*)out, out_lse, sinks, H);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, bool strided, hipStream_t stream) {
+                        float* out_lse, bool strided, const float* sinks, hipStream_t stream) {
   switch (out_kind) {
-    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, strided, stream);
-    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, strided, stream);
-    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, strided, stream);
+    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
+    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
+    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,7 +41,50 @@ struct AttnParams {
   float v_scale;
   const float* k_head_scale;  // [Hkv] or null: fp8 K of head h is decode(byte) * k_scale * k_head_scale[h]
   const float* v_head_scale;  // [Hkv] or null
+  const float* sinks;         // [Hq] or null: one more logit per q head in the softmax denominator
+  int window_left;            // < 0: none; the token at key p sees keys >= p - window_left
 };
+
+// First key visible to the token at key position `pos` under the left window.
+__device__ __forceinline__ int window_lo(const AttnParams& p, int pos) {
+  return p.window_left < 0 ? 0 : max(0, pos - p.window_left);
+}
+
+// Start of a work group's tiles: klo moved up to the tile that holds the
+// earliest window start of its rows (first_pos = key position of its first
+// token), staying on the klo + 32 t grid.
+__device__ __forceinline__ int window_klo(const AttnParams& p, int klo, int khi, int first_pos) {
+  const int lo = window_lo(p, first_pos);
+  if (lo <= klo) return klo;
+  const int t = min(lo, khi) - klo;
+  return klo + (t / 32) * 32;
+}
+
+// Epilogue of an unsplit row: output factor and natural-log lse from the row
+// state (m: running max in log2 units of the scaled scores, l: the sum of
+// exp2(s - m)), with the head's sink taken into the denominator.
+// `sinks` is p.sinks for a final output and null for a partial record.
+__device__ __forceinline__ void final_row(const float* sinks, int hq, float m, float l, float out_scale,
+                                          float& inv, float& lse_nat) {
+  const float kNegInfF = -__builtin_huge_valf();
+  if (sinks == nullptr) {
+    const bool empty = (m == kNegInfF) || !(l > 0.0f);
+    inv = empty ? 0.0f : out_scale / l;
+    lse_nat = empty ? kNegInfF : (m + __log2f(l)) * 0.69314718055994530942f;
+    return;
+  }
+  const float sk = sinks[hq] * 1.4426950408889634f;
+  const float M = fmaxf(m, sk);
+  if (M == kNegInfF) {  // no visible key and a sink of -inf
+    inv = 0.0f;
+    lse_nat = kNegInfF;
+    return;
+  }
+  const float a = m == kNegInfF ? 0.0f : exp2f(m - M);
+  const float l2 = l * a + exp2f(sk - M);
+  inv = out_scale * a / l2;
+  lse_nat = (M + __log2f(l2)) * 0.69314718055994530942f;
+}
 
 // The score factor (scale * k_scale * log2 e, times the head's K scale) and the
 // output factor (v_scale times the head's V scale) of kv head h.

@@ -19,7 +19,7 @@ hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dp
 hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                             hipStream_t stream);
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, bool strided, hipStream_t stream);
+                        float* out_lse, bool strided, const float* sinks, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks,
                                 hipStream_t stream);
@@ -291,8 +291,8 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
 static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
                          const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
                          int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
-                         int splits, int part_keys, bool is_decode, void* workspace, size_t ws_bytes,
-                         hipStream_t stream) {
+                         int splits, int part_keys, bool is_decode, const pa_attn_options* opts,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   const int g = hq / kv->num_kv_heads;
   const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
   const int rows = rows_for(kind, dpad_of(kv->head_dim), is_decode);
@@ -343,6 +343,8 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.v_scale = is_fp8(kv->dtype) ? kv->v_scale : 1.0f;
   p.k_head_scale = kv->k_head_scales;
   p.v_head_scale = kv->v_head_scales;
+  p.sinks = opts ? opts->sinks : nullptr;
+  p.window_left = opts ? opts->window_left : -1;
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
@@ -354,11 +356,18 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
     e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, part_keys > 0,
-                         stream);
+                         p.sinks, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   (void)ws_bytes;
   return ok();
+}
+
+static int check_options(const pa_attn_options* opts) {
+  if (opts == nullptr) return PA_OK;
+  if (opts->reserved != 0) return fail(PA_ERR_INVALID_ARGUMENT, "pa_attn_options.reserved must be 0");
+  if ((uintptr_t)opts->sinks & 3u) return fail(PA_ERR_INVALID_ARGUMENT, "sinks must be 4-byte aligned");
+  return PA_OK;
 }
 
 static int check_common(const void* q, int q_dtype, void* out, const int32_t* cu, const int32_t* seq_lens,
@@ -375,13 +384,15 @@ static int check_common(const void* q, int q_dtype, void* out, const int32_t* cu
   return PA_OK;
 }
 
-int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
-                     const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs,
-                     int32_t max_pages_per_seq, int32_t total_q, int32_t max_seqlen_q,
-                     int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_kv_splits,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+int pa_paged_prefill_ex(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs,
+                        int32_t max_pages_per_seq, int32_t total_q, int32_t max_seqlen_q,
+                        int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_kv_splits,
+                        const pa_attn_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq,
                         total_q, max_seqlen_q, num_q_heads, kv);
+  if (st != PA_OK) return st;
+  st = check_options(opts);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
@@ -406,15 +417,26 @@ int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, cons
                   splits, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
   }
   return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_seqs,
-                       max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, 0, false,
+                       max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, splits, 0, false, opts,
                        workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int pa_paged_prefill(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                     const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs,
+                     int32_t max_pages_per_seq, int32_t total_q, int32_t max_seqlen_q,
+                     int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_kv_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_paged_prefill_ex(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_seqs,
+                             max_pages_per_seq, total_q, max_seqlen_q, num_q_heads, kv, scale, num_kv_splits,
+                             nullptr, workspace, workspace_bytes, stream);
 }
 
 static int decode_call(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
                        const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
                        int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
                        int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
-                       int32_t part_keys, void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t part_keys, const pa_attn_options* opts, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
                         total_q, max_q_per_row, num_q_heads, kv);
   if (st != PA_OK) return st;
@@ -424,6 +446,10 @@ static int decode_call(const void* q, int32_t q_dtype, void* out, float* lse, co
     return fail(PA_ERR_UNSUPPORTED, "max_q_per_row %d > %d (longer rows go to pa_paged_prefill)", max_q_per_row,
                 PA_DECODE_MAX_Q);
   if (num_splits < 1 || num_splits > 4096) return fail(PA_ERR_INVALID_ARGUMENT, "num_splits must be in [1, 4096]");
+  if (part_keys < 0 || part_keys % PA_DECODE_SPLIT_TILE != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "part_keys must be 0 or a positive multiple of %d", PA_DECODE_SPLIT_TILE);
+  st = check_options(opts);
+  if (st != PA_OK) return st;
   if (out == nullptr && lse != nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "lse must be NULL when out is NULL");
   if (num_rows == 0 || total_q == 0) return ok();
   const size_t need = pa_decode_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_splits);
@@ -431,7 +457,7 @@ static int decode_call(const void* q, int32_t q_dtype, void* out, float* lse, co
     return fail(PA_ERR_WORKSPACE, "decode needs %zu bytes of 8-byte aligned workspace (got %zu)", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   return run_attention(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
-                       total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, part_keys, true, workspace,
+                       total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, part_keys, true, opts, workspace,
                        workspace_bytes, (hipStream_t)stream);
 }
 
@@ -441,8 +467,8 @@ int pa_split_kv_decode(const void* q, int32_t q_dtype, void* out, float* lse, co
                        int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
                        void* workspace, size_t workspace_bytes, void* stream) {
   return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
-                     total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, 0, workspace, workspace_bytes,
-                     stream);
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, 0, nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
@@ -453,7 +479,7 @@ int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* l
   if (part_keys < PA_DECODE_SPLIT_TILE || part_keys % PA_DECODE_SPLIT_TILE != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "part_keys must be a positive multiple of %d", PA_DECODE_SPLIT_TILE);
   return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
-                     total_q, max_q_per_row, num_q_heads, kv, scale, num_parts, part_keys, workspace,
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_parts, part_keys, nullptr, workspace,
                      workspace_bytes, stream);
 }
 
@@ -501,6 +527,17 @@ int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const i
   return ok();
 }
 
+int pa_split_kv_decode_ex(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
+                          int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
+                          int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
+                          int32_t part_keys, const pa_attn_options* opts, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, part_keys, opts, workspace,
+                     workspace_bytes, stream);
+}
+
 int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,
                     int32_t head_dim, void* out, int32_t out_dtype, float* out_lse, void* stream) {
   if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 2 || head_dim > 256 || head_dim % 2)
@@ -514,7 +551,7 @@ int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_token
   if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
     return fail(PA_ERR_UNSUPPORTED, "too many rows");
   hipError_t e = pa::launch_merge(partials, num_splits, num_tokens, num_heads, head_dim, out, kind_of(out_dtype),
-                                  out_lse, false, (hipStream_t)stream);
+                                  out_lse, false, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -34,6 +34,10 @@ class PagedAttentionError(RuntimeError):
         self.status = status
 
 
+class AttnOptions(ctypes.Structure):
+    _fields_ = [("sinks", ctypes.c_void_p), ("window_left", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class KvCache(ctypes.Structure):
     _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
                 ("stride_page", ctypes.c_int64), ("stride_token", ctypes.c_int64),
@@ -62,6 +66,9 @@ def lib():
                                        ctypes.POINTER(KvCache), ctypes.c_float, _I, _P, _SZ, _P]
         L.pa_split_kv_decode.argtypes = L.pa_paged_prefill.argtypes
         L.pa_split_kv_decode_fixed.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, _P, _SZ, _P]
+        L.pa_paged_prefill_ex.argtypes = L.pa_paged_prefill.argtypes[:15] + [ctypes.POINTER(AttnOptions), _P, _SZ, _P]
+        L.pa_split_kv_decode_ex.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, ctypes.POINTER(AttnOptions),
+                                                                              _P, _SZ, _P]
         L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.pa_write_kv.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), _P]
         L.pa_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I]
@@ -74,7 +81,7 @@ def lib():
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
         for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_split_kv_decode_fixed", "pa_merge_states",
-                     "pa_write_kv",
+                     "pa_write_kv", "pa_paged_prefill_ex", "pa_split_kv_decode_ex",
                      "pa_check_supported",
                      "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
             if name != "pa_status_string":
@@ -146,6 +153,16 @@ def _i32(t, name):
     return t
 
 
+def _options(sinks, window_left):
+    """pa_attn_options for the *_ex calls, or None when neither is set."""
+    if sinks is None and (window_left is None or window_left < 0):
+        return None
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "sinks must be a contiguous float32 [Hq] tensor")
+    o = AttnOptions(None if sinks is None else sinks.data_ptr(), -1 if window_left is None else int(window_left), 0)
+    return ctypes.byref(o), o  # keep the struct alive with the reference
+
+
 def prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits):
     return int(lib().pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, num_kv_splits))
 
@@ -170,8 +187,9 @@ def _partials_view(workspace, total_q, Hq, D, splits):
 def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_seqlen_q, scale,
                   *, k_scale=1.0, v_scale=1.0, num_kv_splits=1, out=None, lse=None,
                   return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
-                  v_head_scales=None):
-    """pa_paged_prefill on torch tensors; returns out (and lse).
+                  v_head_scales=None, sinks=None, window_left=-1):
+    """pa_paged_prefill(_ex) on torch tensors; returns out (and lse).
+    sinks (float32 [Hq] on the device) and window_left select the options.
 
     merge=False (num_kv_splits >= 2): runs the first pass only and returns the
     FP32 records [total_q, Hq, num_kv_splits, D + 2] for merge_states."""
@@ -189,11 +207,13 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
     ws_bytes = prefill_workspace_bytes(total_q, Hq, D, num_kv_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_paged_prefill(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
-                                  _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
-                                  _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
-                                  total_q, int(max_seqlen_q), Hq, ctypes.byref(kv), float(scale),
-                                  int(num_kv_splits), _ptr(workspace), ws_have, _stream(stream)))
+    opts = _options(sinks, window_left)
+    _check(lib().pa_paged_prefill_ex(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
+                                     _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
+                                     _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
+                                     total_q, int(max_seqlen_q), Hq, ctypes.byref(kv), float(scale),
+                                     int(num_kv_splits), opts[0] if opts else None, _ptr(workspace), ws_have,
+                                     _stream(stream)))
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_kv_splits)
     return (out, lse) if return_lse or lse is not None else out
@@ -202,7 +222,7 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
 def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
                     *, num_splits=16, part_keys=0, k_scale=1.0, v_scale=1.0, out=None, lse=None,
                     return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
-                    v_head_scales=None):
+                    v_head_scales=None, sinks=None, window_left=-1):
     """pa_split_kv_decode on torch tensors; returns out (and lse).
 
     part_keys > 0: pa_split_kv_decode_fixed, num_splits absolute parts of
@@ -226,11 +246,9 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     args = (_ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
             _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
             total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale))
-    tail = (_ptr(workspace), ws_have, _stream(stream))
-    if part_keys:
-        _check(lib().pa_split_kv_decode_fixed(*args, int(part_keys), int(num_splits), *tail))
-    else:
-        _check(lib().pa_split_kv_decode(*args, int(num_splits), *tail))
+    opts = _options(sinks, window_left)
+    _check(lib().pa_split_kv_decode_ex(*args, int(num_splits), int(part_keys), opts[0] if opts else None,
+                                       _ptr(workspace), ws_have, _stream(stream)))
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_splits)
     return (out, lse) if return_lse or lse is not None else out

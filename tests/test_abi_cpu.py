@@ -197,3 +197,23 @@ def test_out_null_needs_split_and_no_lse():
                                     ctypes.byref(kv), 0.1, 16, None, 0, None)
     assert dec(None, 0x90000) == ops.PA_ERR_INVALID_ARGUMENT
     assert dec(None, None) == ops.PA_ERR_WORKSPACE
+
+
+def test_options_are_checked_before_launch():
+    L = ops.lib()
+    kv = _fake_kv()
+    bad = ops.AttnOptions(None, 10, 1)
+    st = L.pa_paged_prefill_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 2, 4, 10, 8, 8,
+                               ctypes.byref(kv), 0.1, 1, ctypes.byref(bad), None, 0, None)
+    assert st == ops.PA_ERR_INVALID_ARGUMENT
+    mis = ops.AttnOptions(0x1002, -1, 0)
+    st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
+                                 ctypes.byref(kv), 0.1, 8, 0, ctypes.byref(mis), None, 0, None)
+    assert st == ops.PA_ERR_INVALID_ARGUMENT
+    st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
+                                 ctypes.byref(kv), 0.1, 8, 48, None, None, 0, None)
+    assert st == ops.PA_ERR_INVALID_ARGUMENT  # part_keys not a multiple of 32
+    ok = ops.AttnOptions(0x1000, 5, 0)
+    st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
+                                 ctypes.byref(kv), 0.1, 8, 0, ctypes.byref(ok), None, 0, None)
+    assert st == ops.PA_ERR_WORKSPACE  # accepted up to the workspace check

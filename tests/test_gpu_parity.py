@@ -612,3 +612,68 @@ def test_fp8_per_head_scales(fmt, D, P):
     dec = gen.select_seqs(c, [1, 2])
     out, lse = gpu_decode(dec, splits=8, max_q=4)
     compare(f"{fmt} per-head decode D={D}", fmt, out.float().cpu().numpy(), ref[90:], lse.cpu().numpy(), rl[90:])
+
+
+# ------------------------------------------------------------------ sliding window and sinks
+
+WINDOW_CASES = [
+    # (q dtype, KV dtype, D, Hq, Hkv, page, window_left, with sinks)
+    ("bf16", "bf16", 128, 8, 2, 32, 37, True),
+    ("f16", "f16", 256, 12, 2, 64, 300, True),
+    ("f16", "f16", 64, 4, 4, 16, 0, False),
+    ("f16", "f16", 256, 6, 1, 48, 1000, False),
+    ("f32", "f32", 64, 4, 1, 16, 50, True),
+    ("f16", "e5m2", 256, 8, 2, 64, 129, True),
+    ("f16", "e4m3", 128, 8, 2, 16, 64, True),
+]
+
+
+@pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,window,with_sinks", WINDOW_CASES)
+def test_window_and_sinks(qk, kvk, D, Hq, Hkv, P, window, with_sinks):
+    """Left sliding window and attention sinks against the oracle: prefill with
+    1 and 3 parts (sinks in the epilogue, then in the merge) and decode with
+    proportional and absolute parts."""
+    c = gen.make_case(f"win_{qk}_{kvk}_D{D}_W{window}", q_lens=[150, 1, 5, 40], seq_lens=[900, 700, 1300, 30],
+                      num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, q_kind=qk, kv_kind=kvk,
+                      seed=5 * D + window)
+    rng = np.random.default_rng(window + D)
+    sinks = rng.normal(size=Hq).astype(np.float32) * 2 if with_sinks else None
+    k, v = oracle_pools(c)
+    ref, rl = oracle.paged_attention(gen.to_numpy64(c.q), k, v, c.cu_seqlens_q, c.seq_lens, c.block_tables,
+                                     c.scale, window_left=window, sinks=sinks)
+    d = gen.to_device(c)
+    sk = None if sinks is None else torch.from_numpy(sinks).cuda()
+    kind = kvk if kvk in ("e5m2", "e4m3") else qk
+    for splits in (1, 3):
+        say(f"  window {window} sinks {with_sinks}: prefill S={splits}")
+        out, lse = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
+                                     c.scale, num_kv_splits=splits, return_lse=True, sinks=sk, window_left=window)
+        torch.cuda.synchronize()
+        compare(f"window prefill S={splits}", kind, out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
+    dec = gen.select_seqs(c, [1, 2])
+    dd = gen.to_device(dec)
+    for part_keys, parts in ((0, 8), (128, 12)):
+        say(f"  window {window} sinks {with_sinks}: decode part_keys={part_keys}")
+        out, lse = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 5, c.scale,
+                                       num_splits=parts, part_keys=part_keys, return_lse=True, sinks=sk,
+                                       window_left=window)
+        torch.cuda.synchronize()
+        compare(f"window decode C={part_keys}", kind, out.float().cpu().numpy(), ref[150:156], lse.cpu().numpy(),
+                rl[150:156])
+
+
+def test_window_verify_row_equals_serial_decode_bitwise():
+    """With a window, absolute parts still give a verify row the bits of its
+    token-wise expansion (each wave's tiles stay anchored at the part start)."""
+    case = gen.make_case("verify_window", q_lens=[5, 1], seq_lens=[3000, 900], num_q_heads=24, num_kv_heads=4,
+                         head_dim=256, page_size=816, q_kind="f16", seed=83)
+    ser = gen.expand_row(case, 0)
+    sk = torch.linspace(-1, 1, 24, device="cuda")
+    d, ds = gen.to_device(case), gen.to_device(ser)
+    outs = []
+    for c, dd, parts, mq in ((case, d, 10, 5), (ser, ds, 6, 1)):
+        out = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], mq, c.scale,
+                                  num_splits=parts, part_keys=512, sinks=sk, window_left=777)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(outs[0][:5]), bits(outs[1]))
