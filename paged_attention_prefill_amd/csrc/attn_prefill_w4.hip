@@ -90,7 +90,9 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 // F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16); the tiles stay 8-bit in
 // LDS and are widened to fp16 as their MFMA operands are read.  F8 = 0: KV of
 // the q dtype.
-template <typename QT, int F8, int DPAD, int NST>
+// WIN: a left sliding window is set (a separate instantiation, so that the
+// default one keeps no per-row window state in this tightly scheduled loop).
+template <typename QT, int F8, int DPAD, int NST, bool WIN>
 __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParams p) {
   constexpr bool KV8 = F8 != 0;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow0 = row0 + wave * WROWS;
   // first tile: the part's start, or the tile of the earliest window start
-  const int kfirst = window_klo(p, klo, khi, L - qlen + row0 / g);
+  const int kfirst = WIN ? window_klo(p, klo, khi, L - qlen + row0 / g) : klo;
 
   // this lane's rows (one per block) and their Q^T fragments (B operand)
   int lim[RB], lo[RB];
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     const int tok = valid ? prow / g : 0;
     const int hq = kvh * g + (valid ? prow - tok * g : 0);
     lim[rb] = valid ? min(L - qlen + tok + 1, khi) : 0;
-    lo[rb] = window_lo(p, L - qlen + tok);
+    lo[rb] = WIN ? window_lo(p, L - qlen + tok) : 0;
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -227,15 +229,26 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   // key j0; only tiles that reach some row's last key or start before some
   // row's window need it.
   auto mask_scores = [&](int j0) {
-    if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1] || j0 < lo[0] || j0 < lo[1])) {
+    if constexpr (WIN) {
+      if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1] || j0 < lo[0] || j0 < lo[1])) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
-        const int t = lim[rb] - j0 - 4 * hi, u = lo[rb] - j0 - 4 * hi;
+        for (int rb = 0; rb < RB; ++rb) {
+          // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
+          const int t = lim[rb] - j0 - 4 * hi, u = lo[rb] - j0 - 4 * hi;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          s[rb][r] = (c < t && c >= u) ? s[rb][r] : kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int c = 8 * (r >> 2) + (r & 3);
+            s[rb][r] = (c < t && c >= u) ? s[rb][r] : kNegInf;
+          }
+        }
+      }
+    } else {
+      if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1])) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int t = lim[rb] - j0 - 4 * hi;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kNegInf;
         }
       }
     }
@@ -466,7 +479,10 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 namespace {
 template <typename QT, int F8, int DPAD, int NST>
 hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST>), dim3(nblocks), dim3(256), 0, stream, p);
+  if (p.window_left >= 0)
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, true>), dim3(nblocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, false>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -488,7 +504,7 @@ hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
   if (dpad == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5>, 256, 0);
+                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5, false>, 256, 0);
   return hipErrorInvalidValue;
 }
 
