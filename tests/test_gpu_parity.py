@@ -250,7 +250,7 @@ def test_page_size_permutation_and_layout_leave_output_bitwise_unchanged():
 
 # ------------------------------------------------------------------ shapes and edge cases
 
-@pytest.mark.parametrize("D", [16, 64, 96, 128, 160, 256])
+@pytest.mark.parametrize("D", [16, 48, 64, 80, 96, 112, 128, 144, 160, 192, 224, 240, 256])
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_head_dims(D, kind):
     c = gen.make_case(f"hd{D}", q_lens=[70, 3, 129], seq_lens=[70, 200, 1000], num_q_heads=6, num_kv_heads=2,
