@@ -73,6 +73,7 @@ class Call:
 
     def __init__(self, kind, case, d, splits, max_q=None):
         self.kind, self.case, self.d, self.splits = kind, case, d, splits
+        self.window = case.meta.get("window_left", -1)
         self.max_q = max_q or max(1, case.max_seqlen_q)
         self.out = torch.empty_like(d["q"])
         self.lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
@@ -95,7 +96,7 @@ class Call:
             # the two passes apart, so that the attention kernel is timed alone
             parts = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
                                       c.scale, k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits,
-                                      workspace=self.ws, stream=stream, merge=False)
+                                      workspace=self.ws, stream=stream, merge=False, window_left=self.window)
             if record:
                 em = torch.cuda.Event(enable_timing=True)
                 em.record(stream)
@@ -104,11 +105,11 @@ class Call:
         elif self.kind == "prefill":
             ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
                               k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits, out=self.out,
-                              lse=self.lse, workspace=self.ws, stream=stream)
+                              lse=self.lse, workspace=self.ws, stream=stream, window_left=self.window)
         else:
             ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], self.max_q, c.scale,
                                 num_splits=self.splits, k_scale=c.k_scale, v_scale=c.v_scale, out=self.out,
-                                lse=self.lse, workspace=self.ws, stream=stream)
+                                lse=self.lse, workspace=self.ws, stream=stream, window_left=self.window)
         if record:
             e1.record(stream)
             self.times.append((e0, e1))
@@ -127,7 +128,8 @@ class Call:
 
 
 # The calls of one step of each workload, in launch order.
-WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "mixed_step": ["prefill", "decode"],
+WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "long_chunk_window": ["prefill", "decode"],
+                  "mixed_step": ["prefill", "decode"],
                   "mixed_step_fp8": ["prefill", "decode"], "mixed_step_e4m3": ["prefill", "decode"],
                   "decode_batch": ["decode"], "varlen": ["prefill"]}
 
@@ -143,6 +145,15 @@ def build_workload(name):
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
                 "seq_len": 152048, "kv_dtype": "f16"}
         return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
+    if name == "long_chunk_window":
+        c = gen.long_chunk()
+        c.meta["window_left"] = 8191
+        pre = gen.select_seqs(c, [0], name="prefill 2048 after 150000, window 8192")
+        dec = gen.select_seqs(c, [1], name="decode q=1 at 152048, window 8192")
+        desc = {"workload": "the long chunk with a left sliding window of 8192 keys (prefill + q=1 decode)",
+                "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
+                "seq_len": 152048, "kv_dtype": "f16", "window_left": 8191}
+        return desc, [("prefill", pre, "auto"), ("decode", dec, 16)]
     if name == "mixed_step":
         c = gen.mixed_step(kv_kind="f16")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
@@ -187,12 +198,14 @@ def prefill_kernel_name(desc):
 
 
 def call_flops(kind, case):
-    return workload.prefill_flops(case.cu_seqlens_q, case.seq_lens, case.num_q_heads, case.head_dim)
+    return workload.prefill_flops(case.cu_seqlens_q, case.seq_lens, case.num_q_heads, case.head_dim,
+                                  case.meta.get("window_left", -1))
 
 
 def call_bytes(kind, case, splits):
     return workload.decode_bytes(case.cu_seqlens_q, case.seq_lens, case.num_q_heads, case.num_kv_heads,
-                                 case.head_dim, case.page_size, case.q_kind, case.kv_kind, splits)
+                                 case.head_dim, case.page_size, case.q_kind, case.kv_kind, splits,
+                                 case.meta.get("window_left", -1))
 
 
 def cpu_baseline(case, budget_rows, seed=0):

@@ -39,6 +39,7 @@ from .attention import (  # noqa: F401
     gather_dense_kv,
     visible_key_count,
     window_start,
+    window_base,
     add_sink,
     attention_rows,
     paged_attention,

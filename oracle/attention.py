@@ -208,7 +208,15 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
     return out, lse
 
 
-def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0):
+def window_base(seq_len, q_len, window_left, tile=SPLIT_TILE):
+    """First key any token of a sequence can see under a left window (its first
+    token's window start), rounded down to the tile grid; 0 without a window."""
+    if window_left is None or window_left < 0:
+        return 0
+    return (max(0, int(seq_len) - int(q_len) - int(window_left)) // tile) * tile
+
+
+def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0, base=0):
     """Key ranges of the S parts of a row of length seq_len.
 
     part_keys == 0: S tile-aligned parts cut from the row's own length
@@ -221,14 +229,15 @@ def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0):
     if part_keys:
         C = int(part_keys)
         return [(min(s * C, L), L if s == num_splits - 1 else min((s + 1) * C, L)) for s in range(num_splits)]
-    tiles = -(-L // tile)
+    # parts of the keys the sequence can see, [base, L) (base: window_base)
+    tiles = -(-(L - base) // tile)
     per = -(-tiles // num_splits)
-    return [(min(s * per * tile, L), min((s + 1) * per * tile, L)) for s in range(num_splits)]
+    return [(min(base + s * per * tile, L), min(base + (s + 1) * per * tile, L)) for s in range(num_splits)]
 
 
-def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0, starts=None):
+def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0, starts=None, base=0):
     """Per-part partial states of rows over one sequence: (o_s [S, n, D], lse_s [S, n])."""
-    ranges = split_ranges(K.shape[0], num_splits, tile, part_keys)
+    ranges = split_ranges(K.shape[0], num_splits, tile, part_keys, base)
     os_, ls_ = [], []
     for lo, hi in ranges:
         o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi, starts=starts)

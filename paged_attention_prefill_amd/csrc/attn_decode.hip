@@ -66,7 +66,7 @@ void attn_decode_kernel(const AttnParams p) {
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  split_range(p, L, qlen, split, klo, khi);
   const int last_tok = (min(row0 + 32, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
 

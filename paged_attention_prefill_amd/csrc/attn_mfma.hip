@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  split_range(p, L, qlen, split, klo, khi);
   klo = window_klo(p, klo, khi, L - qlen + row0 / g);  // first tile: the earliest window start
 
   const int prow = row0 + wave * 32 + r32;

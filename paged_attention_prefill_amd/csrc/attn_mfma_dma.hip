@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  split_range(p, L, qlen, split, klo, khi);
 
   const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);

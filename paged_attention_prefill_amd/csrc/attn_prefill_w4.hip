@@ -129,15 +129,21 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   if (row0 >= nrows) return;
   const int L = p.seq_lens[seq];
   int klo, khi;
-  split_range(L, p.num_splits, split, p.part_keys, klo, khi);
+  split_range(p, L, qlen, split, klo, khi);
   const int last_tok = (min(row0 + ROWS, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow0 = row0 + wave * WROWS;
   // first tile: the part's start, or the tile of the earliest window start
   const int kfirst = WIN ? window_klo(p, klo, khi, L - qlen + row0 / g) : klo;
+  // mask bounds of this wave's rows (monotone in the row): tiles that end
+  // past wlim or (window) start before wlo need the per-element mask
+  const int wlim = wrow0 + WROWS > nrows ? 0 : min(L - qlen + wrow0 / g + 1, khi);
+  const int wlo = (!WIN || wrow0 >= nrows) ? 0 : window_lo(p, L - qlen + (min(wrow0 + WROWS, nrows) - 1) / g);
 
-  // this lane's rows (one per block) and their Q^T fragments (B operand)
-  int lim[RB], lo[RB];
+  // this lane's rows (one per block) and their Q^T fragments (B operand).
+  // lim: one past the row's last visible key (the part's end and the window
+  // start are applied in the rare masked tiles: one register per row block).
+  int lim[RB];
   uint4 qf[RB][NKK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -145,8 +151,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     const bool valid = prow < nrows;
     const int tok = valid ? prow / g : 0;
     const int hq = kvh * g + (valid ? prow - tok * g : 0);
-    lim[rb] = valid ? min(L - qlen + tok + 1, khi) : 0;
-    lo[rb] = WIN ? window_lo(p, L - qlen + tok) : 0;
+    lim[rb] = valid ? L - qlen + tok + 1 : 0;
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -230,11 +235,14 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   // row's window need it.
   auto mask_scores = [&](int j0) {
     if constexpr (WIN) {
-      if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1] || j0 < lo[0] || j0 < lo[1])) {
+      // wave-uniform test: the tile ends past the wave's first row's limit
+      // (or the wave has rows past the end), or starts before the window
+      // start of its last row
+      if (j0 + kKT > wlim || j0 < wlo) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
-          const int t = lim[rb] - j0 - 4 * hi, u = lo[rb] - j0 - 4 * hi;
+          const int t = min(lim[rb], khi) - j0 - 4 * hi, u = lim[rb] - 1 - p.window_left - j0 - 4 * hi;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
@@ -243,10 +251,10 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
         }
       }
     } else {
-      if (__any(j0 + kKT > lim[0] || j0 + kKT > lim[1])) {
+      if (j0 + kKT > wlim) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const int t = lim[rb] - j0 - 4 * hi;
+          const int t = min(lim[rb], khi) - j0 - 4 * hi;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kNegInf;
         }

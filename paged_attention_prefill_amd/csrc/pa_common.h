@@ -166,25 +166,32 @@ __device__ __forceinline__ int seq_by_rank(const AttnParams& p, int r, int* lds,
     if (rank == r) lds[kRankMaxSeqs] = tid;
   }
   __syncthreads();
-  const int seq = lds[kRankMaxSeqs];
+  // the same word in every lane: kept in a scalar register, so that what is
+  // derived from it (the sequence's offsets and lengths) is scalar too
+  const int seq = __builtin_amdgcn_readfirstlane(lds[kRankMaxSeqs]);
   __syncthreads();  // the scratch is free again
   return seq;
 }
 
-// Key range [lo, hi) of part `s` of a row with L keys.  part_keys == 0: S
-// parts of whole kSplitTile-key tiles cut from the row's own length,
-// per = ceil(ceil(L / T) / S) tiles each.  part_keys > 0 (a multiple of T):
-// absolute parts [s * part_keys, (s + 1) * part_keys), the last part (s = S - 1)
-// running on to L, so that the boundaries do not depend on L at all.
-__device__ __forceinline__ void split_range(int L, int S, int s, int part_keys, int& lo, int& hi) {
+// Key range [lo, hi) of part `s` of a sequence with L keys and qlen query
+// tokens.  part_keys == 0: S parts of whole kSplitTile-key tiles cut from the
+// keys the sequence can see, [base, L) with base the tile that holds its first
+// token's window start (0 without a window): per = ceil(ceil((L - base) / T) /
+// S) tiles each, a function of the sequence's own length (and window).
+// part_keys > 0 (a multiple of T): absolute parts [s * part_keys,
+// (s + 1) * part_keys), the last part (s = S - 1) running on to L, so that the
+// boundaries do not depend on L at all.
+__device__ __forceinline__ void split_range(const AttnParams& p, int L, int qlen, int s, int& lo, int& hi) {
+  const int S = p.num_splits;
   long long a, b;
-  if (part_keys > 0) {
-    a = (long long)s * part_keys;
-    b = s == S - 1 ? (long long)L : a + part_keys;
+  if (p.part_keys > 0) {
+    a = (long long)s * p.part_keys;
+    b = s == S - 1 ? (long long)L : a + p.part_keys;
   } else {
-    const int tiles = (L + kSplitTile - 1) / kSplitTile;
+    const int base = p.window_left < 0 ? 0 : (max(0, L - qlen - p.window_left) / kSplitTile) * kSplitTile;
+    const int tiles = (L - base + kSplitTile - 1) / kSplitTile;
     const int per = (tiles + S - 1) / S;
-    a = (long long)s * per * kSplitTile;
+    a = base + (long long)s * per * kSplitTile;
     b = a + (long long)per * kSplitTile;
   }
   lo = (int)(a < L ? a : L);

@@ -17,10 +17,18 @@ KV_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e5m2": 1, "e4m3": 1}
 Q_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
-def attended_pairs(cu_seqlens_q, seq_lens):
-    """Per query head: sum over tokens of max(0, L - Q + i + 1) (closed form per sequence)."""
+def attended_pairs(cu_seqlens_q, seq_lens, window_left=-1):
+    """Per query head: sum over tokens of the visible keys, max(0, L - Q + i + 1)
+    (closed form per sequence), each capped at window_left + 1 under a window."""
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     L = np.asarray(seq_lens, dtype=np.int64)
+    if window_left is not None and window_left >= 0:
+        total = 0
+        for b in range(len(L)):
+            Q = int(cu[b + 1] - cu[b])
+            n = int(L[b]) - Q + 1 + np.arange(Q, dtype=np.int64)
+            total += int(np.minimum(np.maximum(n, 0), window_left + 1).sum())
+        return total
     total = 0
     for b in range(len(L)):
         Q = int(cu[b + 1] - cu[b])
@@ -32,18 +40,23 @@ def attended_pairs(cu_seqlens_q, seq_lens):
     return total
 
 
-def prefill_flops(cu_seqlens_q, seq_lens, num_q_heads, head_dim):
-    return 4 * int(head_dim) * int(num_q_heads) * attended_pairs(cu_seqlens_q, seq_lens)
+def prefill_flops(cu_seqlens_q, seq_lens, num_q_heads, head_dim, window_left=-1):
+    return 4 * int(head_dim) * int(num_q_heads) * attended_pairs(cu_seqlens_q, seq_lens, window_left)
 
 
 def decode_bytes(cu_seqlens_q, seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
-                 q_kind, kv_kind, num_splits):
+                 q_kind, kv_kind, num_splits, window_left=-1):
     L = np.asarray(seq_lens, dtype=np.int64)
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     total_q = int(cu[-1])
-    kv = int(L.sum()) * int(num_kv_heads) * int(head_dim) * 2 * KV_BYTES[kv_kind]
+    if window_left is not None and window_left >= 0:  # keys some token of the row can see
+        Q = np.diff(cu)
+        keys = np.minimum(L, window_left + Q)
+    else:
+        keys = L
+    kv = int(keys.sum()) * int(num_kv_heads) * int(head_dim) * 2 * KV_BYTES[kv_kind]
     qo = 2 * total_q * int(num_q_heads) * int(head_dim) * Q_BYTES[q_kind]
-    bt = int(sum(-(-int(x) // int(page_size)) for x in L)) * 4
+    bt = int(sum(-(-int(x) // int(page_size)) for x in keys)) * 4
     partial = 2 * total_q * int(num_q_heads) * int(num_splits) * (int(head_dim) + 2) * 4
     return kv + qo + bt + partial
 

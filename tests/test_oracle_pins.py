@@ -496,7 +496,7 @@ def test_sink_closed_forms():
                 np.testing.assert_allclose(zl[t, h], np.log(max(n, 0) + np.exp(0.7)), atol=1e-13)
 
 
-@pytest.mark.parametrize("S,window", [(3, 5), (4, 0), (2, 12)])
+@pytest.mark.parametrize("S,window", [(3, 5), (4, 0), (2, 12), (5, 200)])
 def test_window_split_merge_equals_unsplit(S, window):
     case = gen.make_case("wsplit", q_lens=[6], seq_lens=[300], num_q_heads=2, num_kv_heads=1, head_dim=16,
                          page_size=16, q_kind="f32", seed=33)
@@ -507,7 +507,11 @@ def test_window_split_merge_equals_unsplit(S, window):
     counts = oracle.visible_key_count(300, 6, i)
     starts = oracle.window_start(300, 6, i, window)
     o, l = oracle.attention_rows(q, K, V, counts, case.scale, starts=starts)
-    os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S, starts=starts)
-    om, lm = oracle.merge_partials(os_, ls_)
-    np.testing.assert_allclose(om, o, atol=1e-13)
-    np.testing.assert_allclose(lm, l, atol=1e-13)
+    for base in (0, oracle.window_base(300, 6, window)):
+        # parts of [0, L) or of the window range [base, L): both cover every visible key
+        assert base <= starts.min() and base % 32 == 0
+        os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S, starts=starts, base=base)
+        assert oracle.split_ranges(300, S, base=base)[0][0] == base
+        om, lm = oracle.merge_partials(os_, ls_)
+        np.testing.assert_allclose(om, o, atol=1e-13)
+        np.testing.assert_allclose(lm, l, atol=1e-13)
