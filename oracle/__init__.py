@@ -41,6 +41,7 @@ from .attention import (  # noqa: F401
     window_start,
     window_base,
     add_sink,
+    modified_logits,
     attention_rows,
     paged_attention,
     split_ranges,

@@ -93,17 +93,36 @@ def add_sink(o, lse, sink):
     return o * f[..., None], new
 
 
-def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128, starts=None):
+def modified_logits(s, softcap=0.0, slopes=None, dist=None):
+    """Score modifiers on natural-unit logits s = scale * q.k (both readings of
+    variants the pages only name: 1CatAI/1Cat-vLLM PR #1279, commit 1, the
+    Turing selection rule).  softcap > 0: s -> softcap * tanh(s / softcap),
+    which bounds every logit to (-softcap, softcap).  slopes: ALiBi, then
+    s -> s - slope * dist, dist = p - j for the query token at key position p
+    and key j (slopes broadcast against s's rows).  Softcap comes first."""
+    if softcap:
+        s = softcap * np.tanh(s / softcap)
+    if slopes is not None:
+        s = s - np.asarray(slopes, dtype=np.float64).reshape(-1, 1) * dist
+    return s
+
+
+def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128, starts=None,
+                   softcap=0.0, alibi=None):
     """Softmax attention of query rows over a key range.
 
     Row r attends to keys j with max(key_lo, starts[r]) <= j < min(counts[r],
     key_hi, len(K)).  Returns (o [n, D], lse [n]); a row with no key in range
-    gets o = 0 and lse = -inf.
+    gets o = 0 and lse = -inf.  softcap / alibi (a slope per row, or one for
+    all rows): see modified_logits; row r's query token sits at key position
+    counts[r] - 1.
     """
     qrows = np.asarray(qrows, dtype=np.float64)
     counts = np.asarray(counts, dtype=np.int64)
     starts = np.zeros_like(counts) if starts is None else np.asarray(starts, dtype=np.int64)
     n, D = qrows.shape
+    if alibi is not None:
+        alibi = np.broadcast_to(np.asarray(alibi, dtype=np.float64), (n,))
     L = K.shape[0]
     hi = L if key_hi is None else min(int(key_hi), L)
     o = np.zeros((n, D), dtype=np.float64)
@@ -118,6 +137,9 @@ def attention_rows(qrows, K, V, counts, scale, key_lo=0, key_hi=None, block=128,
         Vb = V[key_lo:emax]
         s = scale * (qb @ Kb.T)
         j = np.arange(key_lo, emax)
+        if softcap or alibi is not None:
+            dist = (counts[r0:r0 + block] - 1)[:, None] - j[None, :]
+            s = modified_logits(s, softcap, None if alibi is None else alibi[r0:r0 + block], dist)
         vis = (j[None, :] < end[:, None]) & (j[None, :] >= starts[r0:r0 + block][:, None])
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
@@ -137,7 +159,7 @@ def _token_to_seq(cu):
 
 
 def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, rows=None,
-                    window_left=-1, sinks=None):
+                    window_left=-1, sinks=None, softcap=0.0, alibi_slopes=None):
     """Varlen paged attention in float64.
 
     q            [total_q, Hq, D]
@@ -146,6 +168,9 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
     rows         optional [n, 2] array of (token, q head) pairs to compute.
     window_left  >= 0: token i also needs j >= L - Q + i - window_left (see window_start).
     sinks        optional [Hq] logits, one more term in each head's softmax denominator.
+    softcap      > 0: logits capped by softcap * tanh(logit / softcap) (see modified_logits).
+    alibi_slopes optional [Hq]: head h's logit of key j for the token at key position p
+                 loses alibi_slopes[h] * (p - j).
 
     Returns (out [total_q, Hq, D], lse [total_q, Hq]) or, with ``rows``,
     (out [n, D], lse [n]) in the order given.
@@ -190,7 +215,9 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
                 counts = visible_key_count(Lb, Qb, i)
                 starts = window_start(Lb, Qb, i, window_left)
                 for qh in heads:
-                    o, s = attention_rows(q[t0:t1, qh, :], K, V, counts, scale, starts=starts)
+                    sl = None if alibi_slopes is None else float(alibi_slopes[qh])
+                    o, s = attention_rows(q[t0:t1, qh, :], K, V, counts, scale, starts=starts,
+                                          softcap=softcap, alibi=sl)
                     if sinks is not None:
                         o, s = add_sink(o, s, float(sinks[qh]))
                     out[t0:t1, qh, :] = o
@@ -200,7 +227,8 @@ def paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, sca
                 qrows = q[toks, want[sel, 1], :]
                 counts = visible_key_count(Lb, Qb, toks - t0)
                 starts = window_start(Lb, Qb, toks - t0, window_left)
-                o, s = attention_rows(qrows, K, V, counts, scale, starts=starts)
+                sl = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64)[want[sel, 1]]
+                o, s = attention_rows(qrows, K, V, counts, scale, starts=starts, softcap=softcap, alibi=sl)
                 if sinks is not None:
                     o, s = add_sink(o, s, np.asarray(sinks, dtype=np.float64)[want[sel, 1]])
                 out[sel] = o
@@ -235,12 +263,14 @@ def split_ranges(seq_len, num_splits, tile=SPLIT_TILE, part_keys=0, base=0):
     return [(min(base + s * per * tile, L), min(base + (s + 1) * per * tile, L)) for s in range(num_splits)]
 
 
-def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0, starts=None, base=0):
+def split_partials(qrows, K, V, counts, scale, num_splits, tile=SPLIT_TILE, part_keys=0, starts=None, base=0,
+                   softcap=0.0, alibi=None):
     """Per-part partial states of rows over one sequence: (o_s [S, n, D], lse_s [S, n])."""
     ranges = split_ranges(K.shape[0], num_splits, tile, part_keys, base)
     os_, ls_ = [], []
     for lo, hi in ranges:
-        o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi, starts=starts)
+        o, s = attention_rows(qrows, K, V, counts, scale, key_lo=lo, key_hi=hi, starts=starts,
+                              softcap=softcap, alibi=alibi)
         os_.append(o)
         ls_.append(s)
     return np.stack(os_), np.stack(ls_)

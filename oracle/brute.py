@@ -16,10 +16,12 @@ def _f(x):
 
 
 def brute_paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_tables, scale, window_left=-1,
-                          sinks=None):
+                          sinks=None, softcap=0.0, alibi_slopes=None):
     """q [total_q][Hq][D]; pools [num_pages][page_size][Hkv][D] (float values).
     window_left >= 0: the token at key position p sees keys p - window_left .. p;
-    sinks[h]: a logit with no value added to head h's softmax denominator.
+    sinks[h]: a logit with no value added to head h's softmax denominator;
+    softcap > 0: each logit z becomes softcap * tanh(z / softcap), then
+    alibi_slopes[h]: the logit of key j drops by alibi_slopes[h] * (p - j).
 
     Returns (out, lse) as nested Python lists: out[t][h][d], lse[t][h].
     """
@@ -53,7 +55,12 @@ def brute_paged_attention(q, k_pool, v_pool, cu_seqlens_q, seq_lens, block_table
                     page = int(block_tables[b][j // page_size])
                     slot = j % page_size
                     kj = k_pool[page][slot][kvh]
-                    scores.append(scale * math.fsum(qv[d] * _f(kj[d]) for d in range(D)))
+                    z = scale * math.fsum(qv[d] * _f(kj[d]) for d in range(D))
+                    if softcap:
+                        z = softcap * math.tanh(z / softcap)
+                    if alibi_slopes is not None:
+                        z -= _f(alibi_slopes[h]) * (n_vis - 1 - j)
+                    scores.append(z)
                     vals.append([_f(x) for x in v_pool[page][slot][kvh]])
                 m = max(scores) if sink is None else max(max(scores), sink)
                 w = [math.exp(s - m) for s in scores]

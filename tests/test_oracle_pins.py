@@ -404,11 +404,12 @@ MUTATIONS = {
                           lambda pool, bt, L, h: np.asarray(pool[np.asarray(bt)[np.arange(L) % pool.shape[1] % len(bt)],
                                                                  np.arange(L) // pool.shape[1] % pool.shape[1], h, :], np.float64)),
     "scale_dropped": ("attention_rows",
-                      lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows:
-                      _f(q, K, V, c, 1.0, key_lo, key_hi, block, starts)),
+                      lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows,
+                      **kw: _f(q, K, V, c, 1.0, key_lo, key_hi, block, starts, **kw)),
     "lse_base2": ("attention_rows",
-                  lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows:
-                  (lambda r: (r[0], r[1] / math.log(2)))(_f(q, K, V, c, scale, key_lo, key_hi, block, starts))),
+                  lambda q, K, V, c, scale, key_lo=0, key_hi=None, block=128, starts=None, _f=oa.attention_rows,
+                  **kw: (lambda r: (r[0], r[1] / math.log(2)))(_f(q, K, V, c, scale, key_lo, key_hi, block, starts,
+                                                                   **kw))),
     "merge_unweighted": ("merge_partials",
                          lambda o, l: (np.asarray(o).mean(0), np.asarray(l).max(0))),
 }
@@ -515,3 +516,197 @@ def test_window_split_merge_equals_unsplit(S, window):
         om, lm = oracle.merge_partials(os_, ls_)
         np.testing.assert_allclose(om, o, atol=1e-13)
         np.testing.assert_allclose(lm, l, atol=1e-13)
+
+
+# ---------------------------------------------------------------- softcap and ALiBi
+
+SLOPES6 = [0.5, 0.25, 0.125, 0.0625, 1.0, 0.03125]
+
+
+def _brute_vs_oracle(case, **kw):
+    k, v = _dense(case)
+    o, l = oracle.paged_attention(gen.to_numpy64(case.q), k, v, case.cu_seqlens_q, case.seq_lens,
+                                  case.block_tables, case.scale, **kw)
+    bo, bl = oracle.brute_paged_attention(gen.to_numpy64(case.q).tolist(), k.tolist(), v.tolist(),
+                                          case.cu_seqlens_q.tolist(), case.seq_lens.tolist(),
+                                          case.block_tables.tolist(), case.scale, **kw)
+    bo, bl = np.array(bo), np.array(bl)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert (fin == np.isfinite(l)).all()
+    np.testing.assert_allclose(l[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kw", [dict(softcap=0.8), dict(softcap=5.0), dict(alibi_slopes=SLOPES6),
+                                dict(softcap=1.5, alibi_slopes=SLOPES6),
+                                dict(softcap=2.0, alibi_slopes=SLOPES6, window_left=3, sinks=[0.5] * 6)])
+def test_softcap_and_alibi_match_brute_force(kw):
+    _brute_vs_oracle(small_gqa_case(seed=16, scale=1.5), **kw)
+
+
+def test_softcap_limits():
+    """A cap far above every logit changes nothing (tanh(x) = x - x^3/3 + ...);
+    logits far above (below) the cap all become +cap (-cap): equal weights,
+    o = the mean of the visible values and lse = +-cap + log(n)."""
+    case = small_gqa_case(seed=17)
+    k, v = _dense(case)
+    q = gen.to_numpy64(case.q)
+    args = (case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale)
+    base, bl = oracle.paged_attention(q, k, v, *args)
+    far, fl = oracle.paged_attention(q, k, v, *args, softcap=1e9)
+    np.testing.assert_allclose(far, base, atol=1e-12)
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(fl[fin], bl[fin], atol=1e-12)
+    # every key along +u with a positive length, q = +-big * u
+    u = np.ones(case.head_dim) / np.sqrt(case.head_dim)
+    rng = np.random.default_rng(3)
+    ks = u[None, None, None, :] * rng.uniform(1.0, 2.0, size=k.shape[:3] + (1,))
+    g = case.num_q_heads // case.num_kv_heads
+    for sign in (1.0, -1.0):
+        qs = np.broadcast_to(sign * 1e4 * u, q.shape).copy()
+        o, l = oracle.paged_attention(qs, ks, v, *args, softcap=0.75)
+        for b in range(case.num_seqs):
+            L, Q = int(case.seq_lens[b]), int(case.q_lens[b])
+            for i in range(Q):
+                t, n = int(case.cu_seqlens_q[b]) + i, L - Q + i + 1
+                for h in range(case.num_q_heads):
+                    if n <= 0:
+                        assert l[t, h] == -np.inf
+                        continue
+                    V = oracle.gather_dense_kv(v, case.block_tables[b], L, h // g)[:n]
+                    np.testing.assert_allclose(o[t, h], V.mean(axis=0), atol=1e-13)
+                    np.testing.assert_allclose(l[t, h], sign * 0.75 + np.log(n), atol=1e-13)
+
+
+def _key_index_values(case):
+    """A V pool whose dimension 0 holds the key index j of each (sequence) slot."""
+    v = np.zeros((case.k_pool.shape[0], case.page_size, case.num_kv_heads, case.head_dim))
+    for b in range(case.num_seqs):
+        for j in range(int(case.seq_lens[b])):
+            v[int(case.block_tables[b][j // case.page_size]), j % case.page_size, :, 0] = j
+    return v
+
+
+def test_alibi_closed_form_for_zero_queries():
+    """q = 0: the logits are -slope * d for distances d = 0 .. n-1, so with r =
+    e^-slope the weights are geometric: lse = log((1 - r^n) / (1 - r)) and the
+    mean key index is p - r (1 - n r^(n-1) + (n-1) r^n) / ((1 - r)(1 - r^n))."""
+    case = small_gqa_case(seed=18, seq_lens=[30, 7, 2, 64], q_lens=[5, 1, 3, 4])
+    k, _ = _dense(case)
+    v = _key_index_values(case)
+    q = np.zeros(gen.to_numpy64(case.q).shape)
+    o, l = oracle.paged_attention(q, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale,
+                                  alibi_slopes=SLOPES6)
+    for b in range(case.num_seqs):
+        L, Q = int(case.seq_lens[b]), int(case.q_lens[b])
+        for i in range(Q):
+            t, n = int(case.cu_seqlens_q[b]) + i, L - Q + i + 1
+            p = n - 1
+            for h in range(case.num_q_heads):
+                if n <= 0:  # no visible key
+                    assert l[t, h] == -np.inf and not o[t, h].any()
+                    continue
+                r = math.exp(-SLOPES6[h])
+                geo = (1 - r ** n) / (1 - r)
+                mean_d = r * (1 - n * r ** (n - 1) + (n - 1) * r ** n) / ((1 - r) ** 2 * geo)
+                np.testing.assert_allclose(l[t, h], math.log(geo), rtol=0, atol=1e-13)
+                np.testing.assert_allclose(o[t, h, 0], p - mean_d, rtol=0, atol=1e-11)
+                assert not o[t, h, 1:].any()
+
+
+def test_alibi_equals_plain_attention_with_one_more_dimension():
+    """slope * j is a dot product: with q' = [q, slope / scale] and k'_j = [k_j, j]
+    the plain logits are scale q.k + slope j, which differ from the ALiBi ones by
+    slope * p per row: the same o, and lse shifted by slope * p."""
+    case = small_gqa_case(seed=19, seq_lens=[40, 9, 3, 33])
+    k, v = _dense(case)
+    q = gen.to_numpy64(case.q)
+    o, l = oracle.paged_attention(q, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale,
+                                  alibi_slopes=SLOPES6)
+    kj = _key_index_values(case)[..., :1]
+    k2 = np.concatenate([k, kj], axis=-1)
+    v2 = np.concatenate([v, np.zeros_like(kj)], axis=-1)
+    q2 = np.concatenate([q, np.broadcast_to(np.array(SLOPES6)[None, :, None] / case.scale, q.shape[:2] + (1,))], -1)
+    o2, l2 = oracle.paged_attention(q2, k2, v2, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale)
+    np.testing.assert_allclose(o, o2[..., :-1], atol=1e-12)
+    pos = np.concatenate([int(case.seq_lens[b]) - int(case.q_lens[b]) + np.arange(int(case.q_lens[b]))
+                          for b in range(case.num_seqs)])
+    want = l2 - np.array(SLOPES6)[None, :] * pos[:, None]
+    fin = np.isfinite(l)
+    assert (fin == np.isfinite(want)).all()
+    np.testing.assert_allclose(l[fin], want[fin], atol=1e-11)
+
+
+def test_alibi_matches_torch_sdpa_with_a_bias_matrix():
+    """One sequence, MHA, dense: torch's fp64 scaled_dot_product_attention with an
+    additive mask holding -slope (p - j) on visible keys and -inf elsewhere."""
+    import torch
+    Q, L, H, D = 6, 23, 3, 16
+    case = gen.make_case("alibi_sdpa", q_lens=[Q], seq_lens=[L], num_q_heads=H, num_kv_heads=H, head_dim=D,
+                         page_size=8, q_kind="f32", seed=20)
+    k, v = _dense(case)
+    q = gen.to_numpy64(case.q)
+    slopes = [0.3, 0.05, 1.2]
+    o, l = oracle.paged_attention(q, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale,
+                                  alibi_slopes=slopes)
+    K = np.stack([oracle.gather_dense_kv(k, case.block_tables[0], L, h) for h in range(H)])
+    V = np.stack([oracle.gather_dense_kv(v, case.block_tables[0], L, h) for h in range(H)])
+    p = L - Q + np.arange(Q)
+    j = np.arange(L)
+    dist = p[:, None] - j[None, :]
+    bias = np.where(dist[None] >= 0, -np.array(slopes)[:, None, None] * dist[None], -np.inf)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.transpose(1, 0, 2).copy()), torch.from_numpy(K), torch.from_numpy(V),
+        attn_mask=torch.from_numpy(bias), scale=case.scale).numpy()
+    np.testing.assert_allclose(o, ref.transpose(1, 0, 2), atol=1e-12)
+
+
+@pytest.mark.parametrize("S,window,softcap,slope", [(3, -1, 1.0, 0.2), (4, 7, 0.0, 0.05), (2, -1, 3.0, 0.0),
+                                                    (5, 40, 0.5, 0.7)])
+def test_softcap_alibi_split_merge_equals_unsplit(S, window, softcap, slope):
+    case = gen.make_case("msplit", q_lens=[6], seq_lens=[300], num_q_heads=1, num_kv_heads=1, head_dim=16,
+                         page_size=16, q_kind="f32", seed=34)
+    q = gen.to_numpy64(case.q)[:, 0, :] * 4
+    K = oracle.gather_dense_kv(gen.to_numpy64(case.k_pool), case.block_tables[0], 300, 0)
+    V = oracle.gather_dense_kv(gen.to_numpy64(case.v_pool), case.block_tables[0], 300, 0)
+    i = np.arange(6)
+    counts = oracle.visible_key_count(300, 6, i)
+    starts = oracle.window_start(300, 6, i, window)
+    al = slope if slope else None
+    o, l = oracle.attention_rows(q, K, V, counts, case.scale, starts=starts, softcap=softcap, alibi=al)
+    base = oracle.window_base(300, 6, window)
+    os_, ls_ = oracle.split_partials(q, K, V, counts, case.scale, S, starts=starts, base=base, softcap=softcap,
+                                     alibi=al)
+    om, lm = oracle.merge_partials(os_, ls_)
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, l, atol=1e-13)
+
+
+def _mods_pins_pass():
+    try:
+        test_softcap_and_alibi_match_brute_force(dict(softcap=1.5, alibi_slopes=SLOPES6))
+        test_softcap_limits()
+        test_alibi_closed_form_for_zero_queries()
+        test_alibi_equals_plain_attention_with_one_more_dimension()
+    except AssertionError:
+        return False
+    return True
+
+
+MOD_MUTATIONS = {
+    "softcap_outer_factor_dropped": lambda s, softcap=0.0, slopes=None, dist=None, _f=oa.modified_logits:
+        _f(np.tanh(s / softcap) if softcap else s, 0.0, slopes, dist),
+    "alibi_sign": lambda s, softcap=0.0, slopes=None, dist=None, _f=oa.modified_logits:
+        _f(s, softcap, None if slopes is None else -np.asarray(slopes), dist),
+    "alibi_before_softcap": lambda s, softcap=0.0, slopes=None, dist=None, _f=oa.modified_logits:
+        _f(_f(s, 0.0, slopes, dist), softcap, None, dist),
+    "alibi_distance_off_by_one": lambda s, softcap=0.0, slopes=None, dist=None, _f=oa.modified_logits:
+        _f(s, softcap, slopes, None if dist is None else dist + 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MOD_MUTATIONS))
+def test_planted_score_modifier_mistake_is_caught(name, monkeypatch):
+    assert _mods_pins_pass()
+    monkeypatch.setattr(oa, "modified_logits", MOD_MUTATIONS[name])
+    assert not _mods_pins_pass(), f"mutation {name} survived every pin"
