@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 1
+#define PA_VERSION 2
 #define PA_DECODE_MAX_Q 16       /* largest q of a decode / verify row */
 #define PA_DECODE_SPLIT_TILE 32  /* keys per tile of the split partition */
 #define PA_PREFILL_MAX_AUTO_SPLITS 16
@@ -125,11 +125,23 @@ typedef struct pa_kv_cache {
  *     merge; the FP32 records of pass 1 (out = NULL) stay sink-free.
  *   window_left: < 0 for none; otherwise the token at key position p (p =
  *     seq_len - q_len + i) sees keys p - window_left .. p only.
+ * The same gate lists logit softcapping and ALiBi; the pages define neither,
+ * and these are FlashAttention's conventions, applied to the natural-unit
+ * logit z = scale * q.k of every visible key before the softmax:
+ *   softcap: > 0 (finite): z -> softcap * tanh(z / softcap); 0: none.
+ *   alibi_slopes: device float[num_q_heads] or NULL; for head h, the token
+ *     at key position p and key j <= p: z -> z - alibi_slopes[h] * (p - j)
+ *     (after the softcap).
+ * The score modifiers run in a separate instantiation of each kernel (the
+ * default one is unchanged); tanh is evaluated as 1 - 2 / (1 + e^(2x)) with
+ * the hardware exp2 and reciprocal, so the softcapped logits carry an
+ * absolute error of a few fp32 ulps of softcap.
  */
 typedef struct pa_attn_options {
   const float *sinks;
   int32_t window_left;
-  int32_t reserved;     /* must be 0 */
+  float softcap;
+  const float *alibi_slopes;
 } pa_attn_options;
 
 /*

@@ -29,7 +29,8 @@ using namespace mf;
 // (with one ring stage per wave at D 128: 64 KB of LDS per group): a decode
 // batch has many short parts, and a second resident group hides each part's
 // first-tile latency.
-template <typename QT, int F8, int DPAD, int NSW>
+// MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
+template <typename QT, int F8, int DPAD, int NSW, bool MOD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DPAD <= 128 ? 2 : 1)))
 void attn_decode_kernel(const AttnParams p) {
   constexpr bool KV8 = F8 != 0;
@@ -76,6 +77,7 @@ void attn_decode_kernel(const AttnParams p) {
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
   const int lo = window_lo(p, L - qlen + tok);
+  const float slope = MOD ? alibi_slope_l2(p, hq) : 0.0f;
 
   // Q^T (B operand) over the whole head dimension: k-step kk holds d = 16 kk + 8 hi .. +7
   // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half)
@@ -225,7 +227,9 @@ void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
+      float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
+      if constexpr (MOD)
+        if (v != kNegInf) v = mod_score(p, v, slope, L - qlen + tok - key);
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -333,7 +337,10 @@ void attn_decode_kernel(const AttnParams p) {
 namespace {
 template <typename QT, int F8, int DPAD, int NSW>
 hipError_t launch_dec(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<QT, F8, DPAD, NSW>), dim3(nblocks), dim3(256), 0, stream, p);
+  if (has_score_mods(p))
+    hipLaunchKernelGGL((attn_decode_kernel<QT, F8, DPAD, NSW, true>), dim3(nblocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<QT, F8, DPAD, NSW, false>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 template <typename QT>

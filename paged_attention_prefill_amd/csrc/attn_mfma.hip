@@ -94,7 +94,8 @@ __device__ __forceinline__ int vt_pos(int quad) {
 
 }  // namespace
 
-template <typename QT, int KVK, int DPAD>
+// MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
+template <typename QT, int KVK, int DPAD, bool MOD = false>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p) {
   constexpr int KS = DPAD + 8;     // K row stride in LDS (16-bit elements)
   constexpr int VS = kKT + 8;      // transposed V row stride
@@ -137,6 +138,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
   const int hq = kvh * g + (valid ? prow - (prow / g) * g : 0);
   const int lim = valid ? min(L - qlen + tok + 1, khi) : 0;
   const int lo = window_lo(p, L - qlen + tok);
+  const float slope = MOD ? alibi_slope_l2(p, hq) : 0.0f;
   const int last_tok = (min(row0 + kRows, nrows) - 1) / g;
   const int kend = min(khi, L - qlen + last_tok + 1);
   const int wrow_first = row0 + wave * 32;
@@ -239,7 +241,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
+      float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
+      if constexpr (MOD)
+        if (v != kNegInf) v = mod_score(p, v, slope, L - qlen + tok - key);
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -331,7 +335,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 
 template <typename QT, int KVK, int DPAD>
 static hipError_t launch_t(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_mfma_kernel<QT, KVK, DPAD>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  // the calls routed here: fp8 KV at head dims up to 128
+  constexpr bool kModVariant = (KVK == KV_E5M2 || KVK == KV_E4M3) && DPAD <= 128;
+  if (has_score_mods(p)) {
+    if constexpr (!kModVariant) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((attn_mfma_kernel<QT, KVK, DPAD, true>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_mfma_kernel<QT, KVK, DPAD, false>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

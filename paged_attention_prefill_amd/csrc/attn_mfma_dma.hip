@@ -27,7 +27,8 @@ namespace pa {
 
 using namespace mf;
 
-template <typename QT, int DPAD, int WAVES, int RB, int NST>
+// MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
+template <typename QT, int DPAD, int WAVES, int RB, int NST, bool MOD = false>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void attn_mfma_dma_kernel(
     const AttnParams p) {
   constexpr int WROWS = 32 * RB;                // query rows per wave (RB blocks of 32)
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   // lane holds row r32 of each block, d = 16 kk + 8 hi .. +7
   bool valid[RB], rb_on[RB];
   int tok[RB], hq[RB], lim[RB], lo[RB];
+  float slope[RB];
   uint4 qf[RB][NKK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     hq[rb] = kvh * g + (valid[rb] ? prow - (prow / g) * g : 0);
     lim[rb] = valid[rb] ? min(L - qlen + tok[rb] + 1, khi) : 0;
     lo[rb] = window_lo(p, L - qlen + tok[rb]);
+    if constexpr (MOD) slope[rb] = alibi_slope_l2(p, hq[rb]);
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok[rb]) * p.num_q_heads + hq[rb]) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -144,7 +147,17 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float tmax = kNegInf;
-      if (__any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
+      if constexpr (MOD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          float v = kNegInf;
+          if (key < lim[rb] && key >= lo[rb])
+            v = mod_score(p, s[rb][r] * score_scale, slope[rb], L - qlen + tok[rb] - key);
+          s[rb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      } else if (__any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -282,8 +295,12 @@ namespace {
 template <typename QT, int DPAD, int WAVES, int RB, int NST>
 struct Cfg {
   static hipError_t launch(const AttnParams& p, int nblocks, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST>), dim3(nblocks), dim3(64 * WAVES), 0, stream,
-                       p);
+    if (has_score_mods(p))
+      hipLaunchKernelGGL((attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST, true>), dim3(nblocks), dim3(64 * WAVES), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((attn_mfma_dma_kernel<QT, DPAD, WAVES, RB, NST, false>), dim3(nblocks), dim3(64 * WAVES), 0,
+                         stream, p);
     return hipGetLastError();
   }
   static hipError_t occ(int* n) {

@@ -90,11 +90,14 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 // F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16); the tiles stay 8-bit in
 // LDS and are widened to fp16 as their MFMA operands are read.  F8 = 0: KV of
 // the q dtype.
-// WIN: a left sliding window is set (a separate instantiation, so that the
-// default one keeps no per-row window state in this tightly scheduled loop).
-template <typename QT, int F8, int DPAD, int NST, bool WIN>
+// VAR 0: no options that touch the scores; 1: a left sliding window; 2: score
+// modifiers (softcap / ALiBi, mod_score), with or without a window.  Each is
+// its own instantiation, so that the default one keeps no per-row state in
+// this tightly scheduled loop.
+template <typename QT, int F8, int DPAD, int NST, int VAR>
 __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParams p) {
   constexpr bool KV8 = F8 != 0;
+  constexpr bool WIN = VAR >= 1, MOD = VAR == 2;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
   typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
   constexpr int ROWB = TL::ROWB;
@@ -189,7 +192,16 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   const uint32_t vlane = KV8 ? TILE_BYTES + (8 * (kr >> 2) + 4 * (tg >> 1) + (kr & 3)) * ROWB + 16 * (tg & 1) +
                                    8 * (tk & 1) + 32 * kr
                               : TILE_BYTES + vkey * ROWB + 16 * vcl + 8 * (tk & 1) + 16 * sv;
-  const float c = score_scale;
+  // the modifier pass leaves the scores in log2 units
+  const float c = MOD ? 1.0f : score_scale;
+  // window of the per-element mask (the modifier instantiation also runs without one)
+  const int wleft = (MOD && p.window_left < 0) ? (1 << 30) : p.window_left;
+  float slope[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int prow = wrow0 + rb * 32 + r32;
+    slope[rb] = MOD ? alibi_slope_l2(p, kvh * g + (prow < nrows ? prow % g : 0)) : 0.0f;
+  }
 
   f32x16_t s[RB];
   uint4 pcur[RB][2], pnew[RB][2];
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
-          const int t = min(lim[rb], khi) - j0 - 4 * hi, u = lim[rb] - 1 - p.window_left - j0 - 4 * hi;
+          const int t = min(lim[rb], khi) - j0 - 4 * hi, u = lim[rb] - 1 - wleft - j0 - 4 * hi;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
@@ -260,6 +272,21 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
         }
       }
     }
+  };
+
+  // Score modifiers of the tile starting at key j0, before its mask: scaled
+  // score -> mod_score, with the distance from the row's own key position
+  // (lim - 1; rows past the end are masked afterwards).
+  auto mod_mask = [&](int j0) {
+    if constexpr (MOD) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int d0 = lim[rb] - 1 - j0 - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[rb][r] = mod_score(p, s[rb][r] * score_scale, slope[rb], d0 - (8 * (r >> 2) + (r & 3)));
+      }
+    }
+    mask_scores(j0);
   };
 
   // Online softmax of the (masked) scores in `s` -> pnew, cut into kSmSteps
@@ -405,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     wait_tiles<LPW, DIST - 1>(issued - 1);
     lds_barrier();
     qk_issue(0);
-    mask_scores(kfirst);
+    mod_mask(kfirst);
     softmax();
     if (issued < ntiles) tl.fetch(issued);
     // alpha of the first tile multiplies zero accumulators: nothing to rescale
@@ -420,7 +447,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
       lds_barrier();
       const int j0 = kfirst + it * kKT;
       qk_issue(it % NST);
-      mask_scores(j0);
+      mod_mask(j0);
       pv_softmax((it - 1) % NST);
       rescale();
       if (issued < ntiles) tl.fetch(issued);
@@ -487,10 +514,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 namespace {
 template <typename QT, int F8, int DPAD, int NST>
 hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
-  if (p.window_left >= 0)
-    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, true>), dim3(nblocks), dim3(256), 0, stream, p);
+  if (has_score_mods(p))
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 2>), dim3(nblocks), dim3(256), 0, stream, p);
+  else if (p.window_left >= 0)
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 1>), dim3(nblocks), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, false>), dim3(nblocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 0>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -512,7 +541,7 @@ hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
   if (dpad == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5, false>, 256, 0);
+                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5, 0>, 256, 0);
   return hipErrorInvalidValue;
 }
 

@@ -76,7 +76,8 @@ __device__ __forceinline__ float wave_sum32(float v) {
 
 }  // namespace
 
-template <typename QT, int KVK, int DPAD>
+// MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
+template <typename QT, int KVK, int DPAD, bool MOD>
 __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p) {
   constexpr int KF = DPAD + 1;         // fp32 K row stride in LDS
   constexpr int NC = DPAD / 64;        // output columns per lane
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 
   // this wave's 4 rows
   int lim[4], lo[4], rowtok[4], rowhq[4];
+  float slope[4];
   bool rvalid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
     rowhq[i] = kvh * g + (rvalid[i] ? prow % g : 0);
     lim[i] = rvalid[i] ? min(L - qlen + rowtok[i] + 1, khi) : 0;
     lo[i] = window_lo(p, L - qlen + rowtok[i]);
+    slope[i] = MOD ? alibi_slope_l2(p, rowhq[i]) : 0.0f;
   }
   float m[4], l[4], o[4][NC];
 #pragma unroll
@@ -172,7 +175,9 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 #pragma unroll 8
       for (int d = 0; d < HALF; ++d) dot = fmaf(qr[d], kr[d], dot);
       dot += __shfl_xor(dot, 32);
-      const float s = (j0 + key < lim[i] && j0 + key >= lo[i]) ? dot * score_scale : kNegInfV;
+      float s = (j0 + key < lim[i] && j0 + key >= lo[i]) ? dot * score_scale : kNegInfV;
+      if constexpr (MOD)
+        if (s != kNegInfV) s = mod_score(p, s, slope[i], L - qlen + rowtok[i] - (j0 + key));
       const float tmax = wave_max32(s);
       const float mnew = fmaxf(m[i], tmax);
       const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m[i] - mnew);
@@ -226,7 +231,10 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
 
 template <typename QT, int KVK, int DPAD>
 static hipError_t launch_v(const AttnParams& p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_valu_kernel<QT, KVK, DPAD>), dim3(nblocks), dim3(kThreadsV), 0, stream, p);
+  if (has_score_mods(p))
+    hipLaunchKernelGGL((attn_valu_kernel<QT, KVK, DPAD, true>), dim3(nblocks), dim3(kThreadsV), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_valu_kernel<QT, KVK, DPAD, false>), dim3(nblocks), dim3(kThreadsV), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ struct AttnParams {
   const float* v_head_scale;  // [Hkv] or null
   const float* sinks;         // [Hq] or null: one more logit per q head in the softmax denominator
   int window_left;            // < 0: none; the token at key p sees keys >= p - window_left
+  float softcap_k2;           // 2 / softcap (0: no softcap)
+  float softcap_l2;           // softcap * log2(e)
+  const float* alibi_slopes;  // [Hq] or null (natural units per key of distance)
 };
 
 // First key visible to the token at key position `pos` under the left window.
@@ -199,6 +202,28 @@ __device__ __forceinline__ void split_range(const AttnParams& p, int L, int qlen
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ALiBi slope of q head hq in the kernels' log2 units (0 without ALiBi).
+__device__ __forceinline__ float alibi_slope_l2(const AttnParams& p, int hq) {
+  return p.alibi_slopes == nullptr ? 0.0f : p.alibi_slopes[hq] * 1.4426950408889634f;
+}
+
+// Score modifiers on a scaled score t = log2(e) * z of a visible key (z = the
+// natural-unit logit).  Softcap z -> c tanh(z / c) is t -> c' tanh(t / c')
+// with c' = c log2(e), and tanh(y) = 1 - 2 / (1 + e^(2y)), where e^(2 t / c') =
+// 2^(2 t / c): one exp2 and one reciprocal (the limits come out exact: 2^x
+// overflowing to inf gives 1, underflowing to 0 gives -1).  Then ALiBi: t
+// loses slope_l2 * dist, dist = p - j for the token at key position p.
+__device__ __forceinline__ float mod_score(const AttnParams& p, float t, float slope_l2, int dist) {
+  if (p.softcap_k2 != 0.0f) {
+    const float e = fast_exp2(t * p.softcap_k2);
+    t = p.softcap_l2 * __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+  }
+  return __builtin_fmaf(-slope_l2, (float)dist, t);
+}
+
+// Whether a call carries score modifiers (they select the kernels' MOD instantiations).
+inline bool has_score_mods(const AttnParams& p) { return p.softcap_k2 != 0.0f || p.alibi_slopes != nullptr; }
 
 // Two fp8 E4M3 bytes (byte 2 w and 2 w + 1 of x) -> two fp16 in one 32-bit
 // word, lower byte in the lower half: the gfx950 conversion with a scale of 1

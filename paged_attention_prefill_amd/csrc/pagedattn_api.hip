@@ -345,6 +345,10 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.v_head_scale = kv->v_head_scales;
   p.sinks = opts ? opts->sinks : nullptr;
   p.window_left = opts ? opts->window_left : -1;
+  const float cap = opts ? opts->softcap : 0.0f;
+  p.softcap_k2 = cap > 0.0f ? 2.0f / cap : 0.0f;
+  p.softcap_l2 = cap * 1.4426950408889634f;
+  p.alibi_slopes = opts ? opts->alibi_slopes : nullptr;
 
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
   hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
@@ -365,8 +369,10 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
 
 static int check_options(const pa_attn_options* opts) {
   if (opts == nullptr) return PA_OK;
-  if (opts->reserved != 0) return fail(PA_ERR_INVALID_ARGUMENT, "pa_attn_options.reserved must be 0");
   if ((uintptr_t)opts->sinks & 3u) return fail(PA_ERR_INVALID_ARGUMENT, "sinks must be 4-byte aligned");
+  if (!std::isfinite(opts->softcap) || opts->softcap < 0.0f)
+    return fail(PA_ERR_INVALID_ARGUMENT, "softcap must be 0 (none) or positive and finite");
+  if ((uintptr_t)opts->alibi_slopes & 3u) return fail(PA_ERR_INVALID_ARGUMENT, "alibi_slopes must be 4-byte aligned");
   return PA_OK;
 }
 

@@ -35,7 +35,8 @@ class PagedAttentionError(RuntimeError):
 
 
 class AttnOptions(ctypes.Structure):
-    _fields_ = [("sinks", ctypes.c_void_p), ("window_left", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+    _fields_ = [("sinks", ctypes.c_void_p), ("window_left", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p)]
 
 
 class KvCache(ctypes.Structure):
@@ -52,6 +53,9 @@ _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SZ = ctypes.c_size_t
+
+
+ABI_VERSION = 2  # PA_VERSION of include/pagedattn.h
 
 
 def lib():
@@ -87,6 +91,9 @@ def lib():
             if name != "pa_status_string":
                 getattr(L, name).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
+        if L.pa_version() != ABI_VERSION:  # the option struct's layout is tied to the version
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.pa_version()}, this binding expects {ABI_VERSION}: "
+                               "rebuild it with `python -m paged_attention_prefill_amd.build`")
         _lib = L
     return _lib
 
@@ -153,13 +160,15 @@ def _i32(t, name):
     return t
 
 
-def _options(sinks, window_left):
-    """pa_attn_options for the *_ex calls, or None when neither is set."""
-    if sinks is None and (window_left is None or window_left < 0):
+def _options(num_q_heads, sinks, window_left, softcap=0.0, alibi_slopes=None):
+    """pa_attn_options for the *_ex calls, or None when nothing is set."""
+    if sinks is None and (window_left is None or window_left < 0) and not softcap and alibi_slopes is None:
         return None
-    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
-        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "sinks must be a contiguous float32 [Hq] tensor")
-    o = AttnOptions(None if sinks is None else sinks.data_ptr(), -1 if window_left is None else int(window_left), 0)
+    for t, name in ((sinks, "sinks"), (alibi_slopes, "alibi_slopes")):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != num_q_heads):
+            raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous float32 [Hq] tensor")
+    o = AttnOptions(None if sinks is None else sinks.data_ptr(), -1 if window_left is None else int(window_left),
+                    float(softcap or 0.0), None if alibi_slopes is None else alibi_slopes.data_ptr())
     return ctypes.byref(o), o  # keep the struct alive with the reference
 
 
@@ -187,9 +196,10 @@ def _partials_view(workspace, total_q, Hq, D, splits):
 def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_seqlen_q, scale,
                   *, k_scale=1.0, v_scale=1.0, num_kv_splits=1, out=None, lse=None,
                   return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
-                  v_head_scales=None, sinks=None, window_left=-1):
+                  v_head_scales=None, sinks=None, window_left=-1, softcap=0.0, alibi_slopes=None):
     """pa_paged_prefill(_ex) on torch tensors; returns out (and lse).
-    sinks (float32 [Hq] on the device) and window_left select the options.
+    sinks and alibi_slopes (float32 [Hq] on the device), window_left and
+    softcap select the options.
 
     merge=False (num_kv_splits >= 2): runs the first pass only and returns the
     FP32 records [total_q, Hq, num_kv_splits, D + 2] for merge_states."""
@@ -207,7 +217,7 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
     ws_bytes = prefill_workspace_bytes(total_q, Hq, D, num_kv_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    opts = _options(sinks, window_left)
+    opts = _options(Hq, sinks, window_left, softcap, alibi_slopes)
     _check(lib().pa_paged_prefill_ex(_ptr(q), _dtype(q), _ptr(out), _ptr(lse),
                                      _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")), _ptr(_i32(seq_lens, "seq_lens")),
                                      _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
@@ -222,7 +232,7 @@ def paged_prefill(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max
 def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale,
                     *, num_splits=16, part_keys=0, k_scale=1.0, v_scale=1.0, out=None, lse=None,
                     return_lse=False, workspace=None, stream=None, merge=True, k_head_scales=None,
-                    v_head_scales=None, sinks=None, window_left=-1):
+                    v_head_scales=None, sinks=None, window_left=-1, softcap=0.0, alibi_slopes=None):
     """pa_split_kv_decode on torch tensors; returns out (and lse).
 
     part_keys > 0: pa_split_kv_decode_fixed, num_splits absolute parts of
@@ -246,7 +256,7 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     args = (_ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
             _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B, block_tables.shape[-1],
             total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale))
-    opts = _options(sinks, window_left)
+    opts = _options(Hq, sinks, window_left, softcap, alibi_slopes)
     _check(lib().pa_split_kv_decode_ex(*args, int(num_splits), int(part_keys), opts[0] if opts else None,
                                        _ptr(workspace), ws_have, _stream(stream)))
     if not merge:

@@ -22,7 +22,7 @@ def test_every_declared_symbol_is_exported():
     assert "pa_paged_prefill" in names and "pa_split_kv_decode" in names and "pa_merge_states" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_version() == 1
+    assert L.pa_version() == 2
 
 
 def test_status_strings():
@@ -202,18 +202,19 @@ def test_out_null_needs_split_and_no_lse():
 def test_options_are_checked_before_launch():
     L = ops.lib()
     kv = _fake_kv()
-    bad = ops.AttnOptions(None, 10, 1)
-    st = L.pa_paged_prefill_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 2, 4, 10, 8, 8,
-                               ctypes.byref(kv), 0.1, 1, ctypes.byref(bad), None, 0, None)
-    assert st == ops.PA_ERR_INVALID_ARGUMENT
-    mis = ops.AttnOptions(0x1002, -1, 0)
+    for bad in (ops.AttnOptions(None, 10, -1.0, None), ops.AttnOptions(None, 10, float("inf"), None),
+                ops.AttnOptions(None, 10, float("nan"), None), ops.AttnOptions(None, -1, 0.0, 0x1001)):
+        st = L.pa_paged_prefill_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 2, 4, 10, 8, 8,
+                                   ctypes.byref(kv), 0.1, 1, ctypes.byref(bad), None, 0, None)
+        assert st == ops.PA_ERR_INVALID_ARGUMENT
+    mis = ops.AttnOptions(0x1002, -1, 0.0, None)
     st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
                                  ctypes.byref(kv), 0.1, 8, 0, ctypes.byref(mis), None, 0, None)
     assert st == ops.PA_ERR_INVALID_ARGUMENT
     st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
                                  ctypes.byref(kv), 0.1, 8, 48, None, None, 0, None)
     assert st == ops.PA_ERR_INVALID_ARGUMENT  # part_keys not a multiple of 32
-    ok = ops.AttnOptions(0x1000, 5, 0)
+    ok = ops.AttnOptions(0x1000, 5, 30.0, 0x2000)
     st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
                                  ctypes.byref(kv), 0.1, 8, 0, ctypes.byref(ok), None, 0, None)
     assert st == ops.PA_ERR_WORKSPACE  # accepted up to the workspace check

@@ -677,3 +677,77 @@ def test_window_verify_row_equals_serial_decode_bitwise():
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(bits(outs[0][:5]), bits(outs[1]))
+
+
+# ------------------------------------------------------------------ softcap and ALiBi
+
+MOD_CASES = [
+    # (q dtype, KV dtype, D, Hq, Hkv, page, softcap, with ALiBi, window_left, with sinks)
+    ("f32", "f32", 64, 4, 2, 16, 5.0, True, -1, False),
+    ("bf16", "bf16", 128, 8, 2, 32, 0.0, True, 37, True),
+    ("f16", "f16", 64, 4, 4, 16, 2.0, False, -1, False),
+    ("f16", "f16", 256, 12, 2, 64, 3.0, True, -1, True),
+    ("bf16", "bf16", 256, 6, 1, 48, 0.0, True, 300, False),
+    ("f16", "e5m2", 128, 8, 2, 16, 4.0, True, 64, False),
+    ("f16", "e4m3", 256, 8, 2, 64, 1.5, True, -1, True),
+    ("f16", "e5m2", 256, 8, 2, 64, 10.0, False, 129, False),
+]
+
+
+def alibi_slopes(H):
+    """The geometric ALiBi slopes 2^(-8 (h + 1) / H)."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
+@pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,softcap,with_alibi,window,with_sinks", MOD_CASES)
+def test_softcap_and_alibi(qk, kvk, D, Hq, Hkv, P, softcap, with_alibi, window, with_sinks):
+    """Softcap and ALiBi (with windows and sinks in some cases) against the
+    oracle on every kernel: prefill with 1 and 3 parts, decode with
+    proportional and absolute parts."""
+    c = gen.make_case(f"mod_{qk}_{kvk}_D{D}", q_lens=[150, 1, 5, 40], seq_lens=[900, 700, 1300, 30],
+                      num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, q_kind=qk, kv_kind=kvk,
+                      seed=7 * D + Hq)
+    rng = np.random.default_rng(D + Hq)
+    sinks = rng.normal(size=Hq).astype(np.float32) if with_sinks else None
+    slopes = alibi_slopes(Hq) if with_alibi else None
+    k, v = oracle_pools(c)
+    ref, rl = oracle.paged_attention(gen.to_numpy64(c.q), k, v, c.cu_seqlens_q, c.seq_lens, c.block_tables,
+                                     c.scale, window_left=window, sinks=sinks, softcap=softcap, alibi_slopes=slopes)
+    d = gen.to_device(c)
+    sk = None if sinks is None else torch.from_numpy(sinks).cuda()
+    al = None if slopes is None else torch.from_numpy(slopes).cuda()
+    kind = kvk if kvk in ("e5m2", "e4m3") else qk
+    mods = dict(sinks=sk, window_left=window, softcap=softcap, alibi_slopes=al)
+    for splits in (1, 3):
+        say(f"  softcap {softcap} alibi {with_alibi} window {window}: prefill S={splits}")
+        out, lse = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
+                                     c.scale, num_kv_splits=splits, return_lse=True, **mods)
+        torch.cuda.synchronize()
+        compare(f"modified prefill S={splits}", kind, out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
+    dec = gen.select_seqs(c, [1, 2])
+    dd = gen.to_device(dec)
+    for part_keys, parts in ((0, 8), (128, 12)):
+        say(f"  softcap {softcap} alibi {with_alibi} window {window}: decode part_keys={part_keys}")
+        out, lse = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 5, c.scale,
+                                       num_splits=parts, part_keys=part_keys, return_lse=True, **mods)
+        torch.cuda.synchronize()
+        compare(f"modified decode C={part_keys}", kind, out.float().cpu().numpy(), ref[150:156], lse.cpu().numpy(),
+                rl[150:156])
+
+
+def test_modified_verify_row_equals_serial_decode_bitwise():
+    """Softcap and ALiBi are per-score functions of the row's own key position:
+    with absolute parts a verify row still has the bits of its token-wise
+    expansion."""
+    case = gen.make_case("verify_mod", q_lens=[5, 1], seq_lens=[3000, 900], num_q_heads=24, num_kv_heads=4,
+                         head_dim=256, page_size=816, q_kind="f16", seed=84)
+    ser = gen.expand_row(case, 0)
+    al = torch.from_numpy(alibi_slopes(24)).cuda()
+    d, ds = gen.to_device(case), gen.to_device(ser)
+    outs = []
+    for c, dd, parts, mq in ((case, d, 10, 5), (ser, ds, 6, 1)):
+        out = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], mq, c.scale,
+                                  num_splits=parts, part_keys=512, softcap=20.0, alibi_slopes=al)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(outs[0][:5]), bits(outs[1]))
