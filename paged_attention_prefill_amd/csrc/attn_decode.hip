@@ -224,12 +224,15 @@ void attn_decode_kernel(const AttnParams p) {
     }
 
     float tmax = kNegInf;
+    if constexpr (MOD) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] *= score_scale;
+      mod_scores16(p, s, slope, L - qlen + tok - j0 - 4 * hi);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      float v = (key < lim && key >= lo) ? s[r] * score_scale : kNegInf;
-      if constexpr (MOD)
-        if (v != kNegInf) v = mod_score(p, v, slope, L - qlen + tok - key);
+      const float v = (key < lim && key >= lo) ? (MOD ? s[r] : s[r] * score_scale) : kNegInf;
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }

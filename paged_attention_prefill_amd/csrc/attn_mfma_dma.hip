@@ -149,11 +149,12 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
       float tmax = kNegInf;
       if constexpr (MOD) {
 #pragma unroll
+        for (int r = 0; r < 16; ++r) s[rb][r] *= score_scale;
+        mod_scores16(p, s[rb], slope[rb], L - qlen + tok[rb] - j0 - 4 * hi);
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          float v = kNegInf;
-          if (key < lim[rb] && key >= lo[rb])
-            v = mod_score(p, s[rb][r] * score_scale, slope[rb], L - qlen + tok[rb] - key);
+          const float v = (key < lim[rb] && key >= lo[rb]) ? s[rb][r] : kNegInf;
           s[rb][r] = v;
           tmax = fmaxf(tmax, v);
         }

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   constexpr bool KV8 = F8 != 0;
   constexpr bool WIN = VAR >= 1, MOD = VAR == 2;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
-  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2> TL;
+  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2, false, VAR == 2> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
@@ -177,8 +177,15 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   }
 
   const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
+  // The modifier instantiation runs the tiles from the last one down: under
+  // ALiBi a row's biased scores grow with the key, so in ascending order its
+  // running max would rise by up to slope * 32 every tile and rescale the
+  // accumulators each time; from the nearest keys down the max is set by the
+  // first tile.
+  const int kstart = MOD && ntiles > 0 ? kfirst + (ntiles - 1) * kKT : kfirst;
+  const int kstep = MOD ? -kKT : kKT;
   TL tl;
-  tl.init(p, seq, kvh, wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  tl.init(p, seq, kvh, wave, lane, kstart, kend, (uint32_t)(uintptr_t)(&smem[0]));
 
   const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
@@ -277,14 +284,15 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
   // Score modifiers of the tile starting at key j0, before its mask: scaled
   // score -> mod_score, with the distance from the row's own key position
   // (lim - 1; rows past the end are masked afterwards).
+  // Each modifier is tested once per tile (wave-uniform branches).
   auto mod_mask = [&](int j0) {
     if constexpr (MOD) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int d0 = lim[rb] - 1 - j0 - 4 * hi;
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[rb][r] = mod_score(p, s[rb][r] * score_scale, slope[rb], d0 - (8 * (r >> 2) + (r & 3)));
-      }
+        for (int r = 0; r < 16; ++r) s[rb][r] *= score_scale;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mod_scores16(p, s[rb], slope[rb], lim[rb] - 1 - j0 - 4 * hi);
     }
     mask_scores(j0);
   };
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     wait_tiles<LPW, DIST - 1>(issued - 1);
     lds_barrier();
     qk_issue(0);
-    mod_mask(kfirst);
+    mod_mask(kstart);
     softmax();
     if (issued < ntiles) tl.fetch(issued);
     // alpha of the first tile multiplies zero accumulators: nothing to rescale
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
     for (int it = 1; it < ntiles; ++it) {
       wait_tiles<LPW, DIST - 1>(issued - it - 1);
       lds_barrier();
-      const int j0 = kfirst + it * kKT;
+      const int j0 = kstart + it * kstep;
       qk_issue(it % NST);
       mod_mask(j0);
       pv_softmax((it - 1) % NST);

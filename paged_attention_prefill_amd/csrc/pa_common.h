@@ -222,6 +222,29 @@ __device__ __forceinline__ float mod_score(const AttnParams& p, float t, float s
   return __builtin_fmaf(-slope_l2, (float)dist, t);
 }
 
+// The two modifiers one at a time, for loops that test each flag once per tile.
+__device__ __forceinline__ float softcap_score(const AttnParams& p, float t) {
+  const float e = fast_exp2(t * p.softcap_k2);
+  return p.softcap_l2 * __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+}
+
+// Softcap then ALiBi on the 16 scaled scores of one lane of a 32x32 MFMA
+// score tile (element r: key 8 (r / 4) + r % 4 after the lane's first key,
+// whose distance from the row's key position is d0).  Each modifier is tested
+// once per fragment; masked elements are selected away afterwards.
+template <typename V16>
+__device__ __forceinline__ void mod_scores16(const AttnParams& p, V16& s, float slope_l2, int d0) {
+  if (p.softcap_k2 != 0.0f) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = softcap_score(p, s[r]);
+  }
+  if (p.alibi_slopes != nullptr) {
+    const float a = -slope_l2 * (float)d0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += __builtin_fmaf(slope_l2, (float)(8 * (r >> 2) + (r & 3)), a);
+  }
+}
+
 // Whether a call carries score modifiers (they select the kernels' MOD instantiations).
 inline bool has_score_mods(const AttnParams& p) { return p.softcap_k2 != 0.0f || p.alibi_slopes != nullptr; }
 

@@ -228,7 +228,8 @@ __device__ __forceinline__ uint4 read_vt8(const char* a) {
 // fetch(it) reads the tile's page ids (scalar loads), begin(stage) forms its
 // page bases, part<FAST>(n) issues DMA instruction n of this wave.  FAST may
 // be used when fast() holds (one page, every key inside the range).
-template <int DPAD, int WAVES, int ES = 2, bool NT = false>
+// DESC: tiles are fetched in descending key order (a negative stride).
+template <int DPAD, int WAVES, int ES = 2, bool NT = false, bool DESC = false>
 struct TileLoader {
   static_assert(ES == 2 || (ES == 1 && DPAD == 256), "8-bit KV tiles are laid out for D 256");
   static constexpr int CPK = DPAD * ES / 16;
@@ -272,7 +273,7 @@ struct TileLoader {
     nx_pg = __builtin_amdgcn_readfirstlane(klo / P);
     nx_off = __builtin_amdgcn_readfirstlane(klo - nx_pg * P);
     nx_key = klo;
-    kstep = kKT;
+    kstep = DESC ? -kKT : kKT;
     lkey = lane_ / CPK;
     const int lpos = lane_ % CPK, dchunks = (p.head_dim * ES) >> 4;
 #pragma unroll
@@ -289,7 +290,8 @@ struct TileLoader {
     }
   }
 
-  // Tiles are fetched every `step` keys from klo (a multiple of 32; kKT unless set).
+  // Tiles are fetched every `step` keys from klo (a multiple of 32, negative
+  // with DESC; kKT unless set, -kKT with DESC).
   __device__ __forceinline__ void set_stride(int step) { kstep = step; }
 
   // Reads the page ids of the next tile (keys klo + step * it ...); calls come in tile order.
@@ -300,7 +302,11 @@ struct TileLoader {
     const int pg = nx_pg;
     f_off = nx_off;
     nx_off += kstep;
-    while (nx_off >= P) nx_off -= P, ++nx_pg;
+    if constexpr (DESC) {
+      while (nx_off < 0) nx_off += P, --nx_pg;
+    } else {
+      while (nx_off >= P) nx_off -= P, ++nx_pg;
+    }
     f_first = P - f_off;  // keys of the tile on the first page (a multiple of 16)
     // both ids are loaded without a branch on the first (the second page's id
     // is only used when the tile reaches it; otherwise the first is re-read),
