@@ -73,7 +73,10 @@ class Call:
 
     def __init__(self, kind, case, d, splits, max_q=None):
         self.kind, self.case, self.d, self.splits = kind, case, d, splits
-        self.window = case.meta.get("window_left", -1)
+        # the case's attention options (sliding window, softcap, ALiBi slopes)
+        self.opts = dict(window_left=case.meta.get("window_left", -1), softcap=case.meta.get("softcap", 0.0))
+        if case.meta.get("alibi"):
+            self.opts["alibi_slopes"] = torch.from_numpy(gen.geometric_alibi_slopes(case.num_q_heads)).to(d["q"].device)
         self.max_q = max_q or max(1, case.max_seqlen_q)
         self.out = torch.empty_like(d["q"])
         self.lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
@@ -96,7 +99,7 @@ class Call:
             # the two passes apart, so that the attention kernel is timed alone
             parts = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
                                       c.scale, k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits,
-                                      workspace=self.ws, stream=stream, merge=False, window_left=self.window)
+                                      workspace=self.ws, stream=stream, merge=False, **self.opts)
             if record:
                 em = torch.cuda.Event(enable_timing=True)
                 em.record(stream)
@@ -105,11 +108,11 @@ class Call:
         elif self.kind == "prefill":
             ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q, c.scale,
                               k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits, out=self.out,
-                              lse=self.lse, workspace=self.ws, stream=stream, window_left=self.window)
+                              lse=self.lse, workspace=self.ws, stream=stream, **self.opts)
         else:
             ops.split_kv_decode(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], self.max_q, c.scale,
                                 num_splits=self.splits, k_scale=c.k_scale, v_scale=c.v_scale, out=self.out,
-                                lse=self.lse, workspace=self.ws, stream=stream, window_left=self.window)
+                                lse=self.lse, workspace=self.ws, stream=stream, **self.opts)
         if record:
             e1.record(stream)
             self.times.append((e0, e1))
@@ -129,6 +132,7 @@ class Call:
 
 # The calls of one step of each workload, in launch order.
 WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "long_chunk_window": ["prefill", "decode"],
+                  "long_chunk_softcap": ["prefill", "decode"], "long_chunk_alibi": ["prefill", "decode"],
                   "mixed_step": ["prefill", "decode"],
                   "mixed_step_fp8": ["prefill", "decode"], "mixed_step_e4m3": ["prefill", "decode"],
                   "decode_batch": ["decode"], "varlen": ["prefill"]}
@@ -154,6 +158,18 @@ def build_workload(name):
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
                 "seq_len": 152048, "kv_dtype": "f16", "window_left": 8191}
         return desc, [("prefill", pre, "auto"), ("decode", dec, 16)]
+    if name in ("long_chunk_softcap", "long_chunk_alibi"):
+        c = gen.long_chunk()
+        if name == "long_chunk_softcap":
+            c.meta["softcap"], what, opt = 50.0, "logit softcap 50", {"softcap": 50.0}
+        else:
+            c.meta["alibi"], what, opt = True, "ALiBi slopes 2^(-8 h / 24)", {"alibi": "geometric"}
+        pre = gen.select_seqs(c, [0], name=f"prefill 2048 after 150000, {what}")
+        dec = gen.select_seqs(c, [1], name=f"decode q=1 at 152048, {what}")
+        desc = {"workload": f"the long chunk with {what} (prefill + q=1 decode)",
+                "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
+                "seq_len": 152048, "kv_dtype": "f16", **opt}
+        return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
     if name == "mixed_step":
         c = gen.mixed_step(kv_kind="f16")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
@@ -220,7 +236,10 @@ def cpu_baseline(case, budget_rows, seed=0):
     v = oracle.dequantize_pool(gen.to_numpy64(case.v_pool, case.kv_kind), kind, case.v_scale)
     q64 = gen.to_numpy64(case.q)
     t0 = time.perf_counter()
-    oracle.paged_attention(q64, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale, rows=rows)
+    m = case.meta
+    oracle.paged_attention(q64, k, v, case.cu_seqlens_q, case.seq_lens, case.block_tables, case.scale, rows=rows,
+                           window_left=m.get("window_left", -1), softcap=m.get("softcap", 0.0),
+                           alibi_slopes=gen.geometric_alibi_slopes(case.num_q_heads) if m.get("alibi") else None)
     dt = time.perf_counter() - t0
     # attended pairs of the sampled rows
     L = int(case.seq_lens[0])

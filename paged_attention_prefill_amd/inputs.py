@@ -245,6 +245,12 @@ def long_chunk(seed=4, kind="f16", q_len=2048, prefix=150000, num_q_heads=24, nu
     return case
 
 
+def geometric_alibi_slopes(num_heads):
+    """The usual ALiBi slopes 2^(-8 (h + 1) / H), float32 [H] (an input of the
+    ALiBi option; nothing of the method's arithmetic)."""
+    return (2.0 ** (-8.0 * (np.arange(num_heads) + 1) / num_heads)).astype(np.float32)
+
+
 def mixed_step(seed=5, kv_kind="f16"):
     """D 256, Hq 24 / Hkv 4, page 816: a verify row (q=5, seq_len 240,000) and a
     784-token chunk after 104,000 cached tokens; fp16 or fp8_e5m2 KV, fp16 q."""

@@ -694,9 +694,7 @@ MOD_CASES = [
 ]
 
 
-def alibi_slopes(H):
-    """The geometric ALiBi slopes 2^(-8 (h + 1) / H)."""
-    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+alibi_slopes = gen.geometric_alibi_slopes
 
 
 @pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,softcap,with_alibi,window,with_sinks", MOD_CASES)
