@@ -249,6 +249,40 @@ int pa_split_kv_decode_ex(const void *q, int32_t q_dtype, void *out, float *lse,
                           const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One mixed step: small-q rows (decode / MTP verify, q <= PA_DECODE_MAX_Q) and
+ * prefill chunks over one KV cache in one attention launch (1CatAI/1Cat-vLLM
+ * PR #1279: a step carries chunks next to decode and verify rows; rows up to
+ * the decode limit take the split-KV path, longer ones the prefill kernel),
+ * followed by the merge pass of each part.
+ *   The batch is ordered: sequences [0, num_decode_rows) are the small-q rows
+ *   (their tokens [0, decode_tokens), decode_tokens = cu_seqlens_q[
+ *   num_decode_rows], each row <= max_q_per_row tokens), the rest are chunks
+ *   (max_seqlen_q their longest).  The small-q rows are computed exactly as by
+ *   pa_split_kv_decode_ex(decode_splits, decode_part_keys) and the chunks as
+ *   by pa_paged_prefill_ex(prefill_splits; 0 = auto from the chunks alone,
+ *   capped by the workspace) on the sub-batches: the same work items and
+ *   kernels' code, so the results have the same bits.
+ *   Head dims padded to 256 with fp16 / bf16 / fp8 KV run both in one grid
+ *   (prefill groups first; the decode groups fill the compute units the
+ *   prefill's last wave leaves idle); other shapes run the two pass-1 kernels
+ *   back to back.  out must not be NULL; lse nullable; opts as for the _ex
+ *   calls (both parts).
+ *   Workspace: pa_mixed_workspace_bytes(total_q, decode_tokens, ...), 8-byte
+ *   aligned: the chunks' records (indexed by token like the whole batch, when
+ *   the chunks are split), then the small-q rows' records.
+ *   Device metadata is trusted as for the other calls: decode_tokens must
+ *   equal cu_seqlens_q[num_decode_rows].
+ */
+size_t pa_mixed_workspace_bytes(int32_t total_q, int32_t decode_tokens, int32_t num_q_heads, int32_t head_dim,
+                                int32_t decode_splits, int32_t prefill_splits);
+int pa_mixed_step(const void *q, int32_t q_dtype, void *out, float *lse, const int32_t *cu_seqlens_q,
+                  const int32_t *seq_lens, const int32_t *block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
+                  int32_t total_q, int32_t num_q_heads, const pa_kv_cache *kv, float scale,
+                  int32_t num_decode_rows, int32_t decode_tokens, int32_t max_q_per_row, int32_t decode_splits,
+                  int32_t decode_part_keys, int32_t max_seqlen_q, int32_t prefill_splits,
+                  const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Merge of FP32 partial softmax states (InferMatrixLab/vllm-rlt PR #128,
  * "Purpose", Decode: the second kernel).
  *   partials [num_tokens, num_heads, num_splits, head_dim + 2] float32, record =

@@ -27,6 +27,8 @@ hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, 
                                   hipStream_t stream);
 hipError_t mfma_dma_occupancy(int q_kind, int dpad, int* blocks_per_cu);
 int mfma_dma_rows(int dpad);
+hipError_t launch_attn_mixed(const AttnParams& pp, const AttnParams& pd, int q_kind, int kv_kind, int dpad,
+                             int prefill_blocks, int decode_blocks, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream);
 int decode_rows_per_group();
@@ -183,6 +185,9 @@ int64_t gcd8(int64_t n) { return (n & 7) == 0 ? 8 : (n & 3) == 0 ? 4 : (n & 1) =
 // operand reads) for head dims padded to 256, otherwise the MFMA kernel with
 // register-staged dequant.
 enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
+// Bytes of one q / out element.
+size_t elem_size(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
 KernelKind kernel_for(int q_dtype, int kv_dtype, int dpad, bool decode) {
   if (q_dtype == PA_F32) return K_VALU;
   if (is_fp8(kv_dtype)) return dpad == 256 ? K_DMA : K_REGSTAGE;
@@ -288,11 +293,12 @@ int pa_prefill_auto_splits(int32_t total_q, int32_t num_seqs, int32_t max_seqlen
   return auto_splits(active, cus * occ, PA_PREFILL_MAX_AUTO_SPLITS);
 }
 
-static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
-                         const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
-                         int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
-                         int splits, int part_keys, bool is_decode, const pa_attn_options* opts,
-                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+// Plan of one pass-1 launch: the work decomposition (groups of query tiles
+// cut into XCD runs) and the kernel parameters.  nblocks = 0: nothing to run.
+static int plan_attention(pa::AttnParams& p, int64_t& nblocks, const void* q, int q_dtype, void* out, float* lse,
+                          const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, int num_seqs,
+                          int max_pages, int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
+                          int splits, int part_keys, bool is_decode, const pa_attn_options* opts, void* workspace) {
   const int g = hq / kv->num_kv_heads;
   const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
   const int rows = rows_for(kind, dpad_of(kv->head_dim), is_decode);
@@ -307,12 +313,11 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   while (ceil_div(qtiles, chunks) > 64) chunks *= 2;
   const int64_t run_len = ceil_div(qtiles, chunks);
   const int64_t runs = groups * chunks;
-  const int64_t nblocks = ceil_div(runs, 8) * 8 * run_len;
+  nblocks = ceil_div(runs, 8) * 8 * run_len;
   if (nblocks >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld groups)", (long long)nblocks);
-  if (groups == 0 || total_q == 0) return ok();
+  if (groups == 0 || total_q == 0) nblocks = 0;
   const bool partial = is_decode || splits > 1;
 
-  pa::AttnParams p;
   p.q = q;
   p.out = out;
   p.lse = lse;
@@ -350,17 +355,38 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   p.softcap_l2 = cap * 1.4426950408889634f;
   p.alibi_slopes = opts ? opts->alibi_slopes : nullptr;
 
+  return PA_OK;
+}
+
+// Pass 1 of one planned call on its own kernel.
+static hipError_t launch_pass1(const pa::AttnParams& p, int q_dtype, const pa_kv_cache* kv, bool is_decode,
+                               int64_t nblocks, hipStream_t stream) {
+  const KernelKind kind = kernel_for(q_dtype, kv->dtype, dpad_of(kv->head_dim), is_decode);
   const int qk = kind_of(q_dtype), kk = kind_of(kv->dtype), dp = dpad_of(kv->head_dim);
-  hipError_t e = kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
-                 : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, kk, dp, (int)nblocks, stream)
-                                    : (kk == pa::KV_E5M2 || kk == pa::KV_E4M3)
-                                        ? pa::launch_attn_prefill_w4(p, qk, kk, dp, (int)nblocks, stream)
-                                        : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
-                                 : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
+  return kind == K_VALU ? pa::launch_attn_valu(p, qk, kk, dp, (int)nblocks, stream)
+         : kind == K_DMA ? (is_decode ? pa::launch_attn_decode(p, qk, kk, dp, (int)nblocks, stream)
+                            : (kk == pa::KV_E5M2 || kk == pa::KV_E4M3)
+                                ? pa::launch_attn_prefill_w4(p, qk, kk, dp, (int)nblocks, stream)
+                                : pa::launch_attn_mfma_dma(p, qk, dp, (int)nblocks, stream))
+                         : pa::launch_attn_mfma(p, qk, kk, dp, (int)nblocks, stream);
+}
+
+static int run_attention(const void* q, int q_dtype, void* out, float* lse, const int32_t* cu,
+                         const int32_t* seq_lens, const int32_t* bt, int num_seqs, int max_pages,
+                         int total_q, int max_q, int hq, const pa_kv_cache* kv, float scale,
+                         int splits, int part_keys, bool is_decode, const pa_attn_options* opts,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa::AttnParams p;
+  int64_t nblocks = 0;
+  int st = plan_attention(p, nblocks, q, q_dtype, out, lse, cu, seq_lens, bt, num_seqs, max_pages, total_q, max_q,
+                          hq, kv, scale, splits, part_keys, is_decode, opts, workspace);
+  if (st != PA_OK) return st;
+  if (nblocks == 0) return ok();
+  hipError_t e = launch_pass1(p, q_dtype, kv, is_decode, nblocks, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
-    e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, qk, lse, part_keys > 0,
-                         p.sinks, stream);
+  if (p.write_partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
+    e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, kind_of(q_dtype), lse,
+                         part_keys > 0, p.sinks, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   (void)ws_bytes;
@@ -487,6 +513,121 @@ int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* l
   return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
                      total_q, max_q_per_row, num_q_heads, kv, scale, num_parts, part_keys, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+// Workspace of pa_mixed_step: the prefill records (indexed from token 0 like
+// the whole batch, total_q rows, when the chunks are split), then, 256-byte
+// aligned, the decode records of the decode_tokens small-q tokens.
+static size_t mixed_prefill_region(int32_t total_q, int32_t hq, int32_t d, int32_t prefill_splits) {
+  const size_t b = pa_prefill_workspace_bytes(total_q, hq, d, prefill_splits);
+  return (b + 255) & ~(size_t)255;
+}
+
+size_t pa_mixed_workspace_bytes(int32_t total_q, int32_t decode_tokens, int32_t num_q_heads, int32_t head_dim,
+                                int32_t decode_splits, int32_t prefill_splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return mixed_prefill_region(total_q, num_q_heads, head_dim, prefill_splits) +
+         pa_decode_workspace_bytes(decode_tokens, num_q_heads, head_dim, decode_splits);
+}
+
+int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
+                  int32_t total_q, int32_t num_q_heads, const pa_kv_cache* kv, float scale,
+                  int32_t num_decode_rows, int32_t decode_tokens, int32_t max_q_per_row, int32_t decode_splits,
+                  int32_t decode_part_keys, int32_t max_seqlen_q, int32_t prefill_splits,
+                  const pa_attn_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq,
+                        total_q, max_seqlen_q > max_q_per_row ? max_seqlen_q : max_q_per_row, num_q_heads, kv);
+  if (st != PA_OK) return st;
+  st = check_options(opts);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
+  if (out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (num_decode_rows < 0 || num_decode_rows > num_seqs || decode_tokens < 0 || decode_tokens > total_q)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_decode_rows must be in [0, num_seqs] and decode_tokens in [0, total_q]");
+  if (num_decode_rows == 0 && decode_tokens != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "decode_tokens must be 0 without small-q rows");
+  if (num_decode_rows > 0) {
+    if (max_q_per_row < 1 || max_q_per_row > PA_DECODE_MAX_Q)
+      return fail(PA_ERR_UNSUPPORTED, "max_q_per_row must be in [1, %d]", PA_DECODE_MAX_Q);
+    if ((int64_t)decode_tokens > (int64_t)num_decode_rows * max_q_per_row)
+      return fail(PA_ERR_INVALID_ARGUMENT, "decode_tokens %d > num_decode_rows * max_q_per_row", decode_tokens);
+    if (decode_splits < 1 || decode_splits > 4096)
+      return fail(PA_ERR_INVALID_ARGUMENT, "decode_splits must be in [1, 4096]");
+    if (decode_part_keys < 0 || decode_part_keys % PA_DECODE_SPLIT_TILE != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "decode_part_keys must be 0 or a positive multiple of %d",
+                  PA_DECODE_SPLIT_TILE);
+  }
+  if (prefill_splits < 0 || prefill_splits > 64)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_splits must be in [0, 64]");
+  const int nd = num_decode_rows, np = num_seqs - num_decode_rows, tp = total_q - decode_tokens;
+  if (np > 0 && tp > 0 && max_seqlen_q < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_seqlen_q must be >= 1");
+  if (total_q == 0 || num_seqs == 0) return ok();
+  const int D = kv->head_dim;
+  int sp = prefill_splits;
+  if (np > 0 && tp > 0 && sp == 0) {
+    sp = pa_prefill_auto_splits(tp, np, max_seqlen_q, num_q_heads, kv->num_kv_heads, D, q_dtype, kv->dtype);
+    if (sp < 0) return sp;
+    // at most the parts the workspace holds next to the decode records
+    const size_t dec = pa_decode_workspace_bytes(decode_tokens, num_q_heads, D, decode_splits);
+    const size_t per = pa_prefill_workspace_bytes(total_q, num_q_heads, D, 2) / 2;
+    const size_t room = (workspace == nullptr || ((uintptr_t)workspace & 7u) || workspace_bytes < dec + 256)
+                            ? 0 : workspace_bytes - dec - 256;
+    if ((size_t)sp > room / per) sp = room / per >= 2 ? (int)(room / per) : 1;
+  }
+  if (sp == 0) sp = 1;
+  const size_t need = pa_mixed_workspace_bytes(total_q, nd > 0 ? decode_tokens : 0, num_q_heads, D,
+                                               nd > 0 ? decode_splits : 1, sp);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u)))
+    return fail(PA_ERR_WORKSPACE, "mixed step needs %zu bytes of 8-byte aligned workspace (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  char* ws = (char*)workspace;
+  float* ws_pre = (float*)ws;
+  float* ws_dec = (float*)(ws + mixed_prefill_region(total_q, num_q_heads, D, sp));
+  hipStream_t strm = (hipStream_t)stream;
+
+  // the two segments, each planned as its own call; the chunk sequences are
+  // reached through offset metadata pointers (cu_seqlens_q keeps absolute
+  // token indices, so q, out and the prefill records need no offset)
+  pa::AttnParams pd, pp;
+  int64_t nb_d = 0, nb_p = 0;
+  if (nd > 0 && decode_tokens > 0) {
+    st = plan_attention(pd, nb_d, q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, nd, max_pages_per_seq,
+                        decode_tokens, max_q_per_row, num_q_heads, kv, scale, decode_splits, decode_part_keys, true,
+                        opts, ws_dec);
+    if (st != PA_OK) return st;
+  }
+  if (np > 0 && tp > 0) {
+    st = plan_attention(pp, nb_p, q, q_dtype, out, lse, cu_seqlens_q + nd, seq_lens + nd,
+                        block_tables + (int64_t)nd * max_pages_per_seq, np, max_pages_per_seq, tp, max_seqlen_q,
+                        num_q_heads, kv, scale, sp, 0, false, opts, ws_pre);
+    if (st != PA_OK) return st;
+  }
+  if (nb_d + nb_p >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const bool fused = nb_d > 0 && nb_p > 0 && dpad_of(D) == 256 &&
+                     kernel_for(q_dtype, kv->dtype, 256, false) == K_DMA;
+  hipError_t e = hipSuccess;
+  if (fused) {
+    e = pa::launch_attn_mixed(pp, pd, kind_of(q_dtype), kind_of(kv->dtype), 256, (int)nb_p, (int)nb_d, strm);
+  } else {  // other shapes: the two pass-1 kernels back to back
+    if (nb_p > 0) e = launch_pass1(pp, q_dtype, kv, false, nb_p, strm);
+    if (e == hipSuccess && nb_d > 0) e = launch_pass1(pd, q_dtype, kv, true, nb_d, strm);
+  }
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "mixed-step attention launch failed: %s", hipGetErrorString(e));
+  if (nb_p > 0 && sp > 1) {
+    const size_t row = (size_t)num_q_heads * D * elem_size(q_dtype);
+    e = pa::launch_merge(ws_pre + (size_t)decode_tokens * num_q_heads * sp * (D + 2), sp, tp, num_q_heads, D,
+                         (char*)out + (size_t)decode_tokens * row, kind_of(q_dtype),
+                         lse ? lse + (size_t)decode_tokens * num_q_heads : nullptr, false, pp.sinks, strm);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  if (nb_d > 0) {
+    e = pa::launch_merge(ws_dec, decode_splits, decode_tokens, num_q_heads, D, out, kind_of(q_dtype), lse,
+                         decode_part_keys > 0, pd.sinks, strm);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
 }
 
 int pa_write_kv(const void* k_new, const void* v_new, int32_t src_dtype, const int32_t* cu_seqlens_q,

@@ -73,6 +73,10 @@ def lib():
         L.pa_paged_prefill_ex.argtypes = L.pa_paged_prefill.argtypes[:15] + [ctypes.POINTER(AttnOptions), _P, _SZ, _P]
         L.pa_split_kv_decode_ex.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, ctypes.POINTER(AttnOptions),
                                                                               _P, _SZ, _P]
+        L.pa_mixed_step.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), ctypes.c_float,
+                                    _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(AttnOptions), _P, _SZ, _P]
+        L.pa_mixed_workspace_bytes.argtypes = [_I] * 6
+        L.pa_mixed_workspace_bytes.restype = _SZ
         L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.pa_write_kv.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), _P]
         L.pa_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I]
@@ -85,7 +89,7 @@ def lib():
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
         for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_split_kv_decode_fixed", "pa_merge_states",
-                     "pa_write_kv", "pa_paged_prefill_ex", "pa_split_kv_decode_ex",
+                     "pa_write_kv", "pa_paged_prefill_ex", "pa_split_kv_decode_ex", "pa_mixed_step",
                      "pa_check_supported",
                      "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
             if name != "pa_status_string":
@@ -261,6 +265,39 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
                                        _ptr(workspace), ws_have, _stream(stream)))
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_splits)
+    return (out, lse) if return_lse or lse is not None else out
+
+
+def mixed_workspace_bytes(total_q, decode_tokens, num_q_heads, head_dim, decode_splits, prefill_splits):
+    return int(lib().pa_mixed_workspace_bytes(total_q, decode_tokens, num_q_heads, head_dim, decode_splits,
+                                              prefill_splits))
+
+
+def mixed_step(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, num_decode_rows, decode_tokens,
+               max_q_per_row, max_seqlen_q, scale, *, decode_splits=16, decode_part_keys=0, prefill_splits=0,
+               k_scale=1.0, v_scale=1.0, out=None, lse=None, return_lse=False, workspace=None, stream=None,
+               k_head_scales=None, v_head_scales=None, sinks=None, window_left=-1, softcap=0.0, alibi_slopes=None):
+    """pa_mixed_step: sequences [0, num_decode_rows) are small-q rows (their
+    decode_tokens tokens first in q), the rest prefill chunks; one attention
+    launch for both at head dims padded to 256.  Returns out (and lse)."""
+    total_q, Hq, D = q.shape
+    if not q.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale, k_head_scales, v_head_scales)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    B = int(seq_lens.numel())
+    ws_bytes = mixed_workspace_bytes(total_q, decode_tokens, Hq, D, decode_splits, prefill_splits)
+    workspace = _workspace(workspace, ws_bytes, q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    opts = _options(Hq, sinks, window_left, softcap, alibi_slopes)
+    _check(lib().pa_mixed_step(_ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
+                               _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B,
+                               block_tables.shape[-1], total_q, Hq, ctypes.byref(kv), float(scale),
+                               int(num_decode_rows), int(decode_tokens), int(max_q_per_row), int(decode_splits),
+                               int(decode_part_keys), int(max_seqlen_q), int(prefill_splits),
+                               opts[0] if opts else None, _ptr(workspace), ws_have, _stream(stream)))
     return (out, lse) if return_lse or lse is not None else out
 
 

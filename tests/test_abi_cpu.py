@@ -218,3 +218,26 @@ def test_options_are_checked_before_launch():
     st = L.pa_split_kv_decode_ex(0x30000, ops.PA_F16, 0x40000, None, 0x50000, 0x60000, 0x70000, 4, 4, 4, 1, 8,
                                  ctypes.byref(kv), 0.1, 8, 0, ctypes.byref(ok), None, 0, None)
     assert st == ops.PA_ERR_WORKSPACE  # accepted up to the workspace check
+
+
+def test_mixed_step_arguments_are_checked_before_launch():
+    L = ops.lib()
+    kv = _fake_kv()
+
+    def mixed(out=0x40000, nd=2, dec_tok=2, max_q=1, sd=8, pk=0, max_sq=8, sp=1, ws=None, wsb=0):
+        return L.pa_mixed_step(0x30000, ops.PA_F16, out, None, 0x50000, 0x60000, 0x70000, 4, 4, 10, 8,
+                               ctypes.byref(kv), 0.1, nd, dec_tok, max_q, sd, pk, max_sq, sp, None, ws, wsb, None)
+    assert mixed(out=None) == ops.PA_ERR_INVALID_ARGUMENT
+    assert mixed(nd=5) == ops.PA_ERR_INVALID_ARGUMENT           # more small-q rows than sequences
+    assert mixed(nd=0, dec_tok=1) == ops.PA_ERR_INVALID_ARGUMENT  # tokens without rows
+    assert mixed(dec_tok=3) == ops.PA_ERR_INVALID_ARGUMENT      # 2 rows of at most 1 token
+    assert mixed(max_q=17) == ops.PA_ERR_UNSUPPORTED
+    assert mixed(sd=0) == ops.PA_ERR_INVALID_ARGUMENT
+    assert mixed(pk=48) == ops.PA_ERR_INVALID_ARGUMENT
+    assert mixed(sp=65) == ops.PA_ERR_INVALID_ARGUMENT
+    assert mixed() == ops.PA_ERR_WORKSPACE                        # records of the small-q rows need room
+    need = ops.mixed_workspace_bytes(10, 2, 8, 64, 8, 1)
+    assert need == 2 * 8 * 8 * 66 * 4                             # unsplit chunks: only the decode records
+    need3 = ops.mixed_workspace_bytes(10, 2, 8, 64, 8, 3)
+    assert need3 == ((10 * 8 * 3 * 66 * 4 + 255) // 256) * 256 + need
+    assert mixed(sp=3, ws=0x80000, wsb=need) == ops.PA_ERR_WORKSPACE
