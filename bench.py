@@ -81,7 +81,10 @@ class Call:
         self.out = torch.empty_like(d["q"])
         self.lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
         D = case.head_dim
-        if kind == "prefill":
+        if kind == "mixed":  # splits = (prefill parts, decode parts); meta: the small-q rows first
+            m = case.meta
+            nb = ops.mixed_workspace_bytes(case.total_q, m["decode_tokens"], case.num_q_heads, D, splits[1], splits[0])
+        elif kind == "prefill":
             nb = ops.prefill_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
         else:
             nb = ops.decode_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
@@ -95,7 +98,14 @@ class Call:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if self.kind == "prefill" and self.splits > 1:
+        if self.kind == "mixed":
+            m = c.meta
+            ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], m["decode_rows"],
+                           m["decode_tokens"], m["max_q_per_row"], m["max_seqlen_q_prefill"], c.scale,
+                           decode_splits=self.splits[1], prefill_splits=self.splits[0], k_scale=c.k_scale,
+                           v_scale=c.v_scale, out=self.out, lse=self.lse, workspace=self.ws, stream=stream,
+                           **self.opts)
+        elif self.kind == "prefill" and self.splits > 1:
             # the two passes apart, so that the attention kernel is timed alone
             parts = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], c.max_seqlen_q,
                                       c.scale, k_scale=c.k_scale, v_scale=c.v_scale, num_kv_splits=self.splits,
@@ -132,6 +142,7 @@ class Call:
 
 # The calls of one step of each workload, in launch order.
 WORKLOAD_CALLS = {"long_chunk": ["prefill", "decode"], "long_chunk_window": ["prefill", "decode"],
+                  "mixed_step_fused": ["mixed"],
                   "long_chunk_softcap": ["prefill", "decode"], "long_chunk_alibi": ["prefill", "decode"],
                   "mixed_step": ["prefill", "decode"],
                   "mixed_step_fp8": ["prefill", "decode"], "mixed_step_e4m3": ["prefill", "decode"],
@@ -170,6 +181,14 @@ def build_workload(name):
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 64, "q_len": 2048,
                 "seq_len": 152048, "kv_dtype": "f16", **opt}
         return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
+    if name == "mixed_step_fused":
+        c = gen.mixed_step(kv_kind="f16")  # sequence 0: the verify row (the small-q row first), 1: the chunk
+        c.meta.update(decode_rows=1, decode_tokens=int(c.cu_seqlens_q[1]), max_q_per_row=int(c.q_lens[0]),
+                      max_seqlen_q_prefill=int(c.q_lens[1]))
+        desc = {"workload": "the mixed step in one attention launch (pa_mixed_step): the verify row q=5 at 240,000 "
+                            "keys and the 784-token chunk after 104,000, fp16, D 256, page 816",
+                "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 816, "kv_dtype": "f16"}
+        return desc, [("mixed", c, "auto")]
     if name == "mixed_step":
         c = gen.mixed_step(kv_kind="f16")
         ver = gen.select_seqs(c, [0], name="verify q=5 at 240000")
@@ -476,7 +495,17 @@ def main():
     desc, specs = build_workload(a.workload)
     calls = []
     for kind, case, splits in specs:
-        if kind == "prefill":
+        if kind == "mixed":
+            chunk = gen.select_seqs(case, range(case.meta["decode_rows"], case.num_seqs))
+            sp = a.prefill_splits if a.prefill_splits is not None else splits
+            sp = 0 if sp == "auto" else int(sp)
+            if sp == 0:
+                sp = ops.auto_splits(chunk.total_q, chunk.num_seqs, chunk.max_seqlen_q, case.num_q_heads,
+                                     case.num_kv_heads, case.head_dim, ops._TORCH_TO_PA[case.q.dtype],
+                                     {"e5m2": ops.PA_FP8_E5M2, "e4m3": ops.PA_FP8_E4M3}.get(
+                                         case.kv_kind, ops._TORCH_TO_PA[case.q.dtype]))
+            s = (sp, a.decode_splits or 64)
+        elif kind == "prefill":
             s = a.prefill_splits if a.prefill_splits is not None else splits
             s = 0 if s == "auto" else int(s)
             if s == 0:
@@ -514,6 +543,15 @@ def main():
             parts["prefill"] = {"ms": ms, "ms_median": c.ms_median(), "tflops": f / (ms * 1e-3) / 1e12, "flops": f,
                                 "kernel_ms": kms, "kernel_tflops": f / (kms * 1e-3) / 1e12,
                                 "splits": c.splits, "name": c.case.name}
+        elif c.kind == "mixed":
+            nd = c.case.meta["decode_rows"]
+            rows = gen.select_seqs(c.case, range(nd))
+            chunk = gen.select_seqs(c.case, range(nd, c.case.num_seqs))
+            f = call_flops("prefill", chunk) + call_flops("decode", rows)
+            step_flops += f
+            parts["mixed"] = {"ms": ms, "ms_median": c.ms_median(), "tflops": f / (ms * 1e-3) / 1e12, "flops": f,
+                              "prefill_splits": c.splits[0], "decode_splits": c.splits[1], "name": c.case.name,
+                              "what": "one pa_mixed_step call: the fused attention launch and the two merges"}
         else:
             b = call_bytes(c.kind, c.case, c.splits)
             f = call_flops(c.kind, c.case)
