@@ -262,10 +262,10 @@ int pa_split_kv_decode_ex(const void *q, int32_t q_dtype, void *out, float *lse,
  *   by pa_paged_prefill_ex(prefill_splits; 0 = auto from the chunks alone,
  *   capped by the workspace) on the sub-batches: the same work items and
  *   kernels' code, so the results have the same bits.
- *   Head dims padded to 256 with fp16 / bf16 / fp8 KV run both in one grid
- *   (prefill groups first; the decode groups fill the compute units the
- *   prefill's last wave leaves idle); other shapes run the two pass-1 kernels
- *   back to back.  out must not be NULL; lse nullable; opts as for the _ex
+ *   Head dims padded to 256 with fp16 / bf16 / fp8 KV and no window or score
+ *   modifier run both in one grid (prefill groups first; the decode groups
+ *   fill the compute units the prefill's last wave leaves idle); other shapes
+ *   and options run the two pass-1 kernels back to back.  out must not be NULL; lse nullable; opts as for the _ex
  *   calls (both parts).
  *   Workspace: pa_mixed_workspace_bytes(total_q, decode_tokens, ...), 8-byte
  *   aligned: the chunks' records (indexed by token like the whole batch, when

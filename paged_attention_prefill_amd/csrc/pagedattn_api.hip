@@ -605,8 +605,11 @@ int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const i
     if (st != PA_OK) return st;
   }
   if (nb_d + nb_p >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  // one grid for the default instantiations at D padded to 256 (with a window
+  // or score modifiers the fused kernel spills: the two kernels run instead)
   const bool fused = nb_d > 0 && nb_p > 0 && dpad_of(D) == 256 &&
-                     kernel_for(q_dtype, kv->dtype, 256, false) == K_DMA;
+                     kernel_for(q_dtype, kv->dtype, 256, false) == K_DMA && pp.window_left < 0 &&
+                     !pa::has_score_mods(pp);
   hipError_t e = hipSuccess;
   if (fused) {
     e = pa::launch_attn_mixed(pp, pd, kind_of(q_dtype), kind_of(kv->dtype), 256, (int)nb_p, (int)nb_d, strm);
