@@ -484,6 +484,17 @@ def test_mixed_step_sampled(kv_kind):
     ref, rl = run_oracle(chunk, rows=rows, pools=(k, v))
     compare(f"mixed chunk {kv_kind} (sampled {len(rows)})", kv_kind, out[rows[:, 0], rows[:, 1]], ref,
             lse[rows[:, 0], rows[:, 1]], rl)
+    # the whole step as one pa_mixed_step call (the launch bench.py times as
+    # mixed_step_fused): the same bits as the two calls above
+    d = gen.to_device(c)
+    say(f"  mixed step in one launch {kv_kind}: verify row (64 parts) + chunk (auto parts)")
+    fo, fl = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], 1, 5, 5, 784, c.scale,
+                            decode_splits=64, prefill_splits=0, k_scale=c.k_scale, v_scale=c.v_scale,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(fo[:5]), bits(od)) and torch.equal(bits(fl[:5]), bits(ld))
+    assert np.array_equal(fo[5:].float().cpu().numpy().astype(np.float64), out)
+    assert np.array_equal(fl[5:].cpu().numpy().astype(np.float64), lse)
 
 
 # ------------------------------------------------------------------ fp8 E4M3 KV
