@@ -22,7 +22,8 @@
  *  - fp8 KV (1CatAI/1Cat-vLLM PR #616, fp8_e5m2 paragraph of "Test Result";
  *    the same page's "Test Plan" names an e4m3 path too): E5M2 or E4M3 bytes
  *    are dequantized inside the kernels, value = decode(byte) * k_scale (or
- *    v_scale); q and out stay fp16.
+ *    v_scale); q and out stay fp16 or bf16 (every fp8 value widens exactly
+ *    to either).
  *  - pa_split_kv_decode_fixed: decode with absolute part boundaries, so that
  *    a verify row equals serial decoding bit for bit.
  *  - pa_write_kv: the new tokens' K/V into their pages (fp8: quantised).
@@ -52,8 +53,8 @@
  *    the any-page gate).  Strides and base pointers must be 16-byte aligned.
  *  - Query head hq reads kv head hq / (num_q_heads / num_kv_heads).
  *  - Supported dtypes: (q, KV) = (F32, F32), (F16, F16), (BF16, BF16),
- *    (F16, FP8_E5M2); out has q's dtype.  head_dim is a multiple of 16 in
- *    [16, 256].
+ *    (F16 or BF16, FP8_E5M2), (F16 or BF16, FP8_E4M3); out has q's dtype.
+ *    head_dim is a multiple of 16 in [16, 256].
  *
  * Errors: every call returns PA_OK (0) or a negative pa_status; nothing is
  * launched when an argument is rejected.  pa_last_error() gives a message
@@ -313,7 +314,7 @@ int pa_merge_states(const float *partials, int32_t num_splits, int32_t num_token
  *   negative position (q_len > seq_len) are not written.
  *   The cache (kv->k_pages, kv->v_pages: written through, despite the const of
  *   the descriptor) has src_dtype, which is copied exactly, or FP8_E5M2 (with
- *   F16 src) or FP8_E4M3 (with F16 src), byte = the fp8 code of (x / scale)
+ *   F16 or BF16 src) or FP8_E4M3 (with F16 or BF16 src), byte = the fp8 code of (x / scale)
  *   computed in fp32, scale = k_scale (v_scale for V, both positive) times the
  *   head's k_head_scales[h] when given (the product rounded to fp32), rounded to
  *   nearest with ties to even and saturated to the largest finite magnitude

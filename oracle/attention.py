@@ -306,8 +306,3 @@ def attended_pairs(cu_seqlens_q, seq_lens):
             total += max(0, int(L[b]) - Qb + i + 1)
     return total
 
-
-def attention_flops(cu_seqlens_q, seq_lens, num_q_heads, head_dim):
-    """Causal-exact work: 2*D multiply-adds for QK^T and 2*D for PV per attended pair and head."""
-    return 4 * head_dim * num_q_heads * attended_pairs(cu_seqlens_q, seq_lens)
-

@@ -17,7 +17,9 @@ What is computed (the pages give the step, not its arithmetic):
 The encoder is written as that definition: it searches the table of all
 finite E5M2 values (decoded by ``oracle.fp8`` from the bit layout) for the
 nearest one; no bit tricks.  Pinned against torch's float8_e5m2 conversion
-inside the finite range and against hand-checked values.
+inside the finite range and against hand-checked values.  The float32
+quotient is pinned by exact rational arithmetic on inputs where a float64
+quotient would give another byte.
 """
 
 import numpy as np

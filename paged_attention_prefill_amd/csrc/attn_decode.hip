@@ -36,14 +36,19 @@ hipError_t launch_dec_d(const AttnParams& p, int dpad, int nblocks, hipStream_t 
 }  // namespace
 
 // Decode pass 1, 32 rows per group: fp16 / bf16 q with KV of the same dtype
-// (kv_kind = q_kind), or fp16 q with fp8 KV (E5M2 or E4M3) for head dims
-// padded to 256.
+// (kv_kind = q_kind), or fp16 / bf16 q with fp8 KV (E5M2 or E4M3) for head
+// dims padded to 256.
 hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                               hipStream_t stream) {
   if (kv_kind == KV_E5M2 || kv_kind == KV_E4M3) {
-    if (q_kind != KV_F16 || dpad != 256) return hipErrorInvalidValue;
-    return kv_kind == KV_E5M2 ? launch_dec<_Float16, KV_E5M2, 256, 2>(p, nblocks, stream)
-                              : launch_dec<_Float16, KV_E4M3, 256, 2>(p, nblocks, stream);
+    if (dpad != 256) return hipErrorInvalidValue;
+    if (q_kind == KV_F16)
+      return kv_kind == KV_E5M2 ? launch_dec<_Float16, KV_E5M2, 256, 2>(p, nblocks, stream)
+                                : launch_dec<_Float16, KV_E4M3, 256, 2>(p, nblocks, stream);
+    if (q_kind == KV_BF16)
+      return kv_kind == KV_E5M2 ? launch_dec<__bf16, KV_E5M2, 256, 2>(p, nblocks, stream)
+                                : launch_dec<__bf16, KV_E4M3, 256, 2>(p, nblocks, stream);
+    return hipErrorInvalidValue;
   }
   if (q_kind != kv_kind) return hipErrorInvalidValue;
   if (q_kind == KV_F16) return launch_dec_d<_Float16>(p, dpad, nblocks, stream);

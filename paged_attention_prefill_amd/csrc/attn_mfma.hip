@@ -1,4 +1,4 @@
-// Paged attention pass 1 on MFMA (fp16 / bf16 queries; fp16, bf16 or fp8_e5m2 KV).
+// Paged attention pass 1 on MFMA (fp16 / bf16 queries; fp16, bf16 or fp8 E5M2 / E4M3 KV).
 //
 // One work group = 128 GQA-packed query rows (packed row r of a sequence is
 // query token r / g, query head kv_head * g + r % g) of one sequence and one
@@ -71,9 +71,13 @@ template <int KVK> struct Chunk { typedef uint4 raw; };
 template <> struct Chunk<KV_E5M2> { typedef uint2 raw; };
 template <> struct Chunk<KV_E4M3> { typedef uint2 raw; };
 
-template <int KVK>
+// Eight KV elements -> eight values of the compute type QT (exact for fp8).
+template <typename QT, int KVK>
 __device__ __forceinline__ uint4 to_compute(typename Chunk<KVK>::raw x) {
-  if constexpr (KVK == KV_E5M2) {
+  if constexpr ((KVK == KV_E5M2 || KVK == KV_E4M3) && __is_same(QT, __bf16)) {
+    return make_uint4(fp8x2_to_bf16x2<KVK, false>(x.x), fp8x2_to_bf16x2<KVK, true>(x.x),
+                      fp8x2_to_bf16x2<KVK, false>(x.y), fp8x2_to_bf16x2<KVK, true>(x.y));
+  } else if constexpr (KVK == KV_E5M2) {
     uint4 r;
     e5m2x4_to_f16x4(x.x, r.x, r.y);
     e5m2x4_to_f16x4(x.y, r.z, r.w);
@@ -211,11 +215,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnParams p)
 #pragma unroll
     for (int ps = 0; ps < KPASS; ++ps) {
       const int kr = kkey0 + ps * KKEYS;
-      *(uint4*)&k_lds[buf][kr * KS + kc * 8] = to_compute<KVK>(kst[ps]);
+      *(uint4*)&k_lds[buf][kr * KS + kc * 8] = to_compute<QT, KVK>(kst[ps]);
     }
     if (v_loader) {
-      uint4 x0 = to_compute<KVK>(vst[0]), x1 = to_compute<KVK>(vst[1]);
-      uint4 x2 = to_compute<KVK>(vst[2]), x3 = to_compute<KVK>(vst[3]);
+      uint4 x0 = to_compute<QT, KVK>(vst[0]), x1 = to_compute<QT, KVK>(vst[1]);
+      uint4 x2 = to_compute<QT, KVK>(vst[2]), x3 = to_compute<QT, KVK>(vst[3]);
       const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
       const uint32_t a2[4] = {x2.x, x2.y, x2.z, x2.w}, a3[4] = {x3.x, x3.y, x3.z, x3.w};
       uint16_t* dst = &v_lds[buf][(vc * 8) * VS + vt_pos(vquad)];
@@ -359,13 +363,15 @@ static hipError_t launch_d(const AttnParams& p, int dpad, int nblocks, hipStream
   }
 }
 
-// q_kind: KV_F16 or KV_BF16; kv_kind: same as q_kind, or KV_E5M2 / KV_E4M3 with fp16 q.
+// q_kind: KV_F16 or KV_BF16; kv_kind: same as q_kind, or KV_E5M2 / KV_E4M3.
 hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                             hipStream_t stream) {
   if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_d<_Float16, KV_F16>(p, dpad, nblocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_d<__bf16, KV_BF16>(p, dpad, nblocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_d<_Float16, KV_E5M2>(p, dpad, nblocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_E4M3) return launch_d<_Float16, KV_E4M3>(p, dpad, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E5M2) return launch_d<__bf16, KV_E5M2>(p, dpad, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E4M3) return launch_d<__bf16, KV_E4M3>(p, dpad, nblocks, stream);
   return hipErrorInvalidValue;
 }
 
@@ -396,6 +402,8 @@ hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu)
   if (q_kind == KV_BF16 && kv_kind == KV_BF16) return occ_d<__bf16, KV_BF16>(dpad, blocks_per_cu);
   if (q_kind == KV_F16 && kv_kind == KV_E5M2) return occ_d<_Float16, KV_E5M2>(dpad, blocks_per_cu);
   if (q_kind == KV_F16 && kv_kind == KV_E4M3) return occ_d<_Float16, KV_E4M3>(dpad, blocks_per_cu);
+  if (q_kind == KV_BF16 && kv_kind == KV_E5M2) return occ_d<__bf16, KV_E5M2>(dpad, blocks_per_cu);
+  if (q_kind == KV_BF16 && kv_kind == KV_E4M3) return occ_d<__bf16, KV_E4M3>(dpad, blocks_per_cu);
   return hipErrorInvalidValue;
 }
 

@@ -47,7 +47,7 @@ hipError_t launch_mixed(const AttnParams& pp, const AttnParams& pd, int prefill_
 }  // namespace
 
 // Both segments at head dims padded to 256: fp16 / bf16 q with KV of the same
-// dtype, or fp16 q with fp8 KV (E5M2 or E4M3).  The ring depths are those of
+// dtype, or fp16 / bf16 q with fp8 KV (E5M2 or E4M3).  The ring depths are those of
 // the separate kernels.
 hipError_t launch_attn_mixed(const AttnParams& pp, const AttnParams& pd, int q_kind, int kv_kind, int dpad,
                              int prefill_blocks, int decode_blocks, hipStream_t stream) {
@@ -56,6 +56,10 @@ hipError_t launch_attn_mixed(const AttnParams& pp, const AttnParams& pd, int q_k
     return launch_mixed<_Float16, KV_E5M2, 8, 2>(pp, pd, prefill_blocks, decode_blocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_E4M3)
     return launch_mixed<_Float16, KV_E4M3, 8, 2>(pp, pd, prefill_blocks, decode_blocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E5M2)
+    return launch_mixed<__bf16, KV_E5M2, 8, 2>(pp, pd, prefill_blocks, decode_blocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E4M3)
+    return launch_mixed<__bf16, KV_E4M3, 8, 2>(pp, pd, prefill_blocks, decode_blocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_F16)
     return launch_mixed<_Float16, 0, 5, 1>(pp, pd, prefill_blocks, decode_blocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16)

@@ -27,13 +27,15 @@ hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
 }  // namespace
 
 // Prefill pass 1, head dims padded to 256, 256 query rows per work group:
-// fp16 / bf16 q with KV of the same dtype (kv_kind = q_kind), or fp16 q with
-// fp8 KV (kv_kind = KV_E5M2 or KV_E4M3).
+// fp16 / bf16 q with KV of the same dtype (kv_kind = q_kind), or fp16 / bf16 q
+// with fp8 KV (kv_kind = KV_E5M2 or KV_E4M3).
 hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                                   hipStream_t stream) {
   if (dpad != 256) return hipErrorInvalidValue;
   if (q_kind == KV_F16 && kv_kind == KV_E5M2) return launch_w4<_Float16, KV_E5M2, 256, 8>(p, nblocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_E4M3) return launch_w4<_Float16, KV_E4M3, 256, 8>(p, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E5M2) return launch_w4<__bf16, KV_E5M2, 256, 8>(p, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_E4M3) return launch_w4<__bf16, KV_E4M3, 256, 8>(p, nblocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, 0, 256, 5>(p, nblocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, 0, 256, 5>(p, nblocks, stream);
   return hipErrorInvalidValue;

@@ -1,5 +1,5 @@
 // Split-KV decode pass 1 on MFMA (fp16 / bf16 q; KV of the same dtype, or
-// fp8 E5M2 KV for head dims padded to 256).
+// fp8 E5M2 / E4M3 KV for head dims padded to 256).
 //
 // A decode row has q <= 16 tokens (InferMatrixLab/vllm-rlt PR #128, "Purpose",
 // Decode; MTP verify rows q = K+1, 1CatAI/1Cat-vLLM PR #616, "Purpose"), so a
@@ -25,9 +25,9 @@ using namespace mf;
 // NSW stages of (K, V) tiles in its own part of LDS.  The K half of a stage is
 // refilled as soon as the wave's S^T = K Q^T has read it and the V half after
 // O^T += V^T P^T, so that between one and 2 NSW half-tiles per wave are always
-// in flight.  F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16), 8-bit tiles in
-// LDS widened to fp16 as the MFMA operands are read.  The combined result depends only on
-// the row's own length and the part count.
+// in flight.  F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16 or bf16), 8-bit
+// tiles in LDS widened to the query's type as the MFMA operands are read.  The
+// combined result depends only on the row's own length and the part count.
 // Head dims up to 128 are held to 256 registers so that two groups share a CU
 // (with one ring stage per wave at D 128: 64 KB of LDS per group): a decode
 // batch has many short parts, and a second resident group hides each part's
@@ -206,8 +206,8 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
 #pragma unroll
       for (int kp = 0; kp < NKK / 2; ++kp) {
         const uint4 kw = *(const uint4*)(smem + sb + k_frag(klane, kp));
-        s0 = Mf<QT>::run(fp8x8_to_f16<F8>(kw.x, kw.y), qf[2 * kp], s0);
-        s1 = Mf<QT>::run(fp8x8_to_f16<F8>(kw.z, kw.w), qf[2 * kp + 1], s1);
+        s0 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.x, kw.y), qf[2 * kp], s0);
+        s1 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.z, kw.w), qf[2 * kp + 1], s1);
       }
     } else {
 #pragma unroll
@@ -270,7 +270,7 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint4 a;
-        if constexpr (KV8) a = read_vt8<F8>(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
+        if constexpr (KV8) a = read_vt8<QT, F8>(smem + ((vls + ks * 16 * ROWB) ^ (db << 5)));
         else a = read_vt(smem + (vls ^ (db << 6)) + ks * 16 * ROWB, 8 * ROWB);
         oacc[db] = Mf<QT>::run(a, pf[ks], oacc[db]);
       }

@@ -256,6 +256,17 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
 }
 
+// Two fp8 bytes (byte 2 w and 2 w + 1 of x) -> two bf16 in one 32-bit word,
+// lower byte in the lower half: the gfx950 conversions with a scale of 1
+// (every E5M2 and every E4M3 value is exact in bf16).
+template <int F8, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
+  if constexpr (F8 == KV_E4M3)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x, 1.0f, HI));
+}
+
 // fp8 E5M2 byte -> fp16 bits: E5M2 is the high byte of an fp16 with the same
 // sign/exponent/mantissa layout, so the conversion is exact.
 __device__ __forceinline__ void e5m2x4_to_f16x4(uint32_t x, uint32_t& lo, uint32_t& hi) {

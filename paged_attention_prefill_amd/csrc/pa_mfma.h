@@ -188,10 +188,15 @@ __device__ __forceinline__ uint4 e5m2x8_to_f16(uint32_t a, uint32_t b) {
   return make_uint4(e5m2_lo2(a), e5m2_hi2(a), e5m2_lo2(b), e5m2_hi2(b));
 }
 
-// Eight fp8 bytes (a: elements 0..3, b: 4..7) -> eight fp16, F8 = KV_E5M2 or KV_E4M3.
-template <int F8>
-__device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t a, uint32_t b) {
-  if constexpr (F8 == KV_E4M3)
+// Eight fp8 bytes (a: elements 0..3, b: 4..7) -> eight values of the 16-bit
+// compute type QT (fp16 or bf16, the query's type), F8 = KV_E5M2 or KV_E4M3.
+// Exact: every fp8 value of both formats is representable in fp16 and in bf16.
+template <typename QT, int F8>
+__device__ __forceinline__ uint4 fp8x8_to(uint32_t a, uint32_t b) {
+  if constexpr (__is_same(QT, __bf16))
+    return make_uint4(fp8x2_to_bf16x2<F8, false>(a), fp8x2_to_bf16x2<F8, true>(a), fp8x2_to_bf16x2<F8, false>(b),
+                      fp8x2_to_bf16x2<F8, true>(b));
+  else if constexpr (F8 == KV_E4M3)
     return make_uint4(e4m3x2_to_f16x2<false>(a), e4m3x2_to_f16x2<true>(a), e4m3x2_to_f16x2<false>(b),
                       e4m3x2_to_f16x2<true>(b));
   else
@@ -210,10 +215,10 @@ typedef __attribute__((address_space(3))) v2i32 lds_v2i32_t;
 // k-indices (16 ks + 8 (i / 4) + 4 (lane / 32) + i % 4, i = 0..7); the V chunk
 // swizzle c ^ 2 f(key), f(key) = (key & 3) | (bit 3 of key) << 2, puts those 8
 // rows' chunks in 8 different slots, so the reads are free of bank conflicts.
-template <int F8 = KV_E5M2>
+template <typename QT, int F8>
 __device__ __forceinline__ uint4 read_vt8(const char* a) {
   const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_t*)a);
-  return fp8x8_to_f16<F8>((uint32_t)r.x, (uint32_t)r.y);
+  return fp8x8_to<QT, F8>((uint32_t)r.x, (uint32_t)r.y);
 }
 
 // Gathers 32-key K and V tiles of one kv head through the block table into an

@@ -78,8 +78,8 @@ int check_supported(int q_dtype, int kv_dtype, int head_dim, int page_size, int 
     st = PA_ERR_UNSUPPORTED, r = "q dtype must be F32, F16 or BF16";
   } else if (dtype_size(kv_dtype) == 0) {
     st = PA_ERR_UNSUPPORTED, r = "unknown KV dtype";
-  } else if (!(kv_dtype == q_dtype || (is_fp8(kv_dtype) && q_dtype == PA_F16))) {
-    st = PA_ERR_UNSUPPORTED, r = "KV dtype must equal q dtype, or be FP8_E5M2 / FP8_E4M3 with F16 q";
+  } else if (!(kv_dtype == q_dtype || (is_fp8(kv_dtype) && (q_dtype == PA_F16 || q_dtype == PA_BF16)))) {
+    st = PA_ERR_UNSUPPORTED, r = "KV dtype must equal q dtype, or be FP8_E5M2 / FP8_E4M3 with F16 or BF16 q";
   } else if (head_dim < 16 || head_dim > 256 || head_dim % 16 != 0) {
     st = PA_ERR_UNSUPPORTED, r = "head_dim must be a multiple of 16 in [16, 256]";
   } else if (page_size < 16 || page_size % 16 != 0) {
@@ -181,9 +181,9 @@ int64_t gcd8(int64_t n) { return (n & 7) == 0 ? 8 : (n & 3) == 0 ? 4 : (n & 1) =
 
 // Which pass-1 kernel serves a call: fp32 -> exact-product VALU kernel;
 // fp16/bf16 with same-dtype KV -> MFMA kernels with the LDS DMA pipeline;
-// fp16 q with fp8_e5m2 KV -> the DMA kernels (8-bit tiles widened at the
-// operand reads) for head dims padded to 256, otherwise the MFMA kernel with
-// register-staged dequant.
+// fp16 / bf16 q with fp8 KV -> the DMA kernels (8-bit tiles widened to the
+// query's type at the operand reads) for head dims padded to 256, otherwise
+// the MFMA kernel with register-staged dequant.
 enum KernelKind { K_VALU, K_DMA, K_REGSTAGE };
 // Bytes of one q / out element.
 size_t elem_size(int dtype) { return dtype == PA_F32 ? 4 : 2; }

@@ -54,7 +54,11 @@ __device__ __forceinline__ void mfma_s(f32x16_t& c, uint4 a, uint4 b, bool first
       PA_MFMA_S("v_mfma_f32_32x32x16_f16")
     }
   } else {
-    PA_MFMA_S("v_mfma_f32_32x32x16_bf16")
+    if constexpr (VALU_A) {
+      PA_MFMA_S("s_nop 2\n\tv_mfma_f32_32x32x16_bf16")
+    } else {
+      PA_MFMA_S("v_mfma_f32_32x32x16_bf16")
+    }
   }
 #undef PA_MFMA_S
 }
@@ -90,8 +94,8 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 
 }  // namespace
 
-// F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16); the tiles stay 8-bit in
-// LDS and are widened to fp16 as their MFMA operands are read.  F8 = 0: KV of
+// F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16 or bf16); the tiles stay
+// 8-bit in LDS and are widened to the query's type as their MFMA operands are read.  F8 = 0: KV of
 // the q dtype.
 // VAR 0: no options that touch the scores; 1: a left sliding window; 2: score
 // modifiers (softcap / ALiBi, mod_score), with or without a window.  Each is
@@ -238,7 +242,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
         kw = kf[rd % KPF];
         if (rd + KPF < NRD) kf[rd % KPF] = *(const uint4*)(smem + kls + k_frag(klane, rd + KPF));
       }
-      if constexpr (KV8) a = (kk & 1) ? fp8x8_to_f16<F8>(kw.z, kw.w) : fp8x8_to_f16<F8>(kw.x, kw.y);
+      if constexpr (KV8) a = (kk & 1) ? fp8x8_to<QT, F8>(kw.z, kw.w) : fp8x8_to<QT, F8>(kw.x, kw.y);
       else a = kw;
       mfma_s<QT, KV8>(s[0], a, qf[0][kk], kk == 0);
       mfma_s<QT>(s[1], a, qf[1][kk], kk == 0);
@@ -357,7 +361,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
 
   // V^T fragment n = (d block n / 2, key half n % 2)
   auto vt_read = [&](uint32_t vls, int n) {
-    if constexpr (KV8) return read_vt8<F8>(smem + ((vls + (n & 1) * 16 * ROWB) ^ ((n >> 1) << 5)));
+    if constexpr (KV8) return read_vt8<QT, F8>(smem + ((vls + (n & 1) * 16 * ROWB) ^ ((n >> 1) << 5)));
     else return read_vt(smem + (vls ^ ((n >> 1) << 6)) + (n & 1) * 16 * ROWB, 8 * ROWB);
   };
 

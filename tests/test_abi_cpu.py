@@ -53,12 +53,13 @@ def test_prefill_workspace_sizes():
     ((ops.PA_F16, ops.PA_FP8_E5M2, 256, 816, 24, 4), 0),
     ((ops.PA_F16, ops.PA_FP8_E4M3, 256, 816, 24, 4), 0),
     ((ops.PA_F16, ops.PA_FP8_E4M3, 64, 16, 8, 2), 0),
-    ((ops.PA_BF16, ops.PA_FP8_E4M3, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
+    ((ops.PA_BF16, ops.PA_FP8_E4M3, 128, 16, 8, 8), 0),
     ((ops.PA_FP8_E4M3, ops.PA_FP8_E4M3, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
     ((ops.PA_F16, 5, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
     ((ops.PA_F32, ops.PA_F32, 64, 16, 4, 1), 0),
     ((ops.PA_F16, ops.PA_F16, 96, 48, 6, 2), 0),
-    ((ops.PA_BF16, ops.PA_FP8_E5M2, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
+    ((ops.PA_BF16, ops.PA_FP8_E5M2, 128, 16, 8, 8), 0),
+    ((ops.PA_F32, ops.PA_FP8_E5M2, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
     ((ops.PA_F16, ops.PA_BF16, 128, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
     ((ops.PA_F16, ops.PA_F16, 100, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),
     ((ops.PA_F16, ops.PA_F16, 512, 16, 8, 8), ops.PA_ERR_UNSUPPORTED),

@@ -68,12 +68,13 @@ def test_kv_write_same_dtype_is_an_exact_copy(kind, layout):
     assert np.array_equal(raw(d["k"]), ko) and np.array_equal(raw(d["v"]), vo)
 
 
+@pytest.mark.parametrize("src", ["f16", "bf16"])
 @pytest.mark.parametrize("fmt,k_scale,v_scale", [("e5m2", 1.0, 1.0), ("e5m2", 0.5, 3.0), ("e5m2", 0.0078125, 1.7),
                                                  ("e4m3", 1.0, 1.0), ("e4m3", 0.01, 250.0), ("e4m3", 0.3, 0.7)])
-def test_kv_write_fp8_quantisation_is_bit_exact(fmt, k_scale, v_scale):
-    case = gen.make_case(f"kvw_{fmt}", q_kind="f16", kv_kind=fmt, seed=63, k_scale=k_scale, v_scale=v_scale,
+def test_kv_write_fp8_quantisation_is_bit_exact(fmt, k_scale, v_scale, src):
+    case = gen.make_case(f"kvw_{fmt}_{src}", q_kind=src, kv_kind=fmt, seed=63, k_scale=k_scale, v_scale=v_scale,
                          **dict(CASE, head_dim=256, page_size=64))
-    kn, vn = new_rows(case, "f16", 64, specials=True)
+    kn, vn = new_rows(case, src, 64, specials=True)
     d = run_write(case, kn, vn)
     ko, vo = oracle.write_kv(raw(case.k_pool), raw(case.v_pool), kn.float().numpy(), vn.float().numpy(),
                              case.cu_seqlens_q, case.seq_lens, case.block_tables, fp8=fmt, k_scale=k_scale,

@@ -3,8 +3,6 @@
 separate calls on the two sub-batches, bit for bit (the same work items and
 kernel code), and against the fp64 oracle."""
 
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -12,16 +10,9 @@ import torch
 import oracle
 from paged_attention_prefill_amd import inputs as gen
 from paged_attention_prefill_amd import ops
+from parity_bars import compare, say
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2, "e4m3": 5e-2}
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
 
 def bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
@@ -98,15 +89,8 @@ def test_mixed_step_equals_separate_calls_and_oracle(qk, kvk, D, Hq, Hkv, P, sp,
     ref, rl = oracle.paged_attention(gen.to_numpy64(c.q), k, v, c.cu_seqlens_q, c.seq_lens, c.block_tables, c.scale,
                                      window_left=host["window_left"], sinks=host["sinks"], softcap=host["softcap"],
                                      alibi_slopes=host["alibi_slopes"])
-    got = out.float().cpu().numpy().astype(np.float64)
     kind = kvk if kvk in ("e5m2", "e4m3") else qk
-    err = float(np.abs(got - ref).max())
-    say(f"    max|err| vs oracle {err:.3e} (bar {TOL[kind]})")
-    assert np.isfinite(got).all() and err <= TOL[kind]
-    gl = lse.cpu().numpy().astype(np.float64)
-    fin = np.isfinite(rl)
-    assert (np.isfinite(gl) == fin).all()
-    assert float(np.abs(gl[fin] - rl[fin]).max()) <= 1e-2 * max(1.0, float(np.abs(rl[fin]).max()))
+    compare("mixed step vs oracle", kind, out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
 
 
 def test_mixed_step_with_only_one_kind_of_row():

@@ -9,8 +9,6 @@ alone would be loose).  Bitwise checks: a decode row alone vs in a batch; page
 permutation, page size and KV layout leave outputs unchanged.
 """
 
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -18,17 +16,9 @@ import torch
 import oracle
 from paged_attention_prefill_amd import inputs as gen
 from paged_attention_prefill_amd import ops
+from parity_bars import RMS_BAR, TOL, compare, say  # noqa: F401
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2, "e4m3": 5e-2}
-RMS_BAR = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e5m2": 2e-2, "e4m3": 2e-2}
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -77,29 +67,6 @@ def gpu_decode(case, d=None, splits=None, max_q=None):
                                    v_head_scales=d.get("v_head_scales"))
     torch.cuda.synchronize()
     return out, lse
-
-
-def compare(name, kind, got, ref, got_lse=None, ref_lse=None):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
-    assert np.isfinite(got).all(), f"{name}: non-finite output"
-    err = np.abs(got - ref)
-    mx = float(err.max()) if err.size else 0.0
-    rel = mx / max(float(np.abs(ref).max()), 1e-30) if err.size else 0.0
-    rms = float(np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)) if err.size else 0.0
-    say(f"  {name}: max|err|={mx:.3e} max|err|/max|ref|={rel:.3e} rms ratio={rms:.3e} (bar {TOL[kind]})")
-    assert mx <= TOL[kind], f"{name}: max-abs error {mx} > {TOL[kind]}"
-    assert rms <= RMS_BAR[kind], f"{name}: rms ratio {rms} > {RMS_BAR[kind]}"
-    if got_lse is not None:
-        gl = np.asarray(got_lse, np.float64)
-        rl = np.asarray(ref_lse, np.float64)
-        assert (np.isfinite(gl) == np.isfinite(rl)).all(), f"{name}: lse -inf pattern differs"
-        fin = np.isfinite(rl)
-        if fin.any():
-            lerr = float(np.abs(gl[fin] - rl[fin]).max())
-            say(f"  {name}: lse max|err|={lerr:.3e}")
-            assert lerr <= max(TOL[kind], 1e-4), f"{name}: lse error {lerr}"
 
 
 # ------------------------------------------------------------------ tiny fp32
@@ -436,42 +403,99 @@ def test_fp8_head_dims_and_page_sizes(D, P):
     compare(f"fp8 decode D={D} P={P}", "e5m2", out.float().cpu().numpy(), ref[70:75], lse.cpu().numpy(), rl[70:75])
 
 
-# ------------------------------------------------------------------ full-size workloads (sampled rows)
+@pytest.mark.parametrize("fmt,D,P", [("e5m2", 256, 64), ("e4m3", 256, 816), ("e5m2", 128, 32), ("e4m3", 64, 16),
+                                     ("e5m2", 160, 48)])
+def test_bf16_queries_with_fp8_kv(fmt, D, P):
+    """bf16 q and out over fp8 KV (widened to bf16 in the kernels): prefill with
+    1 and 3 parts, the decode of the small-q rows, and a verify row bit for bit
+    equal to its token-wise expansion, against the oracle fed the decoded values."""
+    c = gen.make_case(f"bf16_{fmt}_D{D}_P{P}", q_lens=[70, 5, 1], seq_lens=[700, 1300, 333], num_q_heads=12,
+                      num_kv_heads=2, head_dim=D, page_size=P, q_kind="bf16", kv_kind=fmt, seed=D + P + 5,
+                      k_scale=0.75, v_scale=1.5)
+    ref, rl = run_oracle(c)
+    for splits in (1, 3):
+        out, lse = gpu_prefill(c, splits=splits)
+        compare(f"bf16/{fmt} prefill D={D} P={P} S={splits}", fmt, out, ref, lse, rl)
+    dec = gen.select_seqs(c, [1, 2])
+    out, lse = gpu_decode(dec, splits=8, max_q=5)
+    compare(f"bf16/{fmt} decode D={D} P={P}", fmt, out.float().cpu().numpy(), ref[70:], lse.cpu().numpy(), rl[70:])
+    ver = gen.select_seqs(c, [1])
+    ser = gen.expand_row(ver, 0)
+    out_v, lse_v = gpu_decode_fixed(ver, part_keys=256, parts=7, max_q=5)
+    out_s, lse_s = gpu_decode_fixed(ser, part_keys=256, parts=6, max_q=1)  # both cover the 1300 keys
+    assert torch.equal(bits(out_v), bits(out_s)) and torch.equal(bits(lse_v), bits(lse_s))
 
-def _sample_rows(case, n, seed, tokens=None):
-    rng = np.random.default_rng(seed)
-    toks = rng.integers(0, case.total_q, n) if tokens is None else np.asarray(tokens)
-    heads = rng.integers(0, case.num_q_heads, len(toks))
-    # always include the first and last rows of every sequence
-    extra = []
-    for b in range(case.num_seqs):
-        t0, t1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
-        if t1 > t0:
-            extra += [(t0, 0), (t1 - 1, case.num_q_heads - 1)]
-    rows = np.concatenate([np.stack([toks, heads], 1), np.array(extra, dtype=np.int64).reshape(-1, 2)])
-    return rows
+
+FP8_FINITE = {"e5m2": [b for b in range(256) if (b & 0x7F) < 0x7C], "e4m3": [b for b in range(256) if (b & 0x7F) != 0x7F]}
+
+
+@pytest.mark.parametrize("qk", ["f16", "bf16"])
+@pytest.mark.parametrize("fmt,D", [("e5m2", 256), ("e4m3", 256), ("e5m2", 128), ("e4m3", 64)])
+def test_fp8_values_widen_exactly(qk, fmt, D):
+    """A row that sees one key outputs that key's value exactly (its weight is 1,
+    the sum 1, v_scale 1), so the first token of a chunk without prefix, and a
+    q=1 row of length 1, give the decoded fp8 values of that key exactly:
+    every finite code of the format goes through the kernels' widening to fp16
+    or bf16, in the prefill and in the decode kernels."""
+    c = gen.make_case(f"widen_{qk}_{fmt}_{D}", q_lens=[40, 1], seq_lens=[40, 1], num_q_heads=4, num_kv_heads=2,
+                      head_dim=D, page_size=16, q_kind=qk, kv_kind=fmt, seed=D + 1)
+    codes = np.array(FP8_FINITE[fmt], dtype=np.uint8)
+    for b in range(2):  # key 0 of each sequence holds the codes, shifted per head
+        page = int(c.block_tables[b, 0])
+        for h in range(2):
+            row = np.roll(np.resize(codes, D), 37 * h + 101 * b)
+            c.v_pool[page, 0, h] = torch.from_numpy(row)
+    dk = oracle.dequantize_pool(gen.to_numpy64(c.v_pool, fmt), fmt, 1.0)
+    want = {b: torch.from_numpy(np.stack([dk[int(c.block_tables[b, 0]), 0, h // 2] for h in range(4)])).to(
+        {"f16": torch.float16, "bf16": torch.bfloat16}[qk]) for b in range(2)}
+    out, _ = gpu_prefill(gen.select_seqs(c, [0]), splits=1)
+    # values compared exactly (not bits: the accumulation turns the code for -0 into +0)
+    got = torch.from_numpy(out[0]).to(want[0].dtype)
+    bad = torch.nonzero(got.float() != want[0].float())
+    for h, j in bad[:8].tolist():
+        say(f"  prefill head {h} d {j}: got {float(got[h, j])!r} want {float(want[0][h, j])!r}")
+    assert len(bad) == 0, f"prefill widening: {len(bad)} values differ"
+    od, _ = gpu_decode(gen.select_seqs(c, [1]), splits=4, max_q=1)
+    got = od[0].cpu()
+    bad = torch.nonzero(got.float() != want[1].float())
+    for h, j in bad[:8].tolist():
+        say(f"  decode head {h} d {j}: got {float(got[h, j])!r} want {float(want[1][h, j])!r}")
+    assert len(bad) == 0, f"decode widening: {len(bad)} values differ"
+
+
+# ------------------------------------------------------------------ full-size workloads (every row)
+
+
+@pytest.fixture(scope="module")
+def long_chunk_ref():
+    """The 2048-token chunk after 150,000 cached tokens and the q=1 row over the
+    same cache, with the oracle's output for every (token, head) row of both."""
+    c = gen.long_chunk()
+    pre, dec = gen.select_seqs(c, [0]), gen.select_seqs(c, [1])
+    k, v = oracle_pools(pre)
+    say(f"  oracle: all {pre.total_q} x {pre.num_q_heads} rows of the long chunk ...")
+    ref, rl = run_oracle(pre, pools=(k, v))
+    rd, rld = run_oracle(dec, pools=(k, v))
+    return pre, dec, ref, rl, rd, rld
 
 
 @pytest.mark.parametrize("splits", [1, 0])
-def test_long_chunk_prefill_sampled(splits):
-    c = gen.long_chunk()
-    pre = gen.select_seqs(c, [0])
-    d = gen.to_device(pre)
-    out, lse = gpu_prefill(pre, d, splits=splits)
-    rows = _sample_rows(pre, 48, seed=splits)
-    k, v = oracle_pools(pre)
-    ref, rl = run_oracle(pre, rows=rows, pools=(k, v))
-    compare(f"long chunk S={splits} (sampled {len(rows)})", "f16", out[rows[:, 0], rows[:, 1]], ref,
-            lse[rows[:, 0], rows[:, 1]], rl)
-    # the q=1 decode row over the same cache
-    dec = gen.select_seqs(c, [1])
-    od, ld = gpu_decode(dec, splits=64, max_q=1)
-    rd, rld = run_oracle(dec, pools=(k, v))
-    compare("long chunk decode row", "f16", od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
+def test_long_chunk_prefill_every_row(long_chunk_ref, splits):
+    """Every output and lse of the long chunk, unsplit and at the automatic part
+    count (4 on 256 compute units), against the oracle."""
+    pre, dec, ref, rl, rd, rld = long_chunk_ref
+    out, lse = gpu_prefill(pre, splits=splits)
+    compare(f"long chunk S={splits} (all {ref.shape[0] * ref.shape[1]} rows)", "f16", out, ref, lse, rl)
+    if splits == 1:  # the q=1 decode row over the same cache
+        od, ld = gpu_decode(dec, splits=64, max_q=1)
+        compare("long chunk decode row", "f16", od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
 
 
 @pytest.mark.parametrize("kv_kind", ["f16", "e5m2"])
-def test_mixed_step_sampled(kv_kind):
+def test_mixed_step_every_row(kv_kind):
+    """The mixed step: the verify row (q=5 at 240,000 keys, 64 parts) and every
+    row of the 784-token chunk after 104,000 (automatic parts) against the oracle,
+    then the same step as one pa_mixed_step call, bit for bit."""
     c = gen.mixed_step(kv_kind=kv_kind)
     k, v = oracle_pools(c)
     ver = gen.select_seqs(c, [0])
@@ -480,10 +504,10 @@ def test_mixed_step_sampled(kv_kind):
     compare(f"mixed verify row {kv_kind}", kv_kind, od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
     chunk = gen.select_seqs(c, [1])
     out, lse = gpu_prefill(chunk, splits=0)
-    rows = _sample_rows(chunk, 32, seed=5)
-    ref, rl = run_oracle(chunk, rows=rows, pools=(k, v))
-    compare(f"mixed chunk {kv_kind} (sampled {len(rows)})", kv_kind, out[rows[:, 0], rows[:, 1]], ref,
-            lse[rows[:, 0], rows[:, 1]], rl)
+    say(f"  oracle: all {chunk.total_q} x {chunk.num_q_heads} rows of the chunk ...")
+    ref, rl = run_oracle(chunk, pools=(k, v))
+    del k, v
+    compare(f"mixed chunk {kv_kind} (all {ref.shape[0] * ref.shape[1]} rows)", kv_kind, out, ref, lse, rl)
     # the whole step as one pa_mixed_step call (the launch bench.py times as
     # mixed_step_fused): the same bits as the two calls above
     d = gen.to_device(c)

@@ -5,11 +5,9 @@ ratio, a page size, ragged query and key lengths (some rows with more query
 tokens than keys, some empty), a part count and a combination of the options
 (window, sinks, softcap, ALiBi), then checks the prefill of the whole batch
 and the split-KV decode of its small-q rows (proportional or absolute parts)
-against the oracle with the same bars as the other parity tests.  Sizes stay
+against the oracle with the bars of parity_bars.py (max-abs, rms ratio and lse).  Sizes stay
 small enough for the oracle to finish each case in about a second.
 """
-
-import sys
 
 import numpy as np
 import pytest
@@ -18,17 +16,12 @@ import torch
 import oracle
 from paged_attention_prefill_amd import inputs as gen
 from paged_attention_prefill_amd import ops
+from parity_bars import compare, say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e5m2": 5e-2, "e4m3": 5e-2}
 KINDS = [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"), ("f16", "e5m2"), ("f16", "e4m3")]
 PAGES = [16, 32, 48, 64, 128, 816]
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
 
 
 def draw(seed):
@@ -63,19 +56,6 @@ def draw(seed):
                 splits=splits, parts=parts, part_keys=part_keys)
 
 
-def check(name, kind, got, ref, got_lse, ref_lse):
-    got = np.asarray(got, np.float64)
-    assert np.isfinite(got).all(), f"{name}: non-finite output"
-    err = float(np.abs(got - ref).max()) if got.size else 0.0
-    say(f"    {name}: max|err| {err:.3e} (bar {TOL[kind]})")
-    assert err <= TOL[kind], f"{name}: {err} > {TOL[kind]}"
-    gl = np.asarray(got_lse, np.float64)
-    fin = np.isfinite(ref_lse)
-    assert (np.isfinite(gl) == fin).all(), f"{name}: lse finiteness differs"
-    if fin.any():
-        assert float(np.abs(gl[fin] - ref_lse[fin]).max()) <= 1e-2 * max(1.0, float(np.abs(ref_lse[fin]).max()))
-
-
 @pytest.mark.parametrize("seed", range(64))
 def test_random_configuration(seed):
     c = draw(seed)
@@ -103,7 +83,7 @@ def test_random_configuration(seed):
                                  case.scale, k_scale=case.k_scale, v_scale=case.v_scale, num_kv_splits=c["splits"],
                                  return_lse=True, **dev)
     torch.cuda.synchronize()
-    check("prefill", kind, out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
+    compare("prefill", kind, out.float().cpu().numpy(), ref, lse.cpu().numpy(), rl)
 
     small = [b for b, q in enumerate(c["q_lens"]) if q <= 16]
     if not small:
@@ -119,4 +99,4 @@ def test_random_configuration(seed):
     torch.cuda.synchronize()
     cu = case.cu_seqlens_q
     idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in small]).astype(np.int64)
-    check("decode", kind, out.float().cpu().numpy(), ref[idx], lse.cpu().numpy(), rl[idx])
+    compare("decode", kind, out.float().cpu().numpy(), ref[idx], lse.cpu().numpy(), rl[idx])

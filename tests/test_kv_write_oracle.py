@@ -2,7 +2,10 @@
 float8_e5m2 conversion and hand-checked values, and the slot arithmetic of the
 write against the oracle's own gather."""
 
+from fractions import Fraction
+
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -47,12 +50,77 @@ def test_e5m2_round_trip_of_every_finite_code():
     assert (back == codes).all()
 
 
-def test_quantize_divides_in_float32():
-    # 1/3 in float32 is below the fp64 third; 0.1 * 3 lands at a tie-free value either way
-    x = np.array([1.0, 0.75, 3.0], dtype=np.float32)
-    got = oracle.quantize_e5m2(x, 3.0)
-    q = x / np.float32(3.0)
-    assert (got == oracle.e5m2_encode(q.astype(np.float64))).all()
+def _round_fraction(q, mant_bits, min_exp):
+    """The binary float nearest to the rational q (ties to the even significand):
+    mant_bits fraction bits, smallest normal exponent min_exp, exact arithmetic."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, min_exp) - mant_bits)
+    n, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and n % 2 == 1):
+        n += 1
+    return sign * n * ulp
+
+
+def _nearest_code(v, fmt):
+    """fp8 code of the exact rational v: nearest finite value of the format,
+    ties to the even code (the values come from the bit-layout decoder, which is
+    pinned against torch on all 256 bytes)."""
+    top = 0x7C if fmt == "e5m2" else 0x7F
+    dec = oracle.e5m2_to_float64 if fmt == "e5m2" else oracle.e4m3_to_float64
+    vals = [Fraction(float(x)) for x in dec(np.arange(top))]
+    a = abs(v)
+    best = min(range(top), key=lambda c: (abs(vals[c] - a), c % 2))
+    return best | (0x80 if v < 0 else 0)
+
+
+# (fmt, source value, scale): the fp32 quotient and the fp64 quotient of these
+# land on different sides of a rounding boundary of the fp8 grid
+DIVERGENT = [("e5m2", 0.000194549560546875, 1.7), ("e5m2", 1.1444091796875e-05, 0.1),
+             ("e5m2", 7.62939453125e-06, 1 / 3), ("e5m2", 2.6702880859375e-05, 0.7),
+             ("e5m2", -2.6702880859375e-05, 0.7), ("e4m3", 0.02490234375, 1.7), ("e4m3", 0.00146484375, 0.1),
+             ("e4m3", 0.0009765625, 1 / 3), ("e4m3", 0.01708984375, 0.7), ("e4m3", -0.00341796875, 0.7)]
+
+
+def _exact_codes(fmt, x, scale):
+    """(code of the quotient rounded to float32, code of it rounded to float64),
+    from the exact rational quotient."""
+    q = Fraction(float(np.float32(x))) / Fraction(float(np.float32(scale)))
+    return _nearest_code(_round_fraction(q, 23, -126), fmt), _nearest_code(_round_fraction(q, 52, -1022), fmt)
+
+
+@pytest.mark.parametrize("fmt,x,scale", DIVERGENT)
+def test_quantize_divides_in_float32(fmt, x, scale):
+    """The reading: byte = fp8 code of the IEEE float32 quotient x / scale.  The
+    expected byte is derived here from the exact rational quotient, rounded to
+    float32 by exact arithmetic; the inputs are chosen so that an fp64 quotient
+    gives another byte, so the test tells the two readings apart."""
+    want32, want64 = _exact_codes(fmt, x, scale)
+    assert want32 != want64
+    got = int(oracle.quantize_fp8(np.array([x], dtype=np.float32), scale, fmt)[0])
+    assert got == want32, (fmt, x, scale, hex(got), hex(want32))
+
+
+def test_quantize_pin_trips_on_fp64_division(monkeypatch):
+    """A planted mistake: the quotient formed in float64 instead of float32."""
+    from oracle import kv_write
+
+    def fp64_quotient(x, scale, fmt="e5m2"):
+        q = np.asarray(x, dtype=np.float32).astype(np.float64) / np.float64(np.float32(scale))
+        return kv_write.fp8_encode(q, fmt)
+    monkeypatch.setattr(oracle, "quantize_fp8", fp64_quotient)
+    tripped = 0
+    for fmt, x, scale in DIVERGENT:
+        try:
+            test_quantize_divides_in_float32(fmt, x, scale)
+        except AssertionError:
+            tripped += 1
+    assert tripped == len(DIVERGENT)
 
 
 def test_write_places_each_token_at_its_slot():
