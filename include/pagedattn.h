@@ -250,6 +250,33 @@ int pa_split_kv_decode_ex(const void *q, int32_t q_dtype, void *out, float *lse,
                           const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Split-KV decode that allocates nothing and takes no workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops and harnesses that forbid allocation).  Computes exactly what
+ * pa_split_kv_decode_ex computes with the same arguments (the same kernels and
+ * partition, so the same bits), but the FP32 records live in a buffer the
+ * library itself holds on each GPU: PA_NOALLOC_SCRATCH_BYTES of device memory
+ * per GPU, reserved when the library's code is loaded on that GPU and kept
+ * until the process ends.  The records of a call need
+ * pa_decode_workspace_bytes(total_q, num_q_heads, head_dim, num_splits) bytes;
+ * a call that needs more returns PA_ERR_WORKSPACE without launching.  out must
+ * not be NULL (the records cannot be handed out); lse nullable.  Nothing in the
+ * buffer has to start at zero (every record the merge reads is written by the
+ * same call's first pass).  The buffer is shared by every call on one GPU:
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads) race on it and must be ordered by the caller.  The first call on a
+ * device looks the buffer's address up (hipGetSymbolAddress, no allocation
+ * and no stream work).  Other arguments and errors as pa_split_kv_decode_ex.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int pa_split_kv_decode_noalloc(const void *q, int32_t q_dtype, void *out, float *lse,
+                               const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                               const int32_t *block_tables, int32_t num_rows, int32_t max_pages_per_seq,
+                               int32_t total_q, int32_t max_q_per_row, int32_t num_q_heads,
+                               const pa_kv_cache *kv, float scale, int32_t num_splits, int32_t part_keys,
+                               const pa_attn_options *opts, void *stream);
+
+/*
  * One mixed step: small-q rows (decode / MTP verify, q <= PA_DECODE_MAX_Q) and
  * prefill chunks over one KV cache in one attention launch (1CatAI/1Cat-vLLM
  * PR #1279: a step carries chunks next to decode and verify rows; rows up to

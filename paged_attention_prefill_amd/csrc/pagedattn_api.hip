@@ -688,6 +688,62 @@ int pa_split_kv_decode_ex(const void* q, int32_t q_dtype, void* out, float* lse,
                      workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// The FP32 records of pa_split_kv_decode_noalloc: a buffer the library owns
+// on every GPU it runs on (a device-code variable, loaded with the library's
+// code object and held until the process ends), so that the call allocates
+// nothing.  Host code never uses the name itself (on the host it stands for
+// a host-side handle): its device address, looked up once per device with
+// that device current, is what the kernels get.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device; no allocation, no stream work).
+int scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return PA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int pa_split_kv_decode_noalloc(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
+                               const int32_t* seq_lens, const int32_t* block_tables, int32_t num_rows,
+                               int32_t max_pages_per_seq, int32_t total_q, int32_t max_q_per_row,
+                               int32_t num_q_heads, const pa_kv_cache* kv, float scale, int32_t num_splits,
+                               int32_t part_keys, const pa_attn_options* opts, void* stream) {
+  if (out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "out is NULL (the records stay in the library's buffer)");
+  if (kv == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (total_q < 0 || num_q_heads < 1 || num_splits < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative total_q, or num_q_heads / num_splits < 1");
+  const size_t need = pa_decode_workspace_bytes(total_q, num_q_heads, kv->head_dim, num_splits);
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE, "the records need %zu bytes, more than the %zu of the library's buffer", need,
+                (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (num_rows > 0 && total_q > 0) {
+    const int st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_call(q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, num_rows, max_pages_per_seq,
+                     total_q, max_q_per_row, num_q_heads, kv, scale, num_splits, part_keys, opts, ws,
+                     (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_tokens, int32_t num_heads,
                     int32_t head_dim, void* out, int32_t out_dtype, float* out_lse, void* stream) {
   if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 2 || head_dim > 256 || head_dim % 2)

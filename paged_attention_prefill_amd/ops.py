@@ -73,6 +73,8 @@ def lib():
         L.pa_paged_prefill_ex.argtypes = L.pa_paged_prefill.argtypes[:15] + [ctypes.POINTER(AttnOptions), _P, _SZ, _P]
         L.pa_split_kv_decode_ex.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, ctypes.POINTER(AttnOptions),
                                                                               _P, _SZ, _P]
+        L.pa_split_kv_decode_noalloc.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, ctypes.POINTER(AttnOptions),
+                                                                                   _P]
         L.pa_mixed_step.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), ctypes.c_float,
                                     _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(AttnOptions), _P, _SZ, _P]
         L.pa_mixed_workspace_bytes.argtypes = [_I] * 6
@@ -89,6 +91,7 @@ def lib():
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
         for name in ("pa_paged_prefill", "pa_split_kv_decode", "pa_split_kv_decode_fixed", "pa_merge_states",
+                     "pa_split_kv_decode_noalloc",
                      "pa_write_kv", "pa_paged_prefill_ex", "pa_split_kv_decode_ex", "pa_mixed_step",
                      "pa_check_supported",
                      "pa_validate_metadata", "pa_prefill_auto_splits", "pa_status_string", "pa_version"):
@@ -266,6 +269,29 @@ def split_kv_decode(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, m
     if not merge:
         return _partials_view(workspace, total_q, Hq, D, num_splits)
     return (out, lse) if return_lse or lse is not None else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # PA_NOALLOC_SCRATCH_BYTES of include/pagedattn.h
+
+
+def split_kv_decode_noalloc(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, max_q_per_row, scale, out,
+                            *, num_splits=16, part_keys=0, k_scale=1.0, v_scale=1.0, lse=None, stream=None,
+                            k_head_scales=None, v_head_scales=None, sinks=None, window_left=-1, softcap=0.0,
+                            alibi_slopes=None):
+    """pa_split_kv_decode_noalloc: split_kv_decode into the caller's out (and lse)
+    with the records in the library's own device buffer; no workspace, nothing
+    allocated by the library or by this wrapper."""
+    total_q, Hq, D = q.shape
+    if not q.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
+    kv = kv_cache(k_pages, v_pages, k_scale, v_scale, k_head_scales, v_head_scales)
+    opts = _options(Hq, sinks, window_left, softcap, alibi_slopes)
+    _check(lib().pa_split_kv_decode_noalloc(
+        _ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
+        _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), int(seq_lens.numel()),
+        block_tables.shape[-1], total_q, int(max_q_per_row), Hq, ctypes.byref(kv), float(scale), int(num_splits),
+        int(part_keys), opts[0] if opts else None, _stream(stream)))
+    return (out, lse) if lse is not None else out
 
 
 def mixed_workspace_bytes(total_q, decode_tokens, num_q_heads, head_dim, decode_splits, prefill_splits):

@@ -161,6 +161,25 @@ def test_decode_rejects_long_rows_and_small_workspace():
     assert dec(ws=0x80004, ws_bytes=need) == ops.PA_ERR_WORKSPACE  # misaligned
 
 
+def test_noalloc_decode_checks_before_any_device_call():
+    """pa_split_kv_decode_noalloc rejects a NULL out and records past its buffer
+    before it touches a device (no GPU here); the buffer size matches the header."""
+    L = ops.lib()
+    kv = _fake_kv()
+    text = open(ops.HEADER_PATH).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)" in text
+    assert ops.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+
+    def dec(out=0x40000, total_q=4, splits=16):
+        return L.pa_split_kv_decode_noalloc(0x30000, ops.PA_F16, out, None, 0x50000, 0x60000, 0x70000, 4, 4,
+                                            total_q, 1, 8, ctypes.byref(kv), 0.1, splits, 0, None, None)
+    assert dec(out=None) == ops.PA_ERR_INVALID_ARGUMENT
+    # 4096 tokens x 8 heads x 4096 parts x 130 floats: past the 64 MiB buffer
+    assert ops.decode_workspace_bytes(4096, 8, 128, 4096) > ops.NOALLOC_SCRATCH_BYTES
+    assert dec(total_q=4096, splits=4096) == ops.PA_ERR_WORKSPACE
+    assert "buffer" in L.pa_last_error().decode()
+
+
 def test_fixed_part_decode_rejects_bad_part_sizes():
     L = ops.lib()
     kv = _fake_kv()
