@@ -171,8 +171,83 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     }
   }
 
+  const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
   f32x16_t oacc[RB][NDB];
   float m[RB], lsum[RB];
+
+  // ---- epilogue: o = O / l into out (+ lse), or the part's FP32 record.
+  // ZERO: the group sees no key of its part, so every row gets o = 0 and lse
+  // -inf (or its sink) without reading the accumulators.
+  auto epilogue = [&](auto zero_tag) {
+    constexpr bool ZERO = decltype(zero_tag)::value;
+    // the lane index, the row offsets and the output factor formed again here
+    // (mbcnt, a scalar load), so that nothing of the epilogue is kept alive
+    // (in scratch memory) across the tile loop
+    int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane_e));
+    const int hi = lane_e >> 5, r32 = lane_e & 31;
+    const float out_scale = head_v_scale(p, kvh);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float ltot = 0.0f, mrow = kNegInf;
+      if constexpr (!ZERO) ltot = lsum[rb] + __shfl_xor(lsum[rb], 32), mrow = m[rb];
+      const int prow = wrow0 + rb * 32 + r32;
+      if (prow >= nrows) continue;
+      const int tok = prow / g;
+      const int hq = kvh * g + (prow - tok * g);
+      float inv, lse_nat;
+      final_row(p.write_partial ? nullptr : p.sinks, hq, mrow, ltot, out_scale, inv, lse_nat);
+      const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
+      // element i of accumulator block db, normalised
+      auto o = [&](int db, int i) {
+        if constexpr (ZERO) return 0.0f;
+        else return oacc[rb][db][i] * inv;
+      };
+      if (p.write_partial) {
+        float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int d = db * 32 + 8 * rr + 4 * hi;
+            if (d < p.head_dim) {
+              float2 a = {o(db, 4 * rr + 0), o(db, 4 * rr + 1)};
+              float2 b = {o(db, 4 * rr + 2), o(db, 4 * rr + 3)};
+              *(float2*)(rec + d) = a;
+              *(float2*)(rec + d + 2) = b;
+            }
+          }
+        }
+        if (hi == 0) {
+          float2 t = {lse_nat, 0.0f};
+          *(float2*)(rec + p.head_dim) = t;
+        }
+      } else {
+        QT* orow = (QT*)p.out + rowidx * p.head_dim;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int d = db * 32 + 8 * rr + 4 * hi;
+            if (d < p.head_dim) {
+              uint2 v = {Mf<QT>::pack2(o(db, 4 * rr + 0), o(db, 4 * rr + 1)),
+                         Mf<QT>::pack2(o(db, 4 * rr + 2), o(db, 4 * rr + 3))};
+              *(uint2*)(orow + d) = v;
+            }
+          }
+        }
+        if (p.lse != nullptr && hi == 0) p.lse[rowidx] = lse_nat;
+      }
+    }
+  };
+  // Written apart so that the accumulators' zero start values are not kept
+  // alive across the tile loop for this path (the register allocator parked
+  // all 256 of them in scratch memory to have them here).
+  if (ntiles == 0) {
+    epilogue(std::true_type());
+    return;
+  }
+
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegInf;
@@ -182,7 +257,6 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     acc_fence<NDB>(oacc[rb]);
   }
 
-  const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
   // The modifier instantiation runs the tiles from the last one down: under
   // ALiBi a row's biased scores grow with the key, so in ascending order its
   // running max would rise by up to slope * 32 every tile and rescale the
@@ -474,53 +548,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     pv((ntiles - 1) % NST);
   }
 
-  // ---- epilogue
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
-    const int prow = wrow0 + rb * 32 + r32;
-    if (prow >= nrows) continue;
-    const int tok = prow / g;
-    const int hq = kvh * g + (prow - tok * g);
-    float inv, lse_nat;
-    final_row(p.write_partial ? nullptr : p.sinks, hq, m[rb], ltot, out_scale, inv, lse_nat);
-    const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
-    if (p.write_partial) {
-      float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int d = db * 32 + 8 * rr + 4 * hi;
-          if (d < p.head_dim) {
-            float2 a = {oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv};
-            float2 b = {oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv};
-            *(float2*)(rec + d) = a;
-            *(float2*)(rec + d + 2) = b;
-          }
-        }
-      }
-      if (hi == 0) {
-        float2 t = {lse_nat, 0.0f};
-        *(float2*)(rec + p.head_dim) = t;
-      }
-    } else {
-      QT* orow = (QT*)p.out + rowidx * p.head_dim;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int d = db * 32 + 8 * rr + 4 * hi;
-          if (d < p.head_dim) {
-            uint2 v = {Mf<QT>::pack2(oacc[rb][db][4 * rr + 0] * inv, oacc[rb][db][4 * rr + 1] * inv),
-                       Mf<QT>::pack2(oacc[rb][db][4 * rr + 2] * inv, oacc[rb][db][4 * rr + 3] * inv)};
-            *(uint2*)(orow + d) = v;
-          }
-        }
-      }
-      if (p.lse != nullptr && hi == 0) p.lse[rowidx] = lse_nat;
-    }
-  }
+  epilogue(std::false_type());
 }
 
 // LDS of the body: NST stages of one K and one V tile.
