@@ -81,9 +81,9 @@ class Call:
         self.out = torch.empty_like(d["q"])
         self.lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
         D = case.head_dim
-        if kind == "mixed":  # splits = (prefill parts, decode parts); meta: the small-q rows first
-            m = case.meta
-            nb = ops.mixed_workspace_bytes(case.total_q, m["decode_tokens"], case.num_q_heads, D, splits[1], splits[0])
+        if kind == "mixed":  # splits = (prefill parts, decode parts); the rows are routed by the library
+            nb = ops.mixed_workspace_bytes(case.q_lens, case.max_pages_per_seq, case.num_q_heads, D,
+                                           ops._TORCH_TO_PA[d["q"].dtype], 0, splits[1], splits[0])
         elif kind == "prefill":
             nb = ops.prefill_workspace_bytes(case.total_q, case.num_q_heads, D, splits)
         else:
@@ -99,9 +99,7 @@ class Call:
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         if self.kind == "mixed":
-            m = c.meta
-            ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], m["decode_rows"],
-                           m["decode_tokens"], m["max_q_per_row"], m["max_seqlen_q_prefill"], c.scale,
+            ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], c.q_lens, d["seq_lens"], d["bt"], c.scale,
                            decode_splits=self.splits[1], prefill_splits=self.splits[0], k_scale=c.k_scale,
                            v_scale=c.v_scale, out=self.out, lse=self.lse, workspace=self.ws, stream=stream,
                            **self.opts)
@@ -182,11 +180,11 @@ def build_workload(name):
                 "seq_len": 152048, "kv_dtype": "f16", **opt}
         return desc, [("prefill", pre, "auto"), ("decode", dec, 64)]
     if name == "mixed_step_fused":
-        c = gen.mixed_step(kv_kind="f16")  # sequence 0: the verify row (the small-q row first), 1: the chunk
-        c.meta.update(decode_rows=1, decode_tokens=int(c.cu_seqlens_q[1]), max_q_per_row=int(c.q_lens[0]),
-                      max_seqlen_q_prefill=int(c.q_lens[1]))
-        desc = {"workload": "the mixed step in one attention launch (pa_mixed_step): the verify row q=5 at 240,000 "
-                            "keys and the 784-token chunk after 104,000, fp16, D 256, page 816",
+        c = gen.mixed_step(kv_kind="f16")  # sequence 0: the verify row, 1: the chunk
+        c.meta.update(decode_rows=1)
+        desc = {"workload": "the mixed step as one pa_mixed_step call (rows routed by q on the device, one attention "
+                            "launch): the verify row q=5 at 240,000 keys and the 784-token chunk after 104,000, "
+                            "fp16, D 256, page 816",
                 "num_q_heads": 24, "num_kv_heads": 4, "head_dim": 256, "page_size": 816, "kv_dtype": "f16"}
         return desc, [("mixed", c, "auto")]
     if name == "mixed_step":
@@ -460,6 +458,42 @@ def ceilings(seed=0):
     return 0
 
 
+def crossover(reps=20):
+    """Time one small-q row (q = 1..16 tokens) through the split-KV decode and
+    through the prefill kernel, at the shapes of the mixed step (D 256, GQA 6,
+    fp16) and of the varlen prefill (D 128, GQA 4, bf16), short and long
+    contexts: the q at which the prefill call overtakes the decode call is the
+    routing threshold of a mixed step.  One JSON line per (shape, q)."""
+    stream = torch.cuda.current_stream()
+    shapes = [("D256 GQA 24:4 f16 page 816", 24, 4, 256, 816, "f16"),
+              ("D128 GQA 32:8 bf16 page 32", 32, 8, 128, 32, "bf16")]
+    for name, hq, hkv, D, P, kind in shapes:
+        for L in (2048, 32768, 131072):
+            for q in (1, 2, 3, 4, 5, 6, 8, 10, 12, 16):
+                case = gen.make_case("crossover", q_lens=[q], seq_lens=[L], num_q_heads=hq, num_kv_heads=hkv,
+                                     head_dim=D, page_size=P, q_kind=kind, seed=q + L)
+                d = gen.to_device(case)
+                dec = Call("decode", case, d, 64 if L > 8192 else 16, max_q=q)
+                sp = ops.auto_splits(case.total_q, 1, q, hq, hkv, D, ops._TORCH_TO_PA[case.q.dtype],
+                                     ops._TORCH_TO_PA[case.q.dtype])
+                pre = Call("prefill", case, d, sp)
+                res = {"mode": "crossover", "shape": name, "seq_len": L, "q": q}
+                for tag, c in (("decode", dec), ("prefill", pre)):
+                    for _ in range(3):
+                        c(stream)
+                    torch.cuda.synchronize()
+                    c.times = []
+                    for _ in range(reps):
+                        c(stream, record=True)
+                    torch.cuda.synchronize()
+                    res[f"{tag}_us"] = c.ms_median() * 1e3
+                    res[f"{tag}_splits"] = c.splits
+                res["faster"] = "decode" if res["decode_us"] <= res["prefill_us"] else "prefill"
+                print(json.dumps(res), flush=True)
+                del d, dec, pre
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,10 +504,11 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
                          "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU); "
-                         "ceilings: a pure MFMA loop and a streaming read, measured")
+                         "ceilings: a pure MFMA loop and a streaming read, measured; "
+                         "crossover: one small-q row through the decode and the prefill calls, q = 1..16")
     ap.add_argument("--pmc-dir", default="gpurun_out",
                     help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
@@ -489,6 +524,8 @@ def main():
         return copy_reference(a.steps)
     if a.mode == "ceilings":
         return ceilings()
+    if a.mode == "crossover":
+        return crossover()
     ops.lib()
 
     log(f"building workload {a.workload} ...")

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 2
+#define PA_VERSION 3
 #define PA_DECODE_MAX_Q 16       /* largest q of a decode / verify row */
 #define PA_DECODE_SPLIT_TILE 32  /* keys per tile of the split partition */
 #define PA_PREFILL_MAX_AUTO_SPLITS 16
@@ -277,37 +277,48 @@ int pa_split_kv_decode_noalloc(const void *q, int32_t q_dtype, void *out, float 
                                const pa_attn_options *opts, void *stream);
 
 /*
- * One mixed step: small-q rows (decode / MTP verify, q <= PA_DECODE_MAX_Q) and
- * prefill chunks over one KV cache in one attention launch (1CatAI/1Cat-vLLM
- * PR #1279: a step carries chunks next to decode and verify rows; rows up to
- * the decode limit take the split-KV path, longer ones the prefill kernel),
- * followed by the merge pass of each part.
- *   The batch is ordered: sequences [0, num_decode_rows) are the small-q rows
- *   (their tokens [0, decode_tokens), decode_tokens = cu_seqlens_q[
- *   num_decode_rows], each row <= max_q_per_row tokens), the rest are chunks
- *   (max_seqlen_q their longest).  The small-q rows are computed exactly as by
- *   pa_split_kv_decode_ex(decode_splits, decode_part_keys) and the chunks as
- *   by pa_paged_prefill_ex(prefill_splits; 0 = auto from the chunks alone,
- *   capped by the workspace) on the sub-batches: the same work items and
- *   kernels' code, so the results have the same bits.
- *   Head dims padded to 256 with fp16 / bf16 / fp8 KV and no window or score
- *   modifier run both in one grid (prefill groups first; the decode groups
- *   fill the compute units the prefill's last wave leaves idle); other shapes
- *   and options run the two pass-1 kernels back to back.  out must not be NULL; lse nullable; opts as for the _ex
- *   calls (both parts).
- *   Workspace: pa_mixed_workspace_bytes(total_q, decode_tokens, ...), 8-byte
- *   aligned: the chunks' records (indexed by token like the whole batch, when
- *   the chunks are split), then the small-q rows' records.
- *   Device metadata is trusted as for the other calls: decode_tokens must
- *   equal cu_seqlens_q[num_decode_rows].
+ * One mixed step: small-q rows (decode / MTP verify) and prefill chunks over
+ * one KV cache, routed by their query length in one call (1CatAI/1Cat-vLLM
+ * PR #1279: a step carries chunks next to decode and verify rows; rows of a
+ * few tokens are expanded token-wise into decode rows, 1CatAI/1Cat-vLLM PR #616
+ * original, "Purpose"; the Turing prefill route starts at a minimum query
+ * length, PR #1279 commit 1).
+ *   The batch is in any order and is described as for pa_paged_prefill_ex,
+ *   plus host_q_lens: a HOST copy of the rows' query lengths (host_q_lens[b]
+ *   = cu_seqlens_q[b+1] - cu_seqlens_q[b], summing to total_q; read during the
+ *   call only).  Every row with 1 <= q <= decode_max_q (0:
+ *   PA_MIXED_DECODE_MAX_Q; at most PA_DECODE_MAX_Q, the decode kernels' limit)
+ *   is computed exactly as by pa_split_kv_decode_ex(decode_splits,
+ *   decode_part_keys) on the small-q rows, the other rows as by
+ *   pa_paged_prefill_ex(prefill_splits; 0 = the automatic count of that call
+ *   on the chunks alone, capped by the workspace) on the chunks: the same
+ *   work items and kernel code, so the same bits.  The default threshold is
+ *   the measured crossover on MI355X: for every q up to 16 (D 256 GQA 6 and
+ *   D 128 GQA 4, 2K to 128K keys) one row takes less time through the decode
+ *   than through the prefill.
+ *   The host counts each class from host_q_lens, which sizes the grids and
+ *   the workspace exactly; on the device a small kernel classifies the rows
+ *   from cu_seqlens_q, gathers the small-q rows' queries and metadata into the
+ *   workspace, the attention runs (head dims padded to 256 with fp16 / bf16 /
+ *   fp8 KV and no window or score modifier: one grid, chunk groups first, the
+ *   decode groups filling the compute units the chunks' last wave leaves
+ *   idle; otherwise the two pass-1 kernels back to back), the merges follow,
+ *   and the small-q rows' outputs are scattered back to their tokens.  out
+ *   must not be NULL; lse nullable; opts as for the _ex calls (both classes).
+ *   Workspace: pa_mixed_workspace_bytes(host_q_lens, ...) bytes, 256-byte
+ *   aligned (prefill_splits 0 sizes it for every automatic count).
+ *   Device metadata is trusted as for the other calls, and must agree with
+ *   host_q_lens (if they disagree, rows are missed, but nothing is written
+ *   outside the workspace and out).
  */
-size_t pa_mixed_workspace_bytes(int32_t total_q, int32_t decode_tokens, int32_t num_q_heads, int32_t head_dim,
+#define PA_MIXED_DECODE_MAX_Q 16
+size_t pa_mixed_workspace_bytes(const int32_t *host_q_lens, int32_t num_seqs, int32_t max_pages_per_seq,
+                                int32_t num_q_heads, int32_t head_dim, int32_t q_dtype, int32_t decode_max_q,
                                 int32_t decode_splits, int32_t prefill_splits);
 int pa_mixed_step(const void *q, int32_t q_dtype, void *out, float *lse, const int32_t *cu_seqlens_q,
-                  const int32_t *seq_lens, const int32_t *block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
-                  int32_t total_q, int32_t num_q_heads, const pa_kv_cache *kv, float scale,
-                  int32_t num_decode_rows, int32_t decode_tokens, int32_t max_q_per_row, int32_t decode_splits,
-                  int32_t decode_part_keys, int32_t max_seqlen_q, int32_t prefill_splits,
+                  const int32_t *host_q_lens, const int32_t *seq_lens, const int32_t *block_tables, int32_t num_seqs,
+                  int32_t max_pages_per_seq, int32_t total_q, int32_t num_q_heads, const pa_kv_cache *kv, float scale,
+                  int32_t decode_max_q, int32_t decode_splits, int32_t decode_part_keys, int32_t prefill_splits,
                   const pa_attn_options *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 SOURCES = ["attn_mixed.hip", "attn_mfma_dma.hip", "attn_prefill_w4.hip", "attn_decode.hip", "attn_mfma.hip",
-           "attn_valu.hip", "merge.hip", "kv_write.hip", "pagedattn_api.hip", "ceilings.hip"]
+           "attn_valu.hip", "merge.hip", "kv_write.hip", "mixed_route.hip", "pagedattn_api.hip", "ceilings.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 64 * WAVES);
 
   const int q0 = p.cu_seqlens_q[seq];
-  const int qlen = p.cu_seqlens_q[seq + 1] - q0;
+  const int qlen = q_end_of(p, seq) - q0;
   const int g = p.group;
   const int nrows = qlen * g;
   const int row0 = qtile * ROWS;

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreadsV) void attn_valu_kernel(const AttnParams p
   const int seq = wi.seqpos;
 
   const int q0 = p.cu_seqlens_q[seq];
-  const int qlen = p.cu_seqlens_q[seq + 1] - q0;
+  const int qlen = q_end_of(p, seq) - q0;
   const int g = p.group;
   const int nrows = qlen * g;
   const int row0 = qtile * kRowsV;

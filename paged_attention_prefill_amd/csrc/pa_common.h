@@ -23,7 +23,8 @@ struct AttnParams {
   void* out;               // [total_q, Hq, D] (written when num_splits == 1 and !force_partial)
   float* lse;              // [total_q, Hq] nullable
   float* partial;          // [total_q, Hq, S, D + 2] when writing partial records
-  const int* cu_seqlens_q; // [B + 1]
+  const int* cu_seqlens_q; // [B + 1]: sequence b's tokens are [cu[b], cu[b + 1]) ...
+  const int* q_end;        // ... or, when set, [cu[b], q_end[b]) (sequences addressed in place)
   const int* seq_lens;     // [B]
   const int* block_tables; // [B, max_pages]
   const void* k_pages;
@@ -47,6 +48,11 @@ struct AttnParams {
   float softcap_l2;           // softcap * log2(e)
   const float* alibi_slopes;  // [Hq] or null (natural units per key of distance)
 };
+
+// One past the last query token of sequence `seq` (see AttnParams::q_end).
+__device__ __forceinline__ int q_end_of(const AttnParams& p, int seq) {
+  return p.q_end != nullptr ? p.q_end[seq] : p.cu_seqlens_q[seq + 1];
+}
 
 // First key visible to the token at key position `pos` under the left window.
 __device__ __forceinline__ int window_lo(const AttnParams& p, int pos) {
@@ -112,6 +118,31 @@ struct KvWriteParams {
   float k_scale, v_scale;  // fp8 cache: byte = fp8(x / scale), scale = k_scale * k_head_scale[h]
   const float* k_head_scale;  // [Hkv] or null
   const float* v_head_scale;
+};
+
+// Routing of a mixed step (mixed_route.hip): what the route kernels read and
+// write, all of the written arrays inside the call's workspace.
+struct RouteParams {
+  const int* cu;        // [B + 1]
+  const int* seq_lens;  // [B]
+  const int* bt;        // [B, max_pages]
+  const char* q;        // [total_q, row_bytes]
+  int B, max_pages, decode_max_q;
+  int n_dec, n_pre, nt_cap;  // rows of each class and small-q tokens (the host's count; every write is bounded by them)
+  int64_t row_bytes;    // one token's q (or out) row, a multiple of 16
+  // small-q rows, compact
+  int* dec_cu;          // [n_dec + 1]
+  int* dec_seq_lens;    // [n_dec]
+  int* dec_src;         // [n_dec]: batch index of compact row i (-1: none)
+  int* dec_tok;         // [nt_cap]: batch token of compact token k (-1: none)
+  int* dec_bt;          // [n_dec, max_pages]
+  char* dec_q;          // [nt_cap, row_bytes]
+  // chunks, in place
+  int* pre_qs;          // [n_pre] first token
+  int* pre_qe;          // [n_pre] one past the last token
+  int* pre_seq_lens;    // [n_pre]
+  int* pre_src;         // [n_pre]
+  int* pre_bt;          // [n_pre, max_pages]
 };
 
 // Block index -> work item.  A group is the query tiles of one (sequence

@@ -323,6 +323,7 @@ static int plan_attention(pa::AttnParams& p, int64_t& nblocks, const void* q, in
   p.lse = lse;
   p.partial = (float*)workspace;
   p.cu_seqlens_q = cu;
+  p.q_end = nullptr;
   p.seq_lens = seq_lens;
   p.block_tables = bt;
   p.k_pages = kv->k_pages;
@@ -515,102 +516,199 @@ int pa_split_kv_decode_fixed(const void* q, int32_t q_dtype, void* out, float* l
                      workspace_bytes, stream);
 }
 
-// Workspace of pa_mixed_step: the prefill records (indexed from token 0 like
-// the whole batch, total_q rows, when the chunks are split), then, 256-byte
-// aligned, the decode records of the decode_tokens small-q tokens.
-static size_t mixed_prefill_region(int32_t total_q, int32_t hq, int32_t d, int32_t prefill_splits) {
-  const size_t b = pa_prefill_workspace_bytes(total_q, hq, d, prefill_splits);
-  return (b + 255) & ~(size_t)255;
+}  // extern "C"
+
+// Workspace of pa_mixed_step, every region 256-byte aligned: the route's int32
+// metadata, the small-q rows' block-table rows and the chunks', the small-q
+// rows' gathered q, their compact out and lse, their FP32 records, then the
+// chunks' records (indexed by batch token, when the chunks are split).
+namespace {
+// The two classes of a batch, counted from the host copy of its query lengths.
+struct MixedSplit {
+  int n_dec = 0, n_pre = 0, max_dec_q = 0, max_pre_q = 0;
+  int64_t dec_tokens = 0, pre_tokens = 0;
+};
+
+struct MixedLayout {
+  size_t meta, dec_bt, pre_bt, dec_q, dec_out, dec_lse, dec_rec, pre_rec, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int mixed_decode_max_q(int32_t decode_max_q) { return decode_max_q == 0 ? PA_MIXED_DECODE_MAX_Q : decode_max_q; }
+
+// Rows with 1 <= q <= dmq are small-q rows, rows with q > dmq chunks, q = 0 neither.
+int mixed_split(const int32_t* host_q_lens, int B, int dmq, MixedSplit& s) {
+  if (host_q_lens == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "host_q_lens is NULL");
+  for (int b = 0; b < B; ++b) {
+    const int q = host_q_lens[b];
+    if (q < 0) return fail(PA_ERR_INVALID_ARGUMENT, "host_q_lens[%d] = %d < 0", b, q);
+    if (q == 0) continue;
+    if (q <= dmq) {
+      ++s.n_dec;
+      s.dec_tokens += q;
+      if (q > s.max_dec_q) s.max_dec_q = q;
+    } else {
+      ++s.n_pre;
+      s.pre_tokens += q;
+      if (q > s.max_pre_q) s.max_pre_q = q;
+    }
+  }
+  return PA_OK;
 }
 
-size_t pa_mixed_workspace_bytes(int32_t total_q, int32_t decode_tokens, int32_t num_q_heads, int32_t head_dim,
+MixedLayout mixed_layout(int64_t total_q, const MixedSplit& s, int64_t max_pages, int64_t hq, int64_t d, int64_t es,
+                         int64_t dsplits, int64_t psplits) {
+  const int64_t nt = s.dec_tokens, nd = s.n_dec, np = s.n_pre;
+  MixedLayout m;
+  size_t o = 0;
+  m.meta = o;
+  o += align256(sizeof(int) * (size_t)(3 * nd + 1 + 4 * np + nt));
+  m.dec_bt = o;
+  o += align256(sizeof(int) * (size_t)(nd * max_pages));
+  m.pre_bt = o;
+  o += align256(sizeof(int) * (size_t)(np * max_pages));
+  m.dec_q = o;
+  o += align256((size_t)(nt * hq * d * es));
+  m.dec_out = o;
+  o += align256((size_t)(nt * hq * d * es));
+  m.dec_lse = o;
+  o += align256(sizeof(float) * (size_t)(nt * hq));
+  m.dec_rec = o;
+  o += align256(sizeof(float) * (size_t)(nt * hq * dsplits * (d + 2)));
+  m.pre_rec = o;
+  if (np > 0 && psplits > 1) o += align256(sizeof(float) * (size_t)(total_q * hq * psplits * (d + 2)));
+  m.total = o;
+  return m;
+}
+}  // namespace
+
+namespace pa {
+hipError_t launch_route(const RouteParams& r, hipStream_t stream);
+hipError_t launch_route_scatter(const int* dec_tok, int nt_cap, const void* dec_out, const float* dec_lse, void* out,
+                                float* lse, int64_t row_bytes, int num_heads, hipStream_t stream);
+}  // namespace pa
+
+extern "C" {
+
+size_t pa_mixed_workspace_bytes(const int32_t* host_q_lens, int32_t num_seqs, int32_t max_pages_per_seq,
+                                int32_t num_q_heads, int32_t head_dim, int32_t q_dtype, int32_t decode_max_q,
                                 int32_t decode_splits, int32_t prefill_splits) {
-  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return mixed_prefill_region(total_q, num_q_heads, head_dim, prefill_splits) +
-         pa_decode_workspace_bytes(decode_tokens, num_q_heads, head_dim, decode_splits);
+  if (num_seqs <= 0 || max_pages_per_seq <= 0 || num_q_heads <= 0 || head_dim <= 0 || decode_splits <= 0 ||
+      decode_max_q < 0 || decode_max_q > PA_DECODE_MAX_Q || prefill_splits < 0 || elem_size(q_dtype) == 0)
+    return 0;
+  MixedSplit s;
+  if (mixed_split(host_q_lens, num_seqs, mixed_decode_max_q(decode_max_q), s) != PA_OK) return 0;
+  const int sp = prefill_splits == 0 ? PA_PREFILL_MAX_AUTO_SPLITS : prefill_splits;
+  return mixed_layout(s.dec_tokens + s.pre_tokens, s, max_pages_per_seq, num_q_heads, head_dim,
+                      (int64_t)elem_size(q_dtype), decode_splits, sp)
+      .total;
 }
 
 int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const int32_t* cu_seqlens_q,
-                  const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs, int32_t max_pages_per_seq,
-                  int32_t total_q, int32_t num_q_heads, const pa_kv_cache* kv, float scale,
-                  int32_t num_decode_rows, int32_t decode_tokens, int32_t max_q_per_row, int32_t decode_splits,
-                  int32_t decode_part_keys, int32_t max_seqlen_q, int32_t prefill_splits,
+                  const int32_t* host_q_lens, const int32_t* seq_lens, const int32_t* block_tables, int32_t num_seqs,
+                  int32_t max_pages_per_seq, int32_t total_q, int32_t num_q_heads, const pa_kv_cache* kv, float scale,
+                  int32_t decode_max_q, int32_t decode_splits, int32_t decode_part_keys, int32_t prefill_splits,
                   const pa_attn_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq,
-                        total_q, max_seqlen_q > max_q_per_row ? max_seqlen_q : max_q_per_row, num_q_heads, kv);
+  if (decode_max_q < 0 || decode_max_q > PA_DECODE_MAX_Q)
+    return fail(PA_ERR_UNSUPPORTED, "decode_max_q must be 0 (the default, %d) or in [1, %d]", PA_MIXED_DECODE_MAX_Q,
+                PA_DECODE_MAX_Q);
+  if (num_seqs < 0 || total_q < 0) return fail(PA_ERR_INVALID_ARGUMENT, "negative size");
+  const int dmq = mixed_decode_max_q(decode_max_q);
+  MixedSplit ms;
+  int st = num_seqs > 0 ? mixed_split(host_q_lens, num_seqs, dmq, ms) : PA_OK;
+  if (st != PA_OK) return st;
+  if (ms.dec_tokens + ms.pre_tokens != total_q)
+    return fail(PA_ERR_INVALID_ARGUMENT, "host_q_lens sum to %lld, total_q is %d",
+                (long long)(ms.dec_tokens + ms.pre_tokens), total_q);
+  const int max_q = ms.max_pre_q > ms.max_dec_q ? ms.max_pre_q : ms.max_dec_q;
+  st = check_common(q, q_dtype, out, cu_seqlens_q, seq_lens, block_tables, num_seqs, max_pages_per_seq, total_q,
+                    max_q, num_q_heads, kv);
   if (st != PA_OK) return st;
   st = check_options(opts);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(PA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
   if (out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
-  if (num_decode_rows < 0 || num_decode_rows > num_seqs || decode_tokens < 0 || decode_tokens > total_q)
-    return fail(PA_ERR_INVALID_ARGUMENT, "num_decode_rows must be in [0, num_seqs] and decode_tokens in [0, total_q]");
-  if (num_decode_rows == 0 && decode_tokens != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "decode_tokens must be 0 without small-q rows");
-  if (num_decode_rows > 0) {
-    if (max_q_per_row < 1 || max_q_per_row > PA_DECODE_MAX_Q)
-      return fail(PA_ERR_UNSUPPORTED, "max_q_per_row must be in [1, %d]", PA_DECODE_MAX_Q);
-    if ((int64_t)decode_tokens > (int64_t)num_decode_rows * max_q_per_row)
-      return fail(PA_ERR_INVALID_ARGUMENT, "decode_tokens %d > num_decode_rows * max_q_per_row", decode_tokens);
-    if (decode_splits < 1 || decode_splits > 4096)
-      return fail(PA_ERR_INVALID_ARGUMENT, "decode_splits must be in [1, 4096]");
-    if (decode_part_keys < 0 || decode_part_keys % PA_DECODE_SPLIT_TILE != 0)
-      return fail(PA_ERR_INVALID_ARGUMENT, "decode_part_keys must be 0 or a positive multiple of %d",
-                  PA_DECODE_SPLIT_TILE);
-  }
+  if (decode_splits < 1 || decode_splits > 4096)
+    return fail(PA_ERR_INVALID_ARGUMENT, "decode_splits must be in [1, 4096]");
+  if (decode_part_keys < 0 || decode_part_keys % PA_DECODE_SPLIT_TILE != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "decode_part_keys must be 0 or a positive multiple of %d",
+                PA_DECODE_SPLIT_TILE);
   if (prefill_splits < 0 || prefill_splits > 64)
     return fail(PA_ERR_INVALID_ARGUMENT, "prefill_splits must be in [0, 64]");
-  const int nd = num_decode_rows, np = num_seqs - num_decode_rows, tp = total_q - decode_tokens;
-  if (np > 0 && tp > 0 && max_seqlen_q < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_seqlen_q must be >= 1");
   if (total_q == 0 || num_seqs == 0) return ok();
   const int D = kv->head_dim;
+  const int64_t es = (int64_t)elem_size(q_dtype);
+  // the chunks' part count: as a prefill call on the chunks alone would pick
+  // it, capped by the workspace
   int sp = prefill_splits;
-  if (np > 0 && tp > 0 && sp == 0) {
-    sp = pa_prefill_auto_splits(tp, np, max_seqlen_q, num_q_heads, kv->num_kv_heads, D, q_dtype, kv->dtype);
+  if (sp == 0 && ms.n_pre > 0) {
+    sp = pa_prefill_auto_splits((int32_t)ms.pre_tokens, ms.n_pre, ms.max_pre_q, num_q_heads, kv->num_kv_heads, D,
+                                q_dtype, kv->dtype);
     if (sp < 0) return sp;
-    // at most the parts the workspace holds next to the decode records
-    const size_t dec = pa_decode_workspace_bytes(decode_tokens, num_q_heads, D, decode_splits);
-    const size_t per = pa_prefill_workspace_bytes(total_q, num_q_heads, D, 2) / 2;
-    const size_t room = (workspace == nullptr || ((uintptr_t)workspace & 7u) || workspace_bytes < dec + 256)
-                            ? 0 : workspace_bytes - dec - 256;
-    if ((size_t)sp > room / per) sp = room / per >= 2 ? (int)(room / per) : 1;
+    while (sp > 1 && (workspace == nullptr ||
+                      mixed_layout(total_q, ms, max_pages_per_seq, num_q_heads, D, es, decode_splits, sp).total >
+                          workspace_bytes))
+      --sp;
   }
   if (sp == 0) sp = 1;
-  const size_t need = pa_mixed_workspace_bytes(total_q, nd > 0 ? decode_tokens : 0, num_q_heads, D,
-                                               nd > 0 ? decode_splits : 1, sp);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 7u)))
-    return fail(PA_ERR_WORKSPACE, "mixed step needs %zu bytes of 8-byte aligned workspace (got %zu)", need,
+  const MixedLayout ml = mixed_layout(total_q, ms, max_pages_per_seq, num_q_heads, D, es, decode_splits, sp);
+  if (workspace == nullptr || workspace_bytes < ml.total || ((uintptr_t)workspace & 255u))
+    return fail(PA_ERR_WORKSPACE, "mixed step needs %zu bytes of 256-byte aligned workspace (got %zu)", ml.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
+  const int nd = ms.n_dec, np = ms.n_pre, nt = (int)ms.dec_tokens;
   char* ws = (char*)workspace;
-  float* ws_pre = (float*)ws;
-  float* ws_dec = (float*)(ws + mixed_prefill_region(total_q, num_q_heads, D, sp));
+  int* meta = (int*)(ws + ml.meta);
+  pa::RouteParams r;
+  r.cu = cu_seqlens_q;
+  r.seq_lens = seq_lens;
+  r.bt = block_tables;
+  r.q = (const char*)q;
+  r.B = num_seqs;
+  r.max_pages = max_pages_per_seq;
+  r.decode_max_q = dmq;
+  r.n_dec = nd;
+  r.n_pre = np;
+  r.nt_cap = nt;
+  r.row_bytes = (int64_t)num_q_heads * D * es;
+  r.dec_cu = meta;
+  r.dec_seq_lens = r.dec_cu + (nd + 1);
+  r.dec_src = r.dec_seq_lens + nd;
+  r.pre_qs = r.dec_src + nd;
+  r.pre_qe = r.pre_qs + np;
+  r.pre_seq_lens = r.pre_qe + np;
+  r.pre_src = r.pre_seq_lens + np;
+  r.dec_tok = r.pre_src + np;
+  r.dec_bt = (int*)(ws + ml.dec_bt);
+  r.pre_bt = (int*)(ws + ml.pre_bt);
+  r.dec_q = ws + ml.dec_q;
   hipStream_t strm = (hipStream_t)stream;
 
-  // the two segments, each planned as its own call; the chunk sequences are
-  // reached through offset metadata pointers (cu_seqlens_q keeps absolute
-  // token indices, so q, out and the prefill records need no offset)
+  // each class planned exactly as its own call on its sub-batch would be
   pa::AttnParams pd, pp;
   int64_t nb_d = 0, nb_p = 0;
-  if (nd > 0 && decode_tokens > 0) {
-    st = plan_attention(pd, nb_d, q, q_dtype, out, lse, cu_seqlens_q, seq_lens, block_tables, nd, max_pages_per_seq,
-                        decode_tokens, max_q_per_row, num_q_heads, kv, scale, decode_splits, decode_part_keys, true,
-                        opts, ws_dec);
+  if (nd > 0) {
+    st = plan_attention(pd, nb_d, r.dec_q, q_dtype, ws + ml.dec_out, (float*)(ws + ml.dec_lse), r.dec_cu,
+                        r.dec_seq_lens, r.dec_bt, nd, max_pages_per_seq, nt, ms.max_dec_q, num_q_heads, kv, scale,
+                        decode_splits, decode_part_keys, true, opts, ws + ml.dec_rec);
     if (st != PA_OK) return st;
   }
-  if (np > 0 && tp > 0) {
-    st = plan_attention(pp, nb_p, q, q_dtype, out, lse, cu_seqlens_q + nd, seq_lens + nd,
-                        block_tables + (int64_t)nd * max_pages_per_seq, np, max_pages_per_seq, tp, max_seqlen_q,
-                        num_q_heads, kv, scale, sp, 0, false, opts, ws_pre);
+  if (np > 0) {
+    st = plan_attention(pp, nb_p, q, q_dtype, out, lse, r.pre_qs, r.pre_seq_lens, r.pre_bt, np, max_pages_per_seq,
+                        total_q, ms.max_pre_q, num_q_heads, kv, scale, sp, 0, false, opts, ws + ml.pre_rec);
     if (st != PA_OK) return st;
+    pp.q_end = r.pre_qe;
   }
   if (nb_d + nb_p >= (int64_t)1 << 31) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+
+  hipError_t e = pa::launch_route(r, strm);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "route launch failed: %s", hipGetErrorString(e));
   // one grid for the default instantiations at D padded to 256 (with a window
   // or score modifiers the fused kernel spills: the two kernels run instead)
   const bool fused = nb_d > 0 && nb_p > 0 && dpad_of(D) == 256 &&
                      kernel_for(q_dtype, kv->dtype, 256, false) == K_DMA && pp.window_left < 0 &&
                      !pa::has_score_mods(pp);
-  hipError_t e = hipSuccess;
   if (fused) {
     e = pa::launch_attn_mixed(pp, pd, kind_of(q_dtype), kind_of(kv->dtype), 256, (int)nb_p, (int)nb_d, strm);
   } else {  // other shapes: the two pass-1 kernels back to back
@@ -618,17 +716,21 @@ int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const i
     if (e == hipSuccess && nb_d > 0) e = launch_pass1(pd, q_dtype, kv, true, nb_d, strm);
   }
   if (e != hipSuccess) return fail(PA_ERR_HIP, "mixed-step attention launch failed: %s", hipGetErrorString(e));
+  // the chunks' merge runs over every token of the batch (records indexed by
+  // batch token); the small-q rows' tokens get values from records no chunk
+  // wrote and are overwritten by the scatter that follows
   if (nb_p > 0 && sp > 1) {
-    const size_t row = (size_t)num_q_heads * D * elem_size(q_dtype);
-    e = pa::launch_merge(ws_pre + (size_t)decode_tokens * num_q_heads * sp * (D + 2), sp, tp, num_q_heads, D,
-                         (char*)out + (size_t)decode_tokens * row, kind_of(q_dtype),
-                         lse ? lse + (size_t)decode_tokens * num_q_heads : nullptr, false, pp.sinks, strm);
+    e = pa::launch_merge((const float*)(ws + ml.pre_rec), sp, total_q, num_q_heads, D, out, kind_of(q_dtype), lse,
+                         false, pp.sinks, strm);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   if (nb_d > 0) {
-    e = pa::launch_merge(ws_dec, decode_splits, decode_tokens, num_q_heads, D, out, kind_of(q_dtype), lse,
-                         decode_part_keys > 0, pd.sinks, strm);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+    e = pa::launch_merge((const float*)(ws + ml.dec_rec), decode_splits, nt, num_q_heads, D, ws + ml.dec_out,
+                         kind_of(q_dtype), (float*)(ws + ml.dec_lse), decode_part_keys > 0, pd.sinks, strm);
+    if (e == hipSuccess)
+      e = pa::launch_route_scatter(r.dec_tok, nt, ws + ml.dec_out, (const float*)(ws + ml.dec_lse), out, lse,
+                                   r.row_bytes, num_q_heads, strm);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge / scatter launch failed: %s", hipGetErrorString(e));
   }
   return ok();
 }

@@ -131,7 +131,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 256);
 
   const int q0 = p.cu_seqlens_q[seq];
-  const int qlen = p.cu_seqlens_q[seq + 1] - q0;
+  const int qlen = q_end_of(p, seq) - q0;
   const int g = p.group;
   const int nrows = qlen * g;
   const int row0 = qtile * ROWS;

@@ -55,7 +55,7 @@ _I = ctypes.c_int32
 _SZ = ctypes.c_size_t
 
 
-ABI_VERSION = 2  # PA_VERSION of include/pagedattn.h
+ABI_VERSION = 3  # PA_VERSION of include/pagedattn.h
 
 
 def lib():
@@ -75,9 +75,9 @@ def lib():
                                                                               _P, _SZ, _P]
         L.pa_split_kv_decode_noalloc.argtypes = L.pa_paged_prefill.argtypes[:14] + [_I, _I, ctypes.POINTER(AttnOptions),
                                                                                    _P]
-        L.pa_mixed_step.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), ctypes.c_float,
-                                    _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(AttnOptions), _P, _SZ, _P]
-        L.pa_mixed_workspace_bytes.argtypes = [_I] * 6
+        L.pa_mixed_step.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache),
+                                    ctypes.c_float, _I, _I, _I, _I, ctypes.POINTER(AttnOptions), _P, _SZ, _P]
+        L.pa_mixed_workspace_bytes.argtypes = [_P] + [_I] * 8
         L.pa_mixed_workspace_bytes.restype = _SZ
         L.pa_merge_states.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.pa_write_kv.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(KvCache), _P]
@@ -294,18 +294,28 @@ def split_kv_decode_noalloc(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_t
     return (out, lse) if lse is not None else out
 
 
-def mixed_workspace_bytes(total_q, decode_tokens, num_q_heads, head_dim, decode_splits, prefill_splits):
-    return int(lib().pa_mixed_workspace_bytes(total_q, decode_tokens, num_q_heads, head_dim, decode_splits,
-                                              prefill_splits))
+MIXED_DECODE_MAX_Q = 16  # PA_MIXED_DECODE_MAX_Q of include/pagedattn.h
 
 
-def mixed_step(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, num_decode_rows, decode_tokens,
-               max_q_per_row, max_seqlen_q, scale, *, decode_splits=16, decode_part_keys=0, prefill_splits=0,
-               k_scale=1.0, v_scale=1.0, out=None, lse=None, return_lse=False, workspace=None, stream=None,
-               k_head_scales=None, v_head_scales=None, sinks=None, window_left=-1, softcap=0.0, alibi_slopes=None):
-    """pa_mixed_step: sequences [0, num_decode_rows) are small-q rows (their
-    decode_tokens tokens first in q), the rest prefill chunks; one attention
-    launch for both at head dims padded to 256.  Returns out (and lse)."""
+def _host_i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+
+
+def mixed_workspace_bytes(host_q_lens, max_pages_per_seq, num_q_heads, head_dim, q_dtype, decode_max_q,
+                          decode_splits, prefill_splits):
+    ql = _host_i32(host_q_lens)
+    return int(lib().pa_mixed_workspace_bytes(ql.ctypes.data, len(ql), max_pages_per_seq, num_q_heads, head_dim,
+                                              q_dtype, decode_max_q, decode_splits, prefill_splits))
+
+
+def mixed_step(q, k_pages, v_pages, cu_seqlens_q, host_q_lens, seq_lens, block_tables, scale, *, decode_max_q=0,
+               decode_splits=16, decode_part_keys=0, prefill_splits=0, k_scale=1.0, v_scale=1.0, out=None, lse=None,
+               return_lse=False, workspace=None, stream=None, k_head_scales=None, v_head_scales=None, sinks=None,
+               window_left=-1, softcap=0.0, alibi_slopes=None):
+    """pa_mixed_step: a batch in any order (host_q_lens: the rows' query
+    lengths on the host, e.g. a numpy array or list); rows with 1 <= q <=
+    decode_max_q (0: the library's default) take the split-KV decode, the
+    others the prefill.  Returns out (and lse)."""
     total_q, Hq, D = q.shape
     if not q.is_contiguous():
         raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "q must be contiguous")
@@ -314,16 +324,20 @@ def mixed_step(q, k_pages, v_pages, cu_seqlens_q, seq_lens, block_tables, num_de
     if return_lse and lse is None:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
     B = int(seq_lens.numel())
-    ws_bytes = mixed_workspace_bytes(total_q, decode_tokens, Hq, D, decode_splits, prefill_splits)
+    ql = _host_i32(host_q_lens)
+    if len(ql) != B:
+        raise PagedAttentionError(PA_ERR_INVALID_ARGUMENT, "host_q_lens must have one entry per sequence")
+    mp = block_tables.shape[-1]
+    ws_bytes = mixed_workspace_bytes(ql, mp, Hq, D, _dtype(q), decode_max_q, decode_splits, prefill_splits)
     workspace = _workspace(workspace, ws_bytes, q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     opts = _options(Hq, sinks, window_left, softcap, alibi_slopes)
     _check(lib().pa_mixed_step(_ptr(q), _dtype(q), _ptr(out), _ptr(lse), _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
-                               _ptr(_i32(seq_lens, "seq_lens")), _ptr(_i32(block_tables, "block_tables")), B,
-                               block_tables.shape[-1], total_q, Hq, ctypes.byref(kv), float(scale),
-                               int(num_decode_rows), int(decode_tokens), int(max_q_per_row), int(decode_splits),
-                               int(decode_part_keys), int(max_seqlen_q), int(prefill_splits),
-                               opts[0] if opts else None, _ptr(workspace), ws_have, _stream(stream)))
+                               ql.ctypes.data, _ptr(_i32(seq_lens, "seq_lens")),
+                               _ptr(_i32(block_tables, "block_tables")), B, mp, total_q, Hq, ctypes.byref(kv),
+                               float(scale), int(decode_max_q), int(decode_splits), int(decode_part_keys),
+                               int(prefill_splits), opts[0] if opts else None, _ptr(workspace), ws_have,
+                               _stream(stream)))
     return (out, lse) if return_lse or lse is not None else out
 
 

@@ -22,7 +22,7 @@ def test_every_declared_symbol_is_exported():
     assert "pa_paged_prefill" in names and "pa_split_kv_decode" in names and "pa_merge_states" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_version() == 2
+    assert L.pa_version() == 3
 
 
 def test_status_strings():
@@ -244,20 +244,31 @@ def test_mixed_step_arguments_are_checked_before_launch():
     L = ops.lib()
     kv = _fake_kv()
 
-    def mixed(out=0x40000, nd=2, dec_tok=2, max_q=1, sd=8, pk=0, max_sq=8, sp=1, ws=None, wsb=0):
-        return L.pa_mixed_step(0x30000, ops.PA_F16, out, None, 0x50000, 0x60000, 0x70000, 4, 4, 10, 8,
-                               ctypes.byref(kv), 0.1, nd, dec_tok, max_q, sd, pk, max_sq, sp, None, ws, wsb, None)
+    # 4 rows: two small-q rows (1 and 2 tokens), a row without tokens and a chunk of 20
+    ql = np.array([1, 2, 0, 20], dtype=np.int32)
+
+    def mixed(out=0x40000, dmq=0, sd=8, pk=0, sp=1, ws=None, wsb=0, lens=ql, total_q=23):
+        return L.pa_mixed_step(0x30000, ops.PA_F16, out, None, 0x50000, lens.ctypes.data, 0x60000, 0x70000, 4, 4,
+                               total_q, 8, ctypes.byref(kv), 0.1, dmq, sd, pk, sp, None, ws, wsb, None)
     assert mixed(out=None) == ops.PA_ERR_INVALID_ARGUMENT
-    assert mixed(nd=5) == ops.PA_ERR_INVALID_ARGUMENT           # more small-q rows than sequences
-    assert mixed(nd=0, dec_tok=1) == ops.PA_ERR_INVALID_ARGUMENT  # tokens without rows
-    assert mixed(dec_tok=3) == ops.PA_ERR_INVALID_ARGUMENT      # 2 rows of at most 1 token
-    assert mixed(max_q=17) == ops.PA_ERR_UNSUPPORTED
+    assert mixed(dmq=17) == ops.PA_ERR_UNSUPPORTED               # past the decode kernels' 16 tokens
+    assert mixed(dmq=-1) == ops.PA_ERR_UNSUPPORTED
     assert mixed(sd=0) == ops.PA_ERR_INVALID_ARGUMENT
     assert mixed(pk=48) == ops.PA_ERR_INVALID_ARGUMENT
     assert mixed(sp=65) == ops.PA_ERR_INVALID_ARGUMENT
-    assert mixed() == ops.PA_ERR_WORKSPACE                        # records of the small-q rows need room
-    need = ops.mixed_workspace_bytes(10, 2, 8, 64, 8, 1)
-    assert need == 2 * 8 * 8 * 66 * 4                             # unsplit chunks: only the decode records
-    need3 = ops.mixed_workspace_bytes(10, 2, 8, 64, 8, 3)
-    assert need3 == ((10 * 8 * 3 * 66 * 4 + 255) // 256) * 256 + need
+    assert mixed(total_q=24) == ops.PA_ERR_INVALID_ARGUMENT      # host lengths must sum to total_q
+    assert mixed(lens=np.array([1, -2, 0, 20], dtype=np.int32)) == ops.PA_ERR_INVALID_ARGUMENT
+    assert mixed() == ops.PA_ERR_WORKSPACE                        # the route's metadata and records need room
+    # the layout: 2 small-q rows with 3 tokens, 1 chunk; 4 pages per row, 8 heads, D 64, fp16, 8 decode parts
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nd, npre, nt = 2, 1, 3
+    want = (a(4 * (3 * nd + 1 + 4 * npre + nt)) + a(4 * nd * 4) + a(4 * npre * 4) + 2 * a(nt * 8 * 64 * 2)
+            + a(4 * nt * 8) + a(4 * nt * 8 * 8 * 66))
+    need = ops.mixed_workspace_bytes(ql, 4, 8, 64, ops.PA_F16, 0, 8, 1)
+    assert need == want
+    need3 = ops.mixed_workspace_bytes(ql, 4, 8, 64, ops.PA_F16, 0, 8, 3)
+    assert need3 == want + a(4 * 23 * 8 * 3 * 66)
+    # with decode_max_q 1 the row of 2 tokens is a chunk: fewer compact small-q tokens
+    assert ops.mixed_workspace_bytes(ql, 4, 8, 64, ops.PA_F16, 1, 8, 1) < need
     assert mixed(sp=3, ws=0x80000, wsb=need) == ops.PA_ERR_WORKSPACE
+    assert mixed(sp=1, ws=0x80010, wsb=need) == ops.PA_ERR_WORKSPACE  # not 256-byte aligned

@@ -1,7 +1,8 @@
-"""One launch for a mixed step (pa_mixed_step) on the GPU, through the C ABI
-(needs an MI355X): the small-q rows and the chunks of one batch against the
-separate calls on the two sub-batches, bit for bit (the same work items and
-kernel code), and against the fp64 oracle."""
+"""A mixed step (pa_mixed_step) on the GPU, through the C ABI (needs an MI355X):
+a batch in any order, its rows routed by query length on the device (small-q
+rows to the split-KV decode, the others to the prefill), against the separate
+calls on the two sub-batches, bit for bit (the same work items and kernel
+code), and against the fp64 oracle."""
 
 import numpy as np
 import pytest
@@ -14,6 +15,7 @@ from parity_bars import compare, say
 
 pytestmark = pytest.mark.gpu
 
+
 def bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
@@ -25,21 +27,22 @@ def pools64(case):
     return k, v
 
 
-# small-q rows first (q 1 and a verify row of 5, one row with q = 0), then chunks
-# (one with more query tokens than keys, so that its first rows see no key)
-Q_LENS = [1, 5, 0, 150, 40, 300]
-SEQ_LENS = [700, 1300, 64, 900, 30, 2000]
-ND = 3
+# rows in no particular order: chunks, q = 1, an empty row, a verify row of 5,
+# a chunk with more query tokens than keys (its first rows see no key), rows of
+# 16 and 17 tokens on both sides of the default threshold
+Q_LENS = [150, 1, 0, 5, 40, 300, 16, 17]
+SEQ_LENS = [900, 700, 64, 1300, 30, 2000, 500, 1000]
 
 MIXED_CASES = [
-    # (q dtype, KV dtype, D, Hq, Hkv, page, prefill parts, decode parts, part_keys, options)
-    ("f16", "f16", 256, 12, 2, 64, 3, 8, 0, {}),
-    ("bf16", "bf16", 256, 6, 1, 48, 1, 12, 128, {"window_left": 300}),
-    ("f16", "e5m2", 256, 8, 2, 64, 0, 8, 0, {"sinks": True}),
-    ("f16", "e4m3", 256, 8, 2, 816, 2, 16, 0, {"softcap": 3.0, "alibi": True}),
-    ("f16", "f16", 208, 8, 8, 32, 4, 8, 0, {"softcap": 2.0, "window_left": 100, "sinks": True}),
-    ("bf16", "bf16", 128, 8, 2, 32, 3, 8, 0, {}),
-    ("f32", "f32", 64, 4, 1, 16, 2, 4, 0, {"sinks": True}),
+    # (q dtype, KV dtype, D, Hq, Hkv, page, prefill parts, decode parts, part_keys, decode_max_q, options)
+    ("f16", "f16", 256, 12, 2, 64, 3, 8, 0, 0, {}),
+    ("bf16", "bf16", 256, 6, 1, 48, 1, 12, 128, 0, {"window_left": 300}),
+    ("f16", "e5m2", 256, 8, 2, 64, 2, 8, 0, 5, {"sinks": True}),
+    ("bf16", "e4m3", 256, 8, 2, 816, 2, 16, 0, 0, {"softcap": 3.0, "alibi": True}),
+    ("f16", "f16", 208, 8, 8, 32, 4, 8, 0, 0, {"softcap": 2.0, "window_left": 100, "sinks": True}),
+    ("bf16", "bf16", 128, 8, 2, 32, 3, 8, 0, 16, {}),
+    ("f16", "e5m2", 128, 8, 2, 32, 1, 8, 0, 1, {}),
+    ("f32", "f32", 64, 4, 1, 16, 2, 4, 0, 0, {"sinks": True}),
 ]
 
 
@@ -55,34 +58,43 @@ def _options(Hq, opts, seed):
     return host, dev
 
 
-@pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,sp,sd,part_keys,opts", MIXED_CASES)
-def test_mixed_step_equals_separate_calls_and_oracle(qk, kvk, D, Hq, Hkv, P, sp, sd, part_keys, opts):
+def token_index(case, seqs):
+    cu = case.cu_seqlens_q
+    parts = [np.arange(cu[b], cu[b + 1]) for b in seqs]
+    return torch.from_numpy(np.concatenate(parts).astype(np.int64)) if parts else torch.zeros(0, dtype=torch.int64)
+
+
+@pytest.mark.parametrize("qk,kvk,D,Hq,Hkv,P,sp,sd,part_keys,dmq,opts", MIXED_CASES)
+def test_mixed_step_routes_rows_and_equals_separate_calls(qk, kvk, D, Hq, Hkv, P, sp, sd, part_keys, dmq, opts):
     c = gen.make_case(f"mixed_{qk}_{kvk}_D{D}", q_lens=Q_LENS, seq_lens=SEQ_LENS, num_q_heads=Hq,
                       num_kv_heads=Hkv, head_dim=D, page_size=P, q_kind=qk, kv_kind=kvk, seed=3 * D + Hq)
     host, dev = _options(Hq, opts, D + P)
     d = gen.to_device(c)
-    dec_tok = int(c.cu_seqlens_q[ND])
-    max_q = int(max(Q_LENS[:ND]))
-    chunk_max = int(max(Q_LENS[ND:]))
-    say(f"  mixed step {qk}/{kvk} D {D}: prefill parts {sp}, decode parts {sd}, part_keys {part_keys}, {opts}")
-    out, lse = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], ND, dec_tok, max_q, chunk_max,
-                              c.scale, decode_splits=sd, decode_part_keys=part_keys, prefill_splits=sp,
+    thr = dmq or ops.MIXED_DECODE_MAX_Q
+    small = [b for b, q in enumerate(Q_LENS) if 1 <= q <= thr]
+    chunks = [b for b, q in enumerate(Q_LENS) if q > thr]
+    say(f"  mixed step {qk}/{kvk} D {D}: decode_max_q {thr} -> small-q rows {small}, chunks {chunks}; "
+        f"prefill parts {sp}, decode parts {sd}, part_keys {part_keys}, {opts}")
+    out, lse = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], Q_LENS, d["seq_lens"], d["bt"], c.scale,
+                              decode_max_q=dmq, decode_splits=sd, decode_part_keys=part_keys, prefill_splits=sp,
                               k_scale=c.k_scale, v_scale=c.v_scale, return_lse=True, **dev)
     torch.cuda.synchronize()
 
     # the separate calls on the two sub-batches
-    dec, pre = gen.select_seqs(c, range(ND)), gen.select_seqs(c, range(ND, c.num_seqs))
+    dec, pre = gen.select_seqs(c, small), gen.select_seqs(c, chunks)
     dd, dp = gen.to_device(dec), gen.to_device(pre)
-    o_d, l_d = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], max_q, c.scale,
-                                   num_splits=sd, part_keys=part_keys, k_scale=c.k_scale, v_scale=c.v_scale,
-                                   return_lse=True, **dev)
-    o_p, l_p = ops.paged_prefill(dp["q"], dp["k"], dp["v"], dp["cu"], dp["seq_lens"], dp["bt"], chunk_max, c.scale,
-                                 num_kv_splits=sp, k_scale=c.k_scale, v_scale=c.v_scale, return_lse=True, **dev)
+    o_d, l_d = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"],
+                                   max(1, dec.max_seqlen_q), c.scale, num_splits=sd, part_keys=part_keys,
+                                   k_scale=c.k_scale, v_scale=c.v_scale, return_lse=True, **dev)
+    o_p, l_p = ops.paged_prefill(dp["q"], dp["k"], dp["v"], dp["cu"], dp["seq_lens"], dp["bt"], pre.max_seqlen_q,
+                                 c.scale, num_kv_splits=sp, k_scale=c.k_scale, v_scale=c.v_scale, return_lse=True,
+                                 **dev)
     torch.cuda.synchronize()
-    assert torch.equal(bits(out[:dec_tok]), bits(o_d)), "small-q rows differ from pa_split_kv_decode_ex"
-    assert torch.equal(bits(lse[:dec_tok]), bits(l_d))
-    assert torch.equal(bits(out[dec_tok:]), bits(o_p)), "chunks differ from pa_paged_prefill_ex"
-    assert torch.equal(bits(lse[dec_tok:]), bits(l_p))
+    ti_d, ti_p = token_index(c, small).cuda(), token_index(c, chunks).cuda()
+    assert torch.equal(bits(out[ti_d]), bits(o_d)), "small-q rows differ from pa_split_kv_decode_ex"
+    assert torch.equal(bits(lse[ti_d]), bits(l_d))
+    assert torch.equal(bits(out[ti_p]), bits(o_p)), "chunks differ from pa_paged_prefill_ex"
+    assert torch.equal(bits(lse[ti_p]), bits(l_p))
 
     # and the oracle over the whole batch
     k, v = pools64(c)
@@ -94,20 +106,38 @@ def test_mixed_step_equals_separate_calls_and_oracle(qk, kvk, D, Hq, Hkv, P, sp,
 
 
 def test_mixed_step_with_only_one_kind_of_row():
-    """No chunks, or no small-q rows: the call runs the one part there is."""
+    """Only small-q rows, or only chunks: the other class's grid finds no row."""
     c = gen.make_case("mixed_one", q_lens=[1, 4, 200], seq_lens=[500, 900, 1200], num_q_heads=8, num_kv_heads=2,
                       head_dim=256, page_size=64, q_kind="f16", seed=91)
     d = gen.to_device(c)
     full = ops.paged_prefill(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], 200, c.scale)
     dec = gen.select_seqs(c, [0, 1])
     dd = gen.to_device(dec)
-    o1 = ops.mixed_step(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 2, 5, 4, 1, c.scale,
+    o1 = ops.mixed_step(dd["q"], dd["k"], dd["v"], dd["cu"], dec.q_lens, dd["seq_lens"], dd["bt"], c.scale,
                         decode_splits=8)
     o2 = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"], 4, c.scale, num_splits=8)
     pre = gen.select_seqs(c, [2])
     dp = gen.to_device(pre)
-    o3 = ops.mixed_step(dp["q"], dp["k"], dp["v"], dp["cu"], dp["seq_lens"], dp["bt"], 0, 0, 1, 200, c.scale,
+    o3 = ops.mixed_step(dp["q"], dp["k"], dp["v"], dp["cu"], pre.q_lens, dp["seq_lens"], dp["bt"], c.scale,
                         prefill_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(bits(o1), bits(o2))
     assert torch.equal(bits(o3), bits(full[5:]))
+
+
+def test_mixed_step_batch_order_does_not_change_a_row():
+    """The same rows in two orders: every row's output and lse have the same bits."""
+    c = gen.make_case("mixed_order", q_lens=[3, 120, 1, 64, 9], seq_lens=[800, 1500, 77, 64, 2222], num_q_heads=12,
+                      num_kv_heads=2, head_dim=256, page_size=64, q_kind="bf16", seed=17)
+    perm = [3, 1, 4, 0, 2]
+    r = gen.select_seqs(c, perm)
+    outs = []
+    for case in (c, r):
+        d = gen.to_device(case)
+        o, l = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], case.q_lens, d["seq_lens"], d["bt"], case.scale,
+                              decode_splits=8, prefill_splits=2, return_lse=True)
+        torch.cuda.synchronize()
+        outs.append((o, l))
+    (o0, l0), (o1, l1) = outs
+    idx = token_index(c, perm).cuda()
+    assert torch.equal(bits(o0[idx]), bits(o1)) and torch.equal(bits(l0[idx]), bits(l1))

@@ -511,9 +511,11 @@ def test_mixed_step_every_row(kv_kind):
     # the whole step as one pa_mixed_step call (the launch bench.py times as
     # mixed_step_fused): the same bits as the two calls above
     d = gen.to_device(c)
-    say(f"  mixed step in one launch {kv_kind}: verify row (64 parts) + chunk (auto parts)")
-    fo, fl = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], d["seq_lens"], d["bt"], 1, 5, 5, 784, c.scale,
-                            decode_splits=64, prefill_splits=0, k_scale=c.k_scale, v_scale=c.v_scale,
+    sp = ops.auto_splits(chunk.total_q, 1, chunk.max_seqlen_q, chunk.num_q_heads, chunk.num_kv_heads,
+                         chunk.head_dim, ops.PA_F16, ops.PA_FP8_E5M2 if kv_kind == "e5m2" else ops.PA_F16)
+    say(f"  mixed step in one launch {kv_kind}: verify row (64 parts) + chunk ({sp} parts, its automatic count)")
+    fo, fl = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], c.q_lens, d["seq_lens"], d["bt"], c.scale,
+                            decode_splits=64, prefill_splits=sp, k_scale=c.k_scale, v_scale=c.v_scale,
                             return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(bits(fo[:5]), bits(od)) and torch.equal(bits(fl[:5]), bits(ld))
