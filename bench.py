@@ -13,11 +13,14 @@ followed by the split-KV decode of a q=1 row over the same 152,048-token cache
 Prints ONE JSON line.  `value` is the step's algorithmic FLOPs (causal-exact:
 4 * D * Hq per attended pair) divided by the step time; the prefill TFLOPS and
 the decode GB/s are reported beside it, each from HIP events recorded on the
-stream the kernels run on.  `roofline` prices the dominant kernel (the prefill
-attention kernel, timed alone: a split prefill runs as pass 1 and the merge
-with an event between them) against the MFMA fp16 dense peak;
-`decode_roofline` prices the decode call against the HBM peak.  `cpu_baseline` times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+stream the kernels run on.  `roofline` prices the prefill call (its attention
+kernel plus, when the keys are split, the merge of the parts; a split prefill
+runs as pass 1 and the merge with an event between them, so the kernel alone
+is reported beside it) against the MFMA fp16 dense peak; `decode_roofline`
+prices the decode call against the HBM peak.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload on the host cores, and the
+whole oracle on the tiny, decode-batch and varlen workloads on all threads and
+on one.
 """
 
 import argparse
@@ -267,7 +270,63 @@ def cpu_baseline(case, budget_rows, seed=0):
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(toks)} of {Q} query tokens x {case.num_q_heads} heads of the prefill "
                       f"({pairs} attended pairs, {dt:.1f} s, numpy fp64)",
-            "seconds": dt}
+            "seconds": dt, "machine": host_machine(), "other_workloads": oracle_workload_timings()}
+
+
+def host_machine():
+    """The host the oracle ran on: logical CPUs, the CPU model, the CPUs this
+    process may use and the BLAS threads numpy's matmul runs."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "cpu_model": model,
+            "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "blas_threads": max([i.get("num_threads", 1) for i in threadpool_info()] or [1])}
+
+
+def oracle_workload_timings():
+    """The whole oracle on the tiny fp32 case, the 32-row decode batch and the
+    varlen prefill, on all BLAS threads and on one (wall clock of the oracle
+    call alone), each priced in its own unit: attended-pair FLOPs per second
+    for the prefills, K/V bytes per second for the decode batch."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    out = {}
+    for name, make, unit in (("tiny_fp32", gen.tiny_fp32, "flops"),
+                             ("decode_batch_bf16", lambda: gen.decode_batch(kind="bf16"), "bytes"),
+                             ("varlen_bf16", lambda: gen.varlen_prefill(kind="bf16"), "flops")):
+        c = make()
+        kind = c.kv_kind if c.kv_kind in ("e5m2", "e4m3") else "float"
+        k = oracle.dequantize_pool(gen.to_numpy64(c.k_pool, c.kv_kind), kind, c.k_scale)
+        v = oracle.dequantize_pool(gen.to_numpy64(c.v_pool, c.kv_kind), kind, c.v_scale)
+        q = gen.to_numpy64(c.q)
+
+        def once():
+            t0 = time.perf_counter()
+            oracle.paged_attention(q, k, v, c.cu_seqlens_q, c.seq_lens, c.block_tables, c.scale)
+            return time.perf_counter() - t0
+        t_all = once()
+        with threadpool_limits(1):
+            t_one = once()
+        if unit == "flops":
+            work = workload.prefill_flops(c.cu_seqlens_q, c.seq_lens, c.num_q_heads, c.head_dim)
+            rate = lambda t: work / t / 1e12  # noqa: E731
+            runit = "TFLOPS"
+        else:
+            work = workload.decode_bytes(c.cu_seqlens_q, c.seq_lens, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                         c.page_size, c.q_kind, c.kv_kind, c.num_splits)
+            rate = lambda t: work / t / 1e9  # noqa: E731
+            runit = "GB/s"
+        out[name] = {"all_threads_s": t_all, "one_thread_s": t_one, unit: work, "unit": runit,
+                     "all_threads": rate(t_all), "one_thread": rate(t_one)}
+        log(f"  oracle {name}: {t_all:.2f} s on all threads, {t_one:.2f} s on one")
+    return out
 
 
 def kv_write_timing(case, d, reps):
@@ -602,12 +661,17 @@ def main():
            "dtype": specs[0][1].q_kind, "data": "synthetic", "config": desc}
     res.update(parts)
     if "prefill" in parts:
+        # the prefill call: its attention kernel and, when the keys are split,
+        # the merge of the parts (both timed; the kernel alone beside them)
         pf = parts["prefill"]
-        res["roofline"] = {"bound": "mfma", "achieved": pf["kernel_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": pf["kernel_tflops"] / MFMA_F16_PEAK_TFLOPS,
-                           "traffic": measured_traffic(a.workload, "prefill", "hbm_bytes_kernel"),
-                           "kernel": prefill_kernel_name(desc),
-                           "kernel_ms": pf["kernel_ms"]}
+        split = pf["splits"] > 1
+        res["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": pf["tflops"] / MFMA_F16_PEAK_TFLOPS,
+                           "traffic": measured_traffic(a.workload, "prefill"),
+                           "kernel": prefill_kernel_name(desc) + (" + merge_rows_kernel" if split else ""),
+                           "call_ms": pf["ms"], "kernel_ms": pf["kernel_ms"],
+                           "merge_ms": pf["ms"] - pf["kernel_ms"] if split else 0.0,
+                           "kernel_alone_tflops": pf["kernel_tflops"]}
     if "decode" in parts:
         dc = parts["decode"]
         res["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
