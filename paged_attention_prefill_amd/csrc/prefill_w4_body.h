@@ -126,7 +126,14 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   WorkItem wi;
   if (!work_of_block(p, bid, true, wi)) return;
   // a sequence's last query tiles see the most keys: they are handed out first
-  const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  // Uniform, and held in scalar registers (OPQ) so that nothing derived from
+  // them takes a vector register across the tile loop.  Register allocation
+  // is tight in every instantiation: this keeps the default and window ones
+  // free of scratch, the modifier one is free of it without.
+  constexpr bool OPQ = !MOD;
+  const int qtile = OPQ ? __builtin_amdgcn_readfirstlane(wi.qtile) : wi.qtile;
+  const int split = OPQ ? __builtin_amdgcn_readfirstlane(wi.split) : wi.split;
+  const int kvh = OPQ ? __builtin_amdgcn_readfirstlane(wi.kvh) : wi.kvh;
   const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = seq_by_rank(p, wi.seqpos, (int*)smem, tid, 256);
 
@@ -185,26 +192,35 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     // (in scratch memory) across the tile loop
     int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(lane_e));
+    // (OPQ: the same for the scalars the row arithmetic starts from, opaque
+    // copies, so that the division by g and the row offsets are not shared
+    // with, and kept alive from, the same arithmetic before the loop)
+    int g_e = g, kvh_e = kvh, q0_e = q0, wrow0_e = wrow0, nrows_e = nrows, split_e = split;
+    if constexpr (OPQ) {
+      g_e = __builtin_amdgcn_readfirstlane(g_e), q0_e = __builtin_amdgcn_readfirstlane(q0_e);
+      wrow0_e = __builtin_amdgcn_readfirstlane(wrow0_e), nrows_e = __builtin_amdgcn_readfirstlane(nrows_e);
+      asm volatile("" : "+s"(g_e), "+s"(kvh_e), "+s"(q0_e), "+s"(wrow0_e), "+s"(nrows_e), "+s"(split_e));
+    }
     const int hi = lane_e >> 5, r32 = lane_e & 31;
-    const float out_scale = head_v_scale(p, kvh);
+    const float out_scale = head_v_scale(p, kvh_e);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float ltot = 0.0f, mrow = kNegInf;
       if constexpr (!ZERO) ltot = lsum[rb] + __shfl_xor(lsum[rb], 32), mrow = m[rb];
-      const int prow = wrow0 + rb * 32 + r32;
-      if (prow >= nrows) continue;
-      const int tok = prow / g;
-      const int hq = kvh * g + (prow - tok * g);
+      const int prow = wrow0_e + rb * 32 + r32;
+      if (prow >= nrows_e) continue;
+      const int tok = prow / g_e;
+      const int hq = kvh_e * g_e + (prow - tok * g_e);
       float inv, lse_nat;
       final_row(p.write_partial ? nullptr : p.sinks, hq, mrow, ltot, out_scale, inv, lse_nat);
-      const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
+      const int64_t rowidx = (int64_t)(q0_e + tok) * p.num_q_heads + hq;
       // element i of accumulator block db, normalised
       auto o = [&](int db, int i) {
         if constexpr (ZERO) return 0.0f;
         else return oacc[rb][db][i] * inv;
       };
       if (p.write_partial) {
-        float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
+        float* rec = p.partial + (rowidx * p.num_splits + split_e) * (int64_t)(p.head_dim + 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
