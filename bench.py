@@ -553,6 +553,34 @@ def crossover(reps=20):
     return 0
 
 
+def sequences(reps=20):
+    """The varlen prefill and subsets of its sequences, each launched alone
+    (one key part; the longest sequence also with 2): how much of the batch's
+    time its longest sequence takes by itself, i.e. whether the batch is bound
+    by the kernel's rate per compute unit or by the groups left over at the
+    end.  One JSON line per launch, kernel time from HIP events."""
+    stream = torch.cuda.current_stream()
+    v = gen.varlen_prefill(kind="bf16")
+    runs = [("all four", list(range(v.num_seqs)), 1), ("2048 after 8192", [3], 1), ("1024 after 4096", [2], 1),
+            ("the three shorter", [0, 1, 2], 1), ("the two longest", [2, 3], 1), ("2048 after 8192", [3], 2)]
+    for name, idx, splits in runs:
+        case = v if len(idx) == v.num_seqs else gen.select_seqs(v, idx)
+        c = Call("prefill", case, gen.to_device(case), splits)
+        for _ in range(5):
+            c(stream)
+        torch.cuda.synchronize()
+        c.times, c.pass1 = [], []
+        for _ in range(reps):
+            c(stream, record=True)
+        torch.cuda.synchronize()
+        f = call_flops("prefill", case)
+        print(json.dumps({"mode": "sequences", "launch": name, "seqs": idx, "splits": splits, "gflop": f / 1e9,
+                          "call_us": c.ms_median() * 1e3, "kernel_us": c.kernel_ms() * 1e3,
+                          "kernel_tflops": f / (c.kernel_ms() * 1e-3) / 1e12}), flush=True)
+        del c
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -563,11 +591,12 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover", "sequences"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
                          "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU); "
                          "ceilings: a pure MFMA loop and a streaming read, measured; "
-                         "crossover: one small-q row through the decode and the prefill calls, q = 1..16")
+                         "crossover: one small-q row through the decode and the prefill calls, q = 1..16; "
+                         "sequences: the varlen prefill and its sequences launched alone")
     ap.add_argument("--pmc-dir", default="gpurun_out",
                     help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
@@ -585,6 +614,8 @@ def main():
         return ceilings()
     if a.mode == "crossover":
         return crossover()
+    if a.mode == "sequences":
+        return sequences()
     ops.lib()
 
     log(f"building workload {a.workload} ...")
