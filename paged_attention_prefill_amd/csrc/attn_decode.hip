@@ -5,9 +5,10 @@
 
 namespace pa {
 
-// Head dims up to 128 are held to 256 registers so that two groups share a CU.
+// Head dims up to 128, and fp8 KV at 256 (query fragments in LDS, one ring
+// stage per wave: 80 KB), are held to 256 registers so that two groups share a CU.
 template <typename QT, int F8, int DPAD, int NSW, bool MOD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DPAD <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DPAD <= 128 || F8 != 0 ? 2 : 1)))
 void attn_decode_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[decode_lds_bytes<F8, DPAD, NSW>()];
   decode_body<QT, F8, DPAD, NSW, MOD>(p, blockIdx.x, smem);
@@ -43,11 +44,11 @@ hipError_t launch_attn_decode(const AttnParams& p, int q_kind, int kv_kind, int 
   if (kv_kind == KV_E5M2 || kv_kind == KV_E4M3) {
     if (dpad != 256) return hipErrorInvalidValue;
     if (q_kind == KV_F16)
-      return kv_kind == KV_E5M2 ? launch_dec<_Float16, KV_E5M2, 256, 2>(p, nblocks, stream)
-                                : launch_dec<_Float16, KV_E4M3, 256, 2>(p, nblocks, stream);
+      return kv_kind == KV_E5M2 ? launch_dec<_Float16, KV_E5M2, 256, 1>(p, nblocks, stream)
+                                : launch_dec<_Float16, KV_E4M3, 256, 1>(p, nblocks, stream);
     if (q_kind == KV_BF16)
-      return kv_kind == KV_E5M2 ? launch_dec<__bf16, KV_E5M2, 256, 2>(p, nblocks, stream)
-                                : launch_dec<__bf16, KV_E4M3, 256, 2>(p, nblocks, stream);
+      return kv_kind == KV_E5M2 ? launch_dec<__bf16, KV_E5M2, 256, 1>(p, nblocks, stream)
+                                : launch_dec<__bf16, KV_E4M3, 256, 1>(p, nblocks, stream);
     return hipErrorInvalidValue;
   }
   if (q_kind != kv_kind) return hipErrorInvalidValue;

@@ -31,7 +31,10 @@ using namespace mf;
 // Head dims up to 128 are held to 256 registers so that two groups share a CU
 // (with one ring stage per wave at D 128: 64 KB of LDS per group): a decode
 // batch has many short parts, and a second resident group hides each part's
-// first-tile latency.
+// first-tile latency.  fp8 KV at D 256 (QLDS) does the same with one stage per
+// wave: its query fragments stay in LDS (16 KB after the ring, written once by
+// wave 0, read at every k-step) instead of 64 registers per lane, which brings
+// a wave to 256 registers and a group to 80 KB of LDS.
 // MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
 template <typename QT, int F8, int DPAD, int NSW, bool MOD>
 __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* smem) {
@@ -44,7 +47,8 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
   constexpr int HALF = TL::HALF;  // DMA instructions of one K (or V) tile
   constexpr int NKK = DPAD / 16, NDB = DPAD / 32;
   constexpr int RING = WAVES * NSW * STAGE_BYTES;
-  static_assert(WAVES * NDB * 4 * 1024 <= RING, "the O exchange reuses the ring");
+  constexpr bool QLDS = KV8 && DPAD == 256;
+  constexpr int QOFF = RING;  // query fragments (QLDS): k-step kk at QOFF + 1 KB kk, 16 bytes per lane
   static_assert(NSW == 1 || NSW == 2, "ring depth");
 
   float2 (*mlx)[32] = (float2 (*)[32])(smem + RING);  // per wave and row: (m, l)
@@ -56,7 +60,11 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
 
   WorkItem wi;
   if (!work_of_block(p, bid, false, wi)) return;
-  const int qtile = wi.qtile, split = wi.split, kvh = wi.kvh;
+  // (QLDS: held in scalar registers, so that none takes a vector register
+  // across the tile loop; the others are free of scratch without that)
+  const int qtile = QLDS ? __builtin_amdgcn_readfirstlane(wi.qtile) : wi.qtile;
+  const int split = QLDS ? __builtin_amdgcn_readfirstlane(wi.split) : wi.split;
+  const int kvh = QLDS ? __builtin_amdgcn_readfirstlane(wi.kvh) : wi.kvh;
   const float score_scale = head_score_scale(p, kvh), out_scale = head_v_scale(p, kvh);
   const int seq = wi.seqpos;
 
@@ -81,16 +89,29 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
   const float slope = MOD ? alibi_slope_l2(p, hq) : 0.0f;
 
   // Q^T (B operand) over the whole head dimension: k-step kk holds d = 16 kk + 8 hi .. +7
-  // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half)
-  uint4 qf[NKK];
-  {
+  // (fp8 K: the pair of k-steps 2j, 2j+1 covers chunk 2j + hi, low then high half).
+  // QLDS: the four waves hold the same rows, so wave 0 alone loads them and
+  // stores them to LDS; the barrier before the tile loop publishes them.
+  uint4 qf[QLDS ? 1 : NKK];
+  if (!QLDS || wave == 0) {
+    uint4 qv[NKK];
     const QT* qrow = (const QT*)p.q + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * p.head_dim;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int d = KV8 ? 32 * (kk >> 1) + 16 * hi + 8 * (kk & 1) : kk * 16 + hi * 8;
-      qf[kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
+      qv[kk] = (valid && d < p.head_dim) ? *(const uint4*)(qrow + d) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if constexpr (QLDS) *(uint4*)(smem + QOFF + kk * 1024 + lane * 16) = qv[kk];
+      else qf[kk] = qv[kk];
     }
   }
+  // B operand of k-step kk
+  auto qfrag = [&](int kk) {
+    if constexpr (QLDS) return *(const uint4*)(smem + QOFF + kk * 1024 + lane * 16);
+    else return qf[kk];
+  };
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -193,6 +214,7 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
   // page ids are read one tile ahead of their use, so that the scalar loads
   // are never waited for on the way to a refill
   if (NSW < nt_w) tl.fetch(NSW);
+  if constexpr (QLDS) lds_barrier();  // wave 0's query fragments are in LDS
 
   for (int i = 0; i < nt_w; ++i) {
     const int st = NSW == 1 ? 0 : (i & 1);
@@ -206,14 +228,14 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
 #pragma unroll
       for (int kp = 0; kp < NKK / 2; ++kp) {
         const uint4 kw = *(const uint4*)(smem + sb + k_frag(klane, kp));
-        s0 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.x, kw.y), qf[2 * kp], s0);
-        s1 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.z, kw.w), qf[2 * kp + 1], s1);
+        s0 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.x, kw.y), qfrag(2 * kp), s0);
+        s1 = Mf<QT>::run(fp8x8_to<QT, F8>(kw.z, kw.w), qfrag(2 * kp + 1), s1);
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < NKK; kk += 2) {
-        s0 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk)), qf[kk], s0);
-        s1 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk + 1)), qf[kk + 1], s1);
+        s0 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk)), qfrag(kk), s0);
+        s1 = Mf<QT>::run(*(const uint4*)(smem + sb + k_frag(klane, kk + 1)), qfrag(kk + 1), s1);
       }
     }
     f32x16_t s = s0 + s1;
@@ -283,63 +305,144 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
     }
   }
 
-  // ---- combine the four waves' states, then the FP32 record of this part
+  // ---- combine the four waves' states, then the FP32 record of this part.
+  // The waves' O go through the ring's LDS, in one round when the ring holds
+  // all of them, else in ROUNDS rounds of DBR d blocks (wave w combining d
+  // blocks w, w + 4, ... of a round, in the order of the waves either way).
+  constexpr int ROUNDS = (WAVES * NDB * 4 * 1024 + RING - 1) / RING;
+  constexpr int DBR = NDB / ROUNDS;
+  static_assert(NDB % ROUNDS == 0 && WAVES * DBR * 4 * 1024 <= RING, "the O exchange reuses the ring");
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  lds_barrier();  // every wave is done with its ring (all of its loads were waited for)
-  if (hi == 0) mlx[wave][r32] = make_float2(m, ltot);
+  lds_barrier();  // every wave is done with its ring (all of its loads were waited for) and the query fragments
   f32x4_t* ox = (f32x4_t*)smem;
+  if constexpr (ROUNDS == 1) {
+    if (hi == 0) mlx[wave][r32] = make_float2(m, ltot);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      ox[((wave * NDB + db) * 4 + rr) * 64 + lane] =
-          (f32x4_t){oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
-  lds_barrier();
-  float mv[WAVES], lv[WAVES];
+      for (int rr = 0; rr < 4; ++rr)
+        ox[((wave * NDB + db) * 4 + rr) * 64 + lane] =
+            (f32x4_t){oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
+    lds_barrier();
+    float mv[WAVES], lv[WAVES];
 #pragma unroll
-  for (int v = 0; v < WAVES; ++v) {
-    const float2 t = mlx[v][r32];
-    mv[v] = t.x;
-    lv[v] = t.y;
-  }
-  float mall = mv[0];
+    for (int v = 0; v < WAVES; ++v) {
+      const float2 t = mlx[v][r32];
+      mv[v] = t.x;
+      lv[v] = t.y;
+    }
+    float mall = mv[0];
 #pragma unroll
-  for (int v = 1; v < WAVES; ++v) mall = fmaxf(mall, mv[v]);
-  float av[WAVES];
-  float lall = 0.0f;
+    for (int v = 1; v < WAVES; ++v) mall = fmaxf(mall, mv[v]);
+    float av[WAVES];
+    float lall = 0.0f;
 #pragma unroll
-  for (int v = 0; v < WAVES; ++v) {
-    av[v] = (mv[v] == kNegInf) ? 0.0f : fast_exp2(mv[v] - mall);
-    lall += av[v] * lv[v];
-  }
-  if (!valid) return;
-  const bool empty = (mall == kNegInf) || !(lall > 0.0f);
-  const float inv = empty ? 0.0f : out_scale / lall;
-  const float lse_nat = empty ? kNegInf : (mall + __log2f(lall)) * 0.69314718055994530942f;
-  const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
-  float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
+    for (int v = 0; v < WAVES; ++v) {
+      av[v] = (mv[v] == kNegInf) ? 0.0f : fast_exp2(mv[v] - mall);
+      lall += av[v] * lv[v];
+    }
+    if (!valid) return;
+    const bool empty = (mall == kNegInf) || !(lall > 0.0f);
+    const float inv = empty ? 0.0f : out_scale / lall;
+    const float lse_nat = empty ? kNegInf : (mall + __log2f(lall)) * 0.69314718055994530942f;
+    const int64_t rowidx = (int64_t)(q0 + tok) * p.num_q_heads + hq;
+    float* rec = p.partial + (rowidx * p.num_splits + split) * (int64_t)(p.head_dim + 2);
 #pragma unroll
-  for (int j = 0; j < (NDB + WAVES - 1) / WAVES; ++j) {
-    const int db = wave + WAVES * j;
+    for (int j = 0; j < (NDB + WAVES - 1) / WAVES; ++j) {
+      const int db = wave + WAVES * j;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d = db * 32 + 8 * rr + 4 * hi;
-      if (db < NDB && d < p.head_dim) {
-        f32x4_t o = (f32x4_t)(0.0f);
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = db * 32 + 8 * rr + 4 * hi;
+        if (db < NDB && d < p.head_dim) {
+          f32x4_t o = (f32x4_t)(0.0f);
 #pragma unroll
-        for (int v = 0; v < WAVES; ++v) o += av[v] * ox[((v * NDB + db) * 4 + rr) * 64 + lane];
-        *(float2*)(rec + d) = make_float2(o[0] * inv, o[1] * inv);
-        *(float2*)(rec + d + 2) = make_float2(o[2] * inv, o[3] * inv);
+          for (int v = 0; v < WAVES; ++v) o += av[v] * ox[((v * NDB + db) * 4 + rr) * 64 + lane];
+          *(float2*)(rec + d) = make_float2(o[0] * inv, o[1] * inv);
+          *(float2*)(rec + d + 2) = make_float2(o[2] * inv, o[3] * inv);
+        }
       }
     }
+    if (wave == 0 && hi == 0) *(float2*)(rec + p.head_dim) = make_float2(lse_nat, 0.0f);
+  } else {
+    // every wave reaches every barrier of the rounds: the rows past the
+    // group's last one skip only their stores.  The row's indices are formed
+    // again here from the lane index and opaque copies of the group's scalars,
+    // so that none of them is kept alive across the tile loop.
+    int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane_e));
+    int g_e = __builtin_amdgcn_readfirstlane(g), kvh_e = kvh, q0_e = __builtin_amdgcn_readfirstlane(q0),
+        row0_e = __builtin_amdgcn_readfirstlane(row0), nrows_e = __builtin_amdgcn_readfirstlane(nrows),
+        split_e = split;
+    asm volatile("" : "+s"(g_e), "+s"(kvh_e), "+s"(q0_e), "+s"(row0_e), "+s"(nrows_e), "+s"(split_e));
+    const int prow_e = row0_e + (lane_e & 31);
+    const int hi_e = lane_e >> 5, r32_e = lane_e & 31;
+    if (hi_e == 0) mlx[wave][r32_e] = make_float2(m, ltot);
+    const bool valid_e = prow_e < nrows_e;
+    const int tok_e = valid_e ? prow_e / g_e : 0;
+    const int hq_e = kvh_e * g_e + (valid_e ? prow_e - tok_e * g_e : 0);
+    float av[WAVES], inv = 0.0f, lse_nat = kNegInf;
+    const int64_t rowidx = (int64_t)(q0_e + tok_e) * p.num_q_heads + hq_e;
+    float* rec = p.partial + (rowidx * p.num_splits + split_e) * (int64_t)(p.head_dim + 2);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (r > 0) lds_barrier();  // the previous round's reads are done
+#pragma unroll
+      for (int b = 0; b < DBR; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int db = r * DBR + b;
+          ox[((wave * DBR + b) * 4 + rr) * 64 + lane_e] =
+              (f32x4_t){oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
+        }
+      lds_barrier();
+      if (r == 0) {
+        float mv[WAVES], lv[WAVES];
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) {
+          const float2 t = mlx[v][r32_e];
+          mv[v] = t.x;
+          lv[v] = t.y;
+        }
+        float mall = mv[0];
+#pragma unroll
+        for (int v = 1; v < WAVES; ++v) mall = fmaxf(mall, mv[v]);
+        float lall = 0.0f;
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) {
+          av[v] = (mv[v] == kNegInf) ? 0.0f : fast_exp2(mv[v] - mall);
+          lall += av[v] * lv[v];
+        }
+        const bool empty = (mall == kNegInf) || !(lall > 0.0f);
+        inv = empty ? 0.0f : out_scale / lall;
+        lse_nat = empty ? kNegInf : (mall + __log2f(lall)) * 0.69314718055994530942f;
+      }
+#pragma unroll
+      for (int j = 0; j < (DBR + WAVES - 1) / WAVES; ++j) {
+        const int b = wave + WAVES * j, db = r * DBR + b;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = db * 32 + 8 * rr + 4 * hi_e;
+          if (valid_e && b < DBR && d < p.head_dim) {
+            f32x4_t o = (f32x4_t)(0.0f);
+#pragma unroll
+            for (int v = 0; v < WAVES; ++v) o += av[v] * ox[((v * DBR + b) * 4 + rr) * 64 + lane_e];
+            *(float2*)(rec + d) = make_float2(o[0] * inv, o[1] * inv);
+            *(float2*)(rec + d + 2) = make_float2(o[2] * inv, o[3] * inv);
+          }
+        }
+      }
+    }
+    if (valid_e && wave == 0 && hi_e == 0) *(float2*)(rec + p.head_dim) = make_float2(lse_nat, 0.0f);
   }
-  if (wave == 0 && hi == 0) *(float2*)(rec + p.head_dim) = make_float2(lse_nat, 0.0f);
 }
 
-// LDS of the body: the ring of NSW stages per wave, then the (m, l) exchange.
+// LDS of the body: the ring of NSW stages per wave, then the (m, l) exchange,
+// which QLDS places over the query fragments (free once the tile loop is done).
 template <int F8, int DPAD, int NSW>
 constexpr int decode_lds_bytes() {
-  return 4 * NSW * TileLoader<DPAD, 1, F8 != 0 ? 1 : 2>::STAGE_BYTES + 4 * 32 * (int)sizeof(float2);
+  constexpr int qbytes = (F8 != 0 && DPAD == 256) ? (DPAD / 16) * 1024 : 0;
+  constexpr int mlx = 4 * 32 * (int)sizeof(float2);
+  return 4 * NSW * TileLoader<DPAD, 1, F8 != 0 ? 1 : 2>::STAGE_BYTES + (qbytes > mlx ? qbytes : mlx);
 }
 
 }  // namespace pa

@@ -128,9 +128,10 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // a sequence's last query tiles see the most keys: they are handed out first
   // Uniform, and held in scalar registers (OPQ) so that nothing derived from
   // them takes a vector register across the tile loop.  Register allocation
-  // is tight in every instantiation: this keeps the default and window ones
-  // free of scratch, the modifier one is free of it without.
-  constexpr bool OPQ = !MOD;
+  // is tight in every instantiation: this keeps the 16-bit default and window
+  // ones free of scratch; the modifier and fp8 ones are free of it without
+  // (and the fp8 ones ran 3 % slower with it).
+  constexpr bool OPQ = !MOD && !KV8;
   const int qtile = OPQ ? __builtin_amdgcn_readfirstlane(wi.qtile) : wi.qtile;
   const int split = OPQ ? __builtin_amdgcn_readfirstlane(wi.split) : wi.split;
   const int kvh = OPQ ? __builtin_amdgcn_readfirstlane(wi.kvh) : wi.kvh;
