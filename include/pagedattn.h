@@ -302,8 +302,8 @@ int pa_split_kv_decode_noalloc(const void *q, int32_t q_dtype, void *out, float 
  *   workspace, the attention runs (head dims padded to 256 with fp16 / bf16 /
  *   fp8 KV and no window or score modifier: one grid, chunk groups first, the
  *   decode groups filling the compute units the chunks' last wave leaves
- *   idle; otherwise the two pass-1 kernels back to back), the merges follow,
- *   and the small-q rows' outputs are scattered back to their tokens.  out
+ *   idle; otherwise the two pass-1 kernels back to back), and the merges
+ *   follow, the small-q rows' merge writing each row to its batch tokens.  out
  *   must not be NULL; lse nullable; opts as for the _ex calls (both classes).
  *   Workspace: pa_mixed_workspace_bytes(host_q_lens, ...) bytes, 256-byte
  *   aligned (prefill_splits 0 sizes it for every automatic count).

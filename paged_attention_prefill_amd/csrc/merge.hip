@@ -28,6 +28,15 @@ namespace {
 constexpr float kNegInfM = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Output row of record row `row` (token row / H, head row % H): the same row,
+// or, with a token map (a routed call's compact tokens -> batch tokens), the
+// mapped token's; -1 for a compact token the map leaves out.
+__device__ __forceinline__ int64_t out_row(const int* tok_map, int64_t row, int H) {
+  if (tok_map == nullptr) return row;
+  const int g = tok_map[row / H];
+  return g < 0 ? -1 : (int64_t)g * H + row % H;
+}
+
 template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, float b) {
   p[0] = (OT)a;
   p[1] = (OT)b;
@@ -41,13 +50,16 @@ template <typename OT> __device__ __forceinline__ void put2(OT* p, float a, floa
 template <typename OT, int kMT, bool STRIDED>
 __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ partials, int S, int D,
                                                     OT* __restrict__ out, float* __restrict__ out_lse,
-                                                    const float* __restrict__ sinks, int H) {
+                                                    const float* __restrict__ sinks, int H,
+                                                    const int* __restrict__ tok_map) {
   constexpr int NW = kMT / 64;
   __shared__ float red[NW];
   __shared__ float2 part[kMT];
   __shared__ float dpart[kMT];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t row = blockIdx.x;
+  const int64_t orow = out_row(tok_map, row, H);
+  if (orow < 0) return;  // (uniform: one row per work group)
   const int R = D + 2;
   const float* rec = partials + row * (int64_t)S * R;
 
@@ -98,8 +110,8 @@ __global__ __launch_bounds__(kMT) void merge_kernel(const float* __restrict__ pa
     if (sk != kNegInfM) sd += exp2f((sk - M) * kLog2e);
     const bool empty = M == kNegInfM || !(sd > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / sd;
-    put2<OT>(out + row * D + 2 * t, sx * inv, sy * inv);
-    if (out_lse != nullptr && t == 0) out_lse[row] = empty ? kNegInfM : M + logf(sd);
+    put2<OT>(out + orow * D + 2 * t, sx * inv, sy * inv);
+    if (out_lse != nullptr && t == 0) out_lse[orow] = empty ? kNegInfM : M + logf(sd);
   }
 }
 
@@ -112,10 +124,13 @@ template <typename OT>
 __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict__ partials, int S, int D,
                                                          int64_t rows, OT* __restrict__ out,
                                                          float* __restrict__ out_lse,
-                                                         const float* __restrict__ sinks, int H) {
+                                                         const float* __restrict__ sinks, int H,
+                                                         const int* __restrict__ tok_map) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  const int64_t orow = out_row(tok_map, row, H);
+  if (orow < 0) return;
   const int R = D + 2;
   const float* rec = partials + row * (int64_t)S * R;
   float M = kNegInfM;
@@ -142,34 +157,34 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
     }
     const bool empty = M == kNegInfM || !(den > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / den;
-    put2<OT>(out + row * D + 2 * dc, ax * inv, ay * inv);
-    if (out_lse != nullptr && dc == 0) out_lse[row] = empty ? kNegInfM : M + logf(den);
+    put2<OT>(out + orow * D + 2 * dc, ax * inv, ay * inv);
+    if (out_lse != nullptr && dc == 0) out_lse[orow] = empty ? kNegInfM : M + logf(den);
   }
 }
 
 template <typename OT>
 static hipError_t launch_m(const float* partials, int S, int ntok, int H, int D, void* out, float* out_lse,
-                           bool strided, const float* sinks, hipStream_t stream) {
+                           bool strided, const float* sinks, const int* tok_map, hipStream_t stream) {
   const int64_t rows = (int64_t)ntok * H;
   if (rows == 0) return hipSuccess;
   if (strided)
     hipLaunchKernelGGL((merge_kernel<OT, 1024, true>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
-                       (OT*)out, out_lse, sinks, H);
+                       (OT*)out, out_lse, sinks, H, tok_map);
   else if (S >= 16)
     hipLaunchKernelGGL((merge_kernel<OT, 1024, false>), dim3((unsigned)rows), dim3(1024), 0, stream, partials, S, D,
-                       (OT*)out, out_lse, sinks, H);
+                       (OT*)out, out_lse, sinks, H, tok_map);
   else
     hipLaunchKernelGGL((merge_rows_kernel<OT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, partials, S,
-                       D, rows, (OT*)out, out_lse, sinks, H);
+                       D, rows, (OT*)out, out_lse, sinks, H, tok_map);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, bool strided, const float* sinks, hipStream_t stream) {
+                        float* out_lse, bool strided, const float* sinks, const int* tok_map, hipStream_t stream) {
   switch (out_kind) {
-    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
-    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
-    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, stream);
+    case KV_F32: return launch_m<float>(partials, S, ntok, H, D, out, out_lse, strided, sinks, tok_map, stream);
+    case KV_F16: return launch_m<_Float16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, tok_map, stream);
+    case KV_BF16: return launch_m<__bf16>(partials, S, ntok, H, D, out, out_lse, strided, sinks, tok_map, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -13,7 +13,8 @@
 //   * small-q rows (1 <= q <= decode_max_q): compact metadata (cu_seqlens_q
 //     from 0, seq_lens, block-table rows) and their query rows gathered into a
 //     compact q, so that their FP32 records are indexed by a compact token
-//     number; after the merge the compact outputs are scattered back;
+//     number; the decode merge writes each compact token's rows to its batch
+//     token;
 //   * chunks (q > decode_max_q): addressed in place ([start, end) token
 //     ranges, AttnParams::q_end), with their seq_lens and block-table rows.
 //
@@ -28,28 +29,34 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
-// Inclusive scan over the block of x (every thread passes one value); returns
-// the inclusive prefix and leaves the block's total in *total.
-__device__ __forceinline__ int block_scan(int x, int* lds, int* total) {
-  const int t = threadIdx.x;
-  lds[t] = x;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int y = t >= off ? lds[t - off] : 0;
-    __syncthreads();
-    lds[t] += y;
-    __syncthreads();
+// Inclusive scans over the work group of three values per thread (a scan
+// within each wave by lane shuffles, then one over the 16 wave totals):
+// returns the inclusive prefixes and leaves the group's totals in tot.
+__device__ __forceinline__ int3 block_scan3(int3 x, int3* lds, int3* tot) {
+  constexpr int NW = kPlanThreads / 64;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(x.x, off), b = __shfl_up(x.y, off), c = __shfl_up(x.z, off);
+    if (lane >= off) x.x += a, x.y += b, x.z += c;
   }
-  const int incl = lds[t];
-  *total = lds[kPlanThreads - 1];
+  if (lane == 63) lds[w] = x;
   __syncthreads();
-  return incl;
+  if (t == 0) {
+    for (int i = 1; i < NW; ++i) lds[i] = make_int3(lds[i].x + lds[i - 1].x, lds[i].y + lds[i - 1].y,
+                                                     lds[i].z + lds[i - 1].z);
+  }
+  __syncthreads();
+  if (w > 0) x = make_int3(x.x + lds[w - 1].x, x.y + lds[w - 1].y, x.z + lds[w - 1].z);
+  *tot = lds[NW - 1];
+  __syncthreads();  // lds is free for the next call
+  return x;
 }
 
 // One work group: classifies the rows in batch order and writes both classes'
 // metadata (everything except the block-table rows and the gathered q).
 __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(RouteParams r) {
-  __shared__ int lds[kPlanThreads];
+  __shared__ int3 lds[kPlanThreads / 64];
   int n_dec = 0, n_pre = 0, n_tok = 0;  // running totals (uniform)
   for (int c0 = 0; c0 < r.B; c0 += kPlanThreads) {
     const int b = c0 + (int)threadIdx.x;
@@ -61,10 +68,11 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(RouteParams r)
     }
     const bool is_dec = b < r.B && q >= 1 && q <= r.decode_max_q;
     const bool is_pre = b < r.B && q > r.decode_max_q;
-    int td, tp, tt;
-    const int id = block_scan(is_dec ? 1 : 0, lds, &td) - (is_dec ? 1 : 0);
-    const int ip = block_scan(is_pre ? 1 : 0, lds, &tp) - (is_pre ? 1 : 0);
-    const int it = block_scan(is_dec ? q : 0, lds, &tt) - (is_dec ? q : 0);
+    const int3 mine = make_int3(is_dec ? 1 : 0, is_pre ? 1 : 0, is_dec ? q : 0);
+    int3 tot;
+    const int3 incl = block_scan3(mine, lds, &tot);
+    const int id = incl.x - mine.x, ip = incl.y - mine.y, it = incl.z - mine.z;
+    const int td = tot.x, tp = tot.y, tt = tot.z;
     const int i = n_dec + id, j = n_pre + ip, k0 = n_tok + it;
     if (is_dec && i < r.n_dec) {
       r.dec_src[i] = b;
@@ -123,21 +131,6 @@ __global__ __launch_bounds__(256) void route_copy_kernel(RouteParams r) {
   for (int64_t c = threadIdx.x; c < r.row_bytes / 16; c += 256) d[c] = s[c];
 }
 
-// The small-q rows' outputs (and lse) from their compact rows to their batch tokens.
-__global__ __launch_bounds__(256) void route_scatter_kernel(const int* dec_tok, const char* dec_out,
-                                                            const float* dec_lse, char* out, float* lse,
-                                                            int64_t row_bytes, int num_heads) {
-  const int k = (int)blockIdx.x;
-  const int g = dec_tok[k];
-  if (g < 0) return;
-  const uint4* s = (const uint4*)(dec_out + (int64_t)k * row_bytes);
-  uint4* d = (uint4*)(out + (int64_t)g * row_bytes);
-  for (int64_t c = threadIdx.x; c < row_bytes / 16; c += 256) d[c] = s[c];
-  if (lse != nullptr)
-    for (int h = (int)threadIdx.x; h < num_heads; h += 256)
-      lse[(int64_t)g * num_heads + h] = dec_lse[(int64_t)k * num_heads + h];
-}
-
 }  // namespace
 
 hipError_t launch_route(const RouteParams& r, hipStream_t stream) {
@@ -147,14 +140,6 @@ hipError_t launch_route(const RouteParams& r, hipStream_t stream) {
   const int blocks = r.n_dec + r.n_pre + r.nt_cap;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(route_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, r);
-  return hipGetLastError();
-}
-
-hipError_t launch_route_scatter(const int* dec_tok, int nt_cap, const void* dec_out, const float* dec_lse, void* out,
-                                float* lse, int64_t row_bytes, int num_heads, hipStream_t stream) {
-  if (nt_cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)nt_cap), dim3(256), 0, stream, dec_tok,
-                     (const char*)dec_out, dec_lse, (char*)out, lse, row_bytes, num_heads);
   return hipGetLastError();
 }
 

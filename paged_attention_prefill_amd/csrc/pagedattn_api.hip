@@ -18,8 +18,9 @@ hipError_t launch_attn_mfma(const AttnParams& p, int q_kind, int kv_kind, int dp
                             hipStream_t stream);
 hipError_t launch_attn_valu(const AttnParams& p, int q_kind, int kv_kind, int dpad, int nblocks,
                             hipStream_t stream);
+// tok_map (nullable): record token t's output goes to token tok_map[t] (none if negative)
 hipError_t launch_merge(const float* partials, int S, int ntok, int H, int D, void* out, int out_kind,
-                        float* out_lse, bool strided, const float* sinks, hipStream_t stream);
+                        float* out_lse, bool strided, const float* sinks, const int* tok_map, hipStream_t stream);
 hipError_t mfma_occupancy(int q_kind, int kv_kind, int dpad, int* blocks_per_cu);
 hipError_t launch_attn_mfma_dma(const AttnParams& p, int q_kind, int dpad, int nblocks,
                                 hipStream_t stream);
@@ -387,7 +388,7 @@ static int run_attention(const void* q, int q_dtype, void* out, float* lse, cons
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (p.write_partial && out != nullptr) {  // out NULL: pass 1 only, the records stay in the workspace
     e = pa::launch_merge((const float*)workspace, splits, total_q, hq, kv->head_dim, out, kind_of(q_dtype), lse,
-                         part_keys > 0, p.sinks, stream);
+                         part_keys > 0, p.sinks, nullptr, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   (void)ws_bytes;
@@ -530,7 +531,7 @@ struct MixedSplit {
 };
 
 struct MixedLayout {
-  size_t meta, dec_bt, pre_bt, dec_q, dec_out, dec_lse, dec_rec, pre_rec, total;
+  size_t meta, dec_bt, pre_bt, dec_q, dec_rec, pre_rec, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -570,10 +571,6 @@ MixedLayout mixed_layout(int64_t total_q, const MixedSplit& s, int64_t max_pages
   o += align256(sizeof(int) * (size_t)(np * max_pages));
   m.dec_q = o;
   o += align256((size_t)(nt * hq * d * es));
-  m.dec_out = o;
-  o += align256((size_t)(nt * hq * d * es));
-  m.dec_lse = o;
-  o += align256(sizeof(float) * (size_t)(nt * hq));
   m.dec_rec = o;
   o += align256(sizeof(float) * (size_t)(nt * hq * dsplits * (d + 2)));
   m.pre_rec = o;
@@ -585,8 +582,6 @@ MixedLayout mixed_layout(int64_t total_q, const MixedSplit& s, int64_t max_pages
 
 namespace pa {
 hipError_t launch_route(const RouteParams& r, hipStream_t stream);
-hipError_t launch_route_scatter(const int* dec_tok, int nt_cap, const void* dec_out, const float* dec_lse, void* out,
-                                float* lse, int64_t row_bytes, int num_heads, hipStream_t stream);
 }  // namespace pa
 
 extern "C" {
@@ -689,7 +684,8 @@ int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const i
   pa::AttnParams pd, pp;
   int64_t nb_d = 0, nb_p = 0;
   if (nd > 0) {
-    st = plan_attention(pd, nb_d, r.dec_q, q_dtype, ws + ml.dec_out, (float*)(ws + ml.dec_lse), r.dec_cu,
+    // (decode pass 1 writes records only; the merge puts the rows into out)
+    st = plan_attention(pd, nb_d, r.dec_q, q_dtype, out, lse, r.dec_cu,
                         r.dec_seq_lens, r.dec_bt, nd, max_pages_per_seq, nt, ms.max_dec_q, num_q_heads, kv, scale,
                         decode_splits, decode_part_keys, true, opts, ws + ml.dec_rec);
     if (st != PA_OK) return st;
@@ -718,19 +714,17 @@ int pa_mixed_step(const void* q, int32_t q_dtype, void* out, float* lse, const i
   if (e != hipSuccess) return fail(PA_ERR_HIP, "mixed-step attention launch failed: %s", hipGetErrorString(e));
   // the chunks' merge runs over every token of the batch (records indexed by
   // batch token); the small-q rows' tokens get values from records no chunk
-  // wrote and are overwritten by the scatter that follows
+  // wrote and are overwritten by the decode merge that follows, which writes
+  // each compact token's rows to its batch token (dec_tok)
   if (nb_p > 0 && sp > 1) {
     e = pa::launch_merge((const float*)(ws + ml.pre_rec), sp, total_q, num_q_heads, D, out, kind_of(q_dtype), lse,
-                         false, pp.sinks, strm);
+                         false, pp.sinks, nullptr, strm);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   if (nb_d > 0) {
-    e = pa::launch_merge((const float*)(ws + ml.dec_rec), decode_splits, nt, num_q_heads, D, ws + ml.dec_out,
-                         kind_of(q_dtype), (float*)(ws + ml.dec_lse), decode_part_keys > 0, pd.sinks, strm);
-    if (e == hipSuccess)
-      e = pa::launch_route_scatter(r.dec_tok, nt, ws + ml.dec_out, (const float*)(ws + ml.dec_lse), out, lse,
-                                   r.row_bytes, num_q_heads, strm);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge / scatter launch failed: %s", hipGetErrorString(e));
+    e = pa::launch_merge((const float*)(ws + ml.dec_rec), decode_splits, nt, num_q_heads, D, out, kind_of(q_dtype),
+                         lse, decode_part_keys > 0, pd.sinks, r.dec_tok, strm);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();
 }
@@ -859,7 +853,7 @@ int pa_merge_states(const float* partials, int32_t num_splits, int32_t num_token
   if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
     return fail(PA_ERR_UNSUPPORTED, "too many rows");
   hipError_t e = pa::launch_merge(partials, num_splits, num_tokens, num_heads, head_dim, out, kind_of(out_dtype),
-                                  out_lse, false, nullptr, (hipStream_t)stream);
+                                  out_lse, false, nullptr, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -262,8 +262,9 @@ def test_mixed_step_arguments_are_checked_before_launch():
     # the layout: 2 small-q rows with 3 tokens, 1 chunk; 4 pages per row, 8 heads, D 64, fp16, 8 decode parts
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     nd, npre, nt = 2, 1, 3
-    want = (a(4 * (3 * nd + 1 + 4 * npre + nt)) + a(4 * nd * 4) + a(4 * npre * 4) + 2 * a(nt * 8 * 64 * 2)
-            + a(4 * nt * 8) + a(4 * nt * 8 * 8 * 66))
+    # metadata, block-table rows of each class, the small-q rows' gathered q, their records
+    want = (a(4 * (3 * nd + 1 + 4 * npre + nt)) + a(4 * nd * 4) + a(4 * npre * 4) + a(nt * 8 * 64 * 2)
+            + a(4 * nt * 8 * 8 * 66))
     need = ops.mixed_workspace_bytes(ql, 4, 8, 64, ops.PA_F16, 0, 8, 1)
     assert need == want
     need3 = ops.mixed_workspace_bytes(ql, 4, 8, 64, ops.PA_F16, 0, 8, 3)

@@ -141,3 +141,32 @@ def test_mixed_step_batch_order_does_not_change_a_row():
     (o0, l0), (o1, l1) = outs
     idx = token_index(c, perm).cuda()
     assert torch.equal(bits(o0[idx]), bits(o1)) and torch.equal(bits(l0[idx]), bits(l1))
+
+
+@pytest.mark.parametrize("D,kvk", [(256, "f16"), (64, "bf16")])
+def test_mixed_step_many_rows(D, kvk):
+    """1,500 rows (more than the routing's work group of 1,024 threads, so its
+    scans run over several waves and two chunks of rows): every row's output
+    and lse equal the separate decode and prefill calls on the two classes."""
+    rng = np.random.default_rng(D)
+    q_lens = rng.choice([0, 1, 1, 2, 5, 16, 17, 40], size=1500)
+    seq_lens = q_lens + rng.integers(0, 200, size=1500)
+    c = gen.make_case(f"mixed_many_{D}", q_lens=q_lens.tolist(), seq_lens=seq_lens.tolist(), num_q_heads=8,
+                      num_kv_heads=2, head_dim=D, page_size=32, q_kind=kvk, seed=D + 1)
+    d = gen.to_device(c)
+    small = [b for b, q in enumerate(q_lens) if 1 <= q <= ops.MIXED_DECODE_MAX_Q]
+    chunks = [b for b, q in enumerate(q_lens) if q > ops.MIXED_DECODE_MAX_Q]
+    say(f"  mixed step, {len(q_lens)} rows, D {D} {kvk}: {len(small)} small-q rows, {len(chunks)} chunks")
+    out, lse = ops.mixed_step(d["q"], d["k"], d["v"], d["cu"], q_lens, d["seq_lens"], d["bt"], c.scale,
+                              decode_splits=4, prefill_splits=1, return_lse=True)
+    torch.cuda.synchronize()
+    dec, pre = gen.select_seqs(c, small), gen.select_seqs(c, chunks)
+    dd, dp = gen.to_device(dec), gen.to_device(pre)
+    o_d, l_d = ops.split_kv_decode(dd["q"], dd["k"], dd["v"], dd["cu"], dd["seq_lens"], dd["bt"],
+                                   max(1, dec.max_seqlen_q), c.scale, num_splits=4, return_lse=True)
+    o_p, l_p = ops.paged_prefill(dp["q"], dp["k"], dp["v"], dp["cu"], dp["seq_lens"], dp["bt"], pre.max_seqlen_q,
+                                 c.scale, num_kv_splits=1, return_lse=True)
+    torch.cuda.synchronize()
+    ti_d, ti_p = token_index(c, small).cuda(), token_index(c, chunks).cuda()
+    assert torch.equal(bits(out[ti_d]), bits(o_d)) and torch.equal(bits(lse[ti_d]), bits(l_d))
+    assert torch.equal(bits(out[ti_p]), bits(o_p)) and torch.equal(bits(lse[ti_p]), bits(l_p))
