@@ -597,13 +597,13 @@ def main():
                          "ceilings: a pure MFMA loop and a streaming read, measured; "
                          "crossover: one small-q row through the decode and the prefill calls, q = 1..16; "
                          "sequences: the varlen prefill and its sequences launched alone")
-    ap.add_argument("--pmc-dir", default="gpurun_out",
+    ap.add_argument("--pmc-dir", default="pmc",
                     help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
     if a.mode == "traffic":
         return write_traffic(a.workload, a.pmc_dir)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not built)"}))
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
