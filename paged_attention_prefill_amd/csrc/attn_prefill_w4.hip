@@ -16,7 +16,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_w4_kernel(const AttnParam
 namespace {
 template <typename QT, int F8, int DPAD, int NST>
 hipError_t launch_w4(const AttnParams& p, int nblocks, hipStream_t stream) {
-  if (has_score_mods(p))
+  const bool cap = p.softcap_k2 != 0.0f, alibi = p.alibi_slopes != nullptr;
+  if (cap && alibi)
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 4>), dim3(nblocks), dim3(256), 0, stream, p);
+  else if (alibi)
+    hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 3>), dim3(nblocks), dim3(256), 0, stream, p);
+  else if (cap)
     hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 2>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (p.window_left >= 0)
     hipLaunchKernelGGL((attn_prefill_w4_kernel<QT, F8, DPAD, NST, 1>), dim3(nblocks), dim3(256), 0, stream, p);

@@ -97,16 +97,15 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&o)[NDB]) {
 // F8 = KV_E5M2 or KV_E4M3: K and V are fp8 (q fp16 or bf16); the tiles stay
 // 8-bit in LDS and are widened to the query's type as their MFMA operands are read.  F8 = 0: KV of
 // the q dtype.
-// VAR 0: no options that touch the scores; 1: a left sliding window; 2: score
-// modifiers (softcap / ALiBi, mod_score), with or without a window.  Each is
-// its own instantiation, so that the default one keeps no per-row state in
-// this tightly scheduled loop.
+// VAR 0: no options that touch the scores; 1: a left sliding window; 2: a
+// logit softcap; 3: ALiBi; 4: both (2 to 4 with or without a window).  Each is its own instantiation, so that the
+// default one keeps no per-row state in this tightly scheduled loop.
 template <typename QT, int F8, int DPAD, int NST, int VAR>
 __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, char* smem) {
   constexpr bool KV8 = F8 != 0;
-  constexpr bool WIN = VAR >= 1, MOD = VAR == 2;
+  constexpr bool WIN = VAR >= 1, MOD = VAR >= 2, CAP = VAR == 2;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
-  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2, false, VAR == 2> TL;
+  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2, false, MOD> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
@@ -349,12 +348,13 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // Causal / key-range / window mask on the scores of the tile starting at
   // key j0; only tiles that reach some row's last key or start before some
   // row's window need it.
+  // wave-uniform test: the tile ends past the wave's first row's limit (or
+  // the wave has rows past the end), or (window) starts before the window
+  // start of its last row
+  auto tile_masked = [&](int j0) { return j0 + kKT > wlim || (WIN && j0 < wlo); };
   auto mask_scores = [&](int j0) {
     if constexpr (WIN) {
-      // wave-uniform test: the tile ends past the wave's first row's limit
-      // (or the wave has rows past the end), or starts before the window
-      // start of its last row
-      if (j0 + kKT > wlim || j0 < wlo) {
+      if (tile_masked(j0)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           // key of element r: j0 + 8 (r / 4) + 4 hi + r % 4
@@ -367,7 +367,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
         }
       }
     } else {
-      if (j0 + kKT > wlim) {
+      if (tile_masked(j0)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int t = min(lim[rb], khi) - j0 - 4 * hi;
@@ -378,12 +378,38 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     }
   };
 
-  // Score modifiers of the tile starting at key j0, before its mask: scaled
-  // score -> mod_score, with the distance from the row's own key position
-  // (lim - 1; rows past the end are masked afterwards).
-  // Each modifier is tested once per tile (wave-uniform branches).
+  // Score modifiers of the tile starting at key j0, before its mask: raw score
+  // s -> scaled score t = score_scale s -> modified score, in log2 units.
+  // The softcap's c' tanh(t / c') (c' the cap in log2 units) is
+  // c' - 2 c' / (1 + e^(2 t / c')) with e^(2 t / c') = 2^(ks s): one exp2 and
+  // one reciprocal, the limits exact (2^x overflowing to inf gives c',
+  // underflowing to 0 gives -c').  The ALiBi bias of element r is -slope dist,
+  // dist = (lim - 1) - key, the distance from the row's own key position
+  // (rows past the end are masked afterwards).
+  // Without ALiBi the softcap runs in steps of two scores (cap_step) that the
+  // PV product of the previous tile places among its MFMAs.
+  constexpr int kCapSteps = CAP ? 16 : 0;
+  auto cap_step = [&](int j) {
+    const int rb = j & 1, q = j >> 1;
+    const float ks = score_scale * p.softcap_k2, m2c = -2.0f * p.softcap_l2;
+#pragma unroll
+    for (int r = 2 * q; r < 2 * q + 2; ++r)
+      s[rb][r] = __builtin_fmaf(m2c, __builtin_amdgcn_rcpf(1.0f + fast_exp2(s[rb][r] * ks)), p.softcap_l2);
+  };
   auto mod_mask = [&](int j0) {
-    if constexpr (MOD) {
+    if constexpr (CAP) {
+#pragma unroll
+      for (int j = 0; j < kCapSteps; ++j) cap_step(j);
+    } else if constexpr (VAR == 3) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float b0 = -slope[rb] * (float)(lim[rb] - 1 - j0 - 4 * hi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[rb][r] = __builtin_fmaf(s[rb][r], score_scale, __builtin_fmaf(slope[rb], (float)(8 * (r >> 2) + (r & 3)), b0));
+      }
+    } else if constexpr (MOD) {
+      // both: the scaled scores through mod_score, one modifier at a time
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -474,8 +500,18 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
 
   // PV of the previous tile with the softmax of the current one placed between
   // its MFMAs by hand (scheduling barriers keep every group where it is).
-  auto pv_softmax = [&](int pstage) {
-    constexpr int NMF = RB * NST2;
+  // CAP: the softcap steps of the current tile (key j0) come first, then its
+  // mask (a wave-uniform branch, taken on the few tiles that need it).
+  auto pv_softmax = [&](int pstage, int j0) {
+    constexpr int NMF = RB * NST2, NSTEP = kCapSteps + kSmSteps;
+    auto step = [&](int j) {
+      if (j < kCapSteps) {
+        cap_step(j);
+        if (j == kCapSteps - 1) mask_scores(j0);
+      } else {
+        sm_step(j - kCapSteps);
+      }
+    };
     const uint32_t vls = pstage * STAGE_BYTES + vlane;
     uint4 vf[VPF];
 #pragma unroll
@@ -490,7 +526,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
         oacc[rb][db] = Mf<QT>::run(a, pcur[rb][ks], oacc[rb][db]);
         const int i = st * RB + rb;
 #pragma unroll
-        for (int j = i * kSmSteps / NMF; j < (i + 1) * kSmSteps / NMF; ++j) sm_step(j);
+        for (int j = i * NSTEP / NMF; j < (i + 1) * NSTEP / NMF; ++j) step(j);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (st + VPF < NST2) vf[st % VPF] = vt_read(vls, st + VPF);
@@ -552,8 +588,8 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
       lds_barrier();
       const int j0 = kstart + it * kstep;
       qk_issue(it % NST);
-      mod_mask(j0);
-      pv_softmax((it - 1) % NST);
+      if constexpr (!CAP) mod_mask(j0);
+      pv_softmax((it - 1) % NST, j0);
       rescale();
       if (issued < ntiles) tl.fetch(issued);
 #pragma unroll
