@@ -581,6 +581,39 @@ def sequences(reps=20):
     return 0
 
 
+def operands(reps=20):
+    """The long-chunk prefill call with its real (random) operands and with Q,
+    K or V replaced by zeros: the same launch, the same instructions and the
+    same memory traffic, only the values the matrix cores multiply differ.  A
+    call that gets faster with zero operands is held back by the chip's power
+    (its clock drops with the switching activity of the MFMA data), not by its
+    instruction schedule.  One JSON line per operand set."""
+    stream = torch.cuda.current_stream()
+    case = gen.select_seqs(gen.long_chunk(), [0])
+    d = gen.to_device(case)
+    sp = ops.auto_splits(case.total_q, case.num_seqs, case.max_seqlen_q, case.num_q_heads, case.num_kv_heads,
+                         case.head_dim, ops._TORCH_TO_PA[case.q.dtype], ops._TORCH_TO_PA[case.q.dtype])
+    c = Call("prefill", case, d, sp)
+    f = call_flops("prefill", case)
+    keep = {k: d[k].clone() for k in ("q", "k", "v")}
+    for zeroed in ((), ("q",), ("k",), ("v",), ("k", "v"), ()):
+        for k in ("q", "k", "v"):
+            d[k].copy_(keep[k])
+            if k in zeroed:
+                d[k].zero_()
+        for _ in range(5):
+            c(stream)
+        torch.cuda.synchronize()
+        c.times, c.pass1 = [], []
+        for _ in range(reps):
+            c(stream, record=True)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "operands", "zero": list(zeroed), "splits": c.splits, "call_ms": c.ms_median(),
+                          "kernel_ms": c.kernel_ms(), "call_tflops": f / (c.ms_median() * 1e-3) / 1e12}),
+              flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -591,7 +624,7 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover", "sequences"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover", "sequences", "operands"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
                          "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU); "
                          "ceilings: a pure MFMA loop and a streaming read, measured; "
@@ -614,6 +647,8 @@ def main():
         return ceilings()
     if a.mode == "crossover":
         return crossover()
+    if a.mode == "operands":
+        return operands()
     if a.mode == "sequences":
         return sequences()
     ops.lib()

@@ -146,11 +146,25 @@ __device__ __forceinline__ float max_halves(float x) {
   return x;
 }
 
+// The same with the minimum.
+__device__ __forceinline__ float min_halves(float x) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_min_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
+}
+
 // max(a, b, c) without the canonicalizing moves the compiler adds around
 // fmaxf of MFMA results (the scores are never signalling NaNs).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 __device__ __forceinline__ float max2f(float a, float b) {

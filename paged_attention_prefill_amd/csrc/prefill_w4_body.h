@@ -352,6 +352,9 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // the wave has rows past the end), or (window) starts before the window
   // start of its last row
   auto tile_masked = [&](int j0) { return j0 + kKT > wlim || (WIN && j0 < wlo); };
+  // value of a masked element: the scaled score -inf, or (CAP, below) the
+  // reciprocal +inf that stands for it
+  constexpr float kMasked = CAP ? __builtin_huge_valf() : kNegInf;
   auto mask_scores = [&](int j0) {
     if constexpr (WIN) {
       if (tile_masked(j0)) {
@@ -362,7 +365,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
-            s[rb][r] = (c < t && c >= u) ? s[rb][r] : kNegInf;
+            s[rb][r] = (c < t && c >= u) ? s[rb][r] : kMasked;
           }
         }
       }
@@ -372,7 +375,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
         for (int rb = 0; rb < RB; ++rb) {
           const int t = min(lim[rb], khi) - j0 - 4 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kNegInf;
+          for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kMasked;
         }
       }
     }
@@ -386,15 +389,18 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // underflowing to 0 gives -c').  The ALiBi bias of element r is -slope dist,
   // dist = (lim - 1) - key, the distance from the row's own key position
   // (rows past the end are masked afterwards).
-  // Without ALiBi the softcap runs in steps of two scores (cap_step) that the
-  // PV product of the previous tile places among its MFMAs.
+  // Without ALiBi (CAP) the softcap runs in steps of two scores (cap_step)
+  // that the PV product of the previous tile places among its MFMAs, and it
+  // stops at the reciprocal r = 1 / (1 + 2^(ks s)): the modified score
+  // t = c' - 2 c' r is decreasing in r, so the softmax takes the row minimum
+  // of r for its maximum and folds t into its exponent's FMA
+  // (2^(t - m) = 2^(-2 c' r + (c' - m))); a masked element is r = +inf.
   constexpr int kCapSteps = CAP ? 16 : 0;
   auto cap_step = [&](int j) {
     const int rb = j & 1, q = j >> 1;
-    const float ks = score_scale * p.softcap_k2, m2c = -2.0f * p.softcap_l2;
+    const float ks = score_scale * p.softcap_k2;
 #pragma unroll
-    for (int r = 2 * q; r < 2 * q + 2; ++r)
-      s[rb][r] = __builtin_fmaf(m2c, __builtin_amdgcn_rcpf(1.0f + fast_exp2(s[rb][r] * ks)), p.softcap_l2);
+    for (int r = 2 * q; r < 2 * q + 2; ++r) s[rb][r] = __builtin_amdgcn_rcpf(1.0f + fast_exp2(s[rb][r] * ks));
   };
   auto mod_mask = [&](int j0) {
     if constexpr (CAP) {
@@ -427,26 +433,31 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // steps of two exponentials each, and the row-sum update.
   constexpr int kSmSteps = 30;
   float tmax[RB], nref[RB], ls[RB];
+  // (CAP: the same steps on r, with minima for maxima)
+  auto red3 = [&](float a, float b, float d) { return CAP ? min3f(a, b, d) : max3f(a, b, d); };
   auto sm_step = [&](int j) {
     const int rb = j & 1, k = j >> 1;
     if (k == 0) {  // elements 0..4
-      tmax[rb] = max3f(max3f(s[rb][0], s[rb][1], s[rb][2]), s[rb][3], s[rb][4]);
+      tmax[rb] = red3(red3(s[rb][0], s[rb][1], s[rb][2]), s[rb][3], s[rb][4]);
     } else if (k < 3) {  // elements 4k + 1 .. 4k + 4
-      tmax[rb] = max3f(max3f(tmax[rb], s[rb][4 * k + 1], s[rb][4 * k + 2]), s[rb][4 * k + 3], s[rb][4 * k + 4]);
+      tmax[rb] = red3(red3(tmax[rb], s[rb][4 * k + 1], s[rb][4 * k + 2]), s[rb][4 * k + 3], s[rb][4 * k + 4]);
     } else if (k == 3) {  // elements 13..15
-      tmax[rb] = max3f(max3f(tmax[rb], s[rb][13], s[rb][14]), s[rb][15], s[rb][15]);
+      tmax[rb] = red3(red3(tmax[rb], s[rb][13], s[rb][14]), s[rb][15], s[rb][15]);
     } else if (k == 4) {
-      tmax[rb] = max_halves(tmax[rb]) * c;
+      if constexpr (CAP) tmax[rb] = __builtin_fmaf(min_halves(tmax[rb]), -2.0f * p.softcap_l2, p.softcap_l2);
+      else tmax[rb] = max_halves(tmax[rb]) * c;
       need[rb] = __any(tmax[rb] > m[rb] + kTau);
     } else if (k == 5) {
       const float mnew = need[rb] ? max2f(m[rb], tmax[rb]) : m[rb];
       alpha[rb] = (need[rb] && mnew != kNegInf) ? fast_exp2(m[rb] - mnew) : 1.0f;
       m[rb] = mnew;
       nref[rb] = mnew == kNegInf ? 0.0f : -mnew;
+      if constexpr (CAP) nref[rb] += p.softcap_l2;
     } else if (k < 14) {
       const int q = k - 6;  // elements 2q, 2q + 1 -> packed word q
-      const float e0 = fast_exp2(__builtin_fmaf(s[rb][2 * q], c, nref[rb]));
-      const float e1 = fast_exp2(__builtin_fmaf(s[rb][2 * q + 1], c, nref[rb]));
+      const float ce = CAP ? -2.0f * p.softcap_l2 : c;
+      const float e0 = fast_exp2(__builtin_fmaf(s[rb][2 * q], ce, nref[rb]));
+      const float e1 = fast_exp2(__builtin_fmaf(s[rb][2 * q + 1], ce, nref[rb]));
       const uint32_t pk = Mf<QT>::pack2(e0, e1);
       ((uint32_t*)pnew[rb])[q] = pk;
       // the row sum adds the rounded P that the PV product uses
