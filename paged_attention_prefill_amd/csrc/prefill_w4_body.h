@@ -355,7 +355,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   // value of a masked element: the scaled score -inf, or (CAP, below) the
   // reciprocal +inf that stands for it
   constexpr float kMasked = CAP ? __builtin_huge_valf() : kNegInf;
-  auto mask_scores = [&](int j0) {
+  auto mask_on = [&](f32x16_t(&sv)[RB], int j0) {
     if constexpr (WIN) {
       if (tile_masked(j0)) {
 #pragma unroll
@@ -365,7 +365,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
-            s[rb][r] = (c < t && c >= u) ? s[rb][r] : kMasked;
+            sv[rb][r] = (c < t && c >= u) ? sv[rb][r] : kMasked;
           }
         }
       }
@@ -375,11 +375,13 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
         for (int rb = 0; rb < RB; ++rb) {
           const int t = min(lim[rb], khi) - j0 - 4 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? s[rb][r] : kMasked;
+          for (int r = 0; r < 16; ++r) sv[rb][r] = (8 * (r >> 2) + (r & 3)) < t ? sv[rb][r] : kMasked;
         }
       }
     }
   };
+
+  auto mask_scores = [&](int j0) { mask_on(s, j0); };
 
   // Score modifiers of the tile starting at key j0, before its mask: raw score
   // s -> scaled score t = score_scale s -> modified score, in log2 units.
@@ -435,14 +437,13 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   float tmax[RB], nref[RB], ls[RB];
   // (CAP: the same steps on r, with minima for maxima)
   auto red3 = [&](float a, float b, float d) { return CAP ? min3f(a, b, d) : max3f(a, b, d); };
-  auto sm_step = [&](int j) {
-    const int rb = j & 1, k = j >> 1;
+  auto sm_on = [&](f32x16_t& sv, int rb, int k) {
     if (k == 0) {  // elements 0..4
-      tmax[rb] = red3(red3(s[rb][0], s[rb][1], s[rb][2]), s[rb][3], s[rb][4]);
+      tmax[rb] = red3(red3(sv[0], sv[1], sv[2]), sv[3], sv[4]);
     } else if (k < 3) {  // elements 4k + 1 .. 4k + 4
-      tmax[rb] = red3(red3(tmax[rb], s[rb][4 * k + 1], s[rb][4 * k + 2]), s[rb][4 * k + 3], s[rb][4 * k + 4]);
+      tmax[rb] = red3(red3(tmax[rb], sv[4 * k + 1], sv[4 * k + 2]), sv[4 * k + 3], sv[4 * k + 4]);
     } else if (k == 3) {  // elements 13..15
-      tmax[rb] = red3(red3(tmax[rb], s[rb][13], s[rb][14]), s[rb][15], s[rb][15]);
+      tmax[rb] = red3(red3(tmax[rb], sv[13], sv[14]), sv[15], sv[15]);
     } else if (k == 4) {
       if constexpr (CAP) tmax[rb] = __builtin_fmaf(min_halves(tmax[rb]), -2.0f * p.softcap_l2, p.softcap_l2);
       else tmax[rb] = max_halves(tmax[rb]) * c;
@@ -456,8 +457,8 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
     } else if (k < 14) {
       const int q = k - 6;  // elements 2q, 2q + 1 -> packed word q
       const float ce = CAP ? -2.0f * p.softcap_l2 : c;
-      const float e0 = fast_exp2(__builtin_fmaf(s[rb][2 * q], ce, nref[rb]));
-      const float e1 = fast_exp2(__builtin_fmaf(s[rb][2 * q + 1], ce, nref[rb]));
+      const float e0 = fast_exp2(__builtin_fmaf(sv[2 * q], ce, nref[rb]));
+      const float e1 = fast_exp2(__builtin_fmaf(sv[2 * q + 1], ce, nref[rb]));
       const uint32_t pk = Mf<QT>::pack2(e0, e1);
       ((uint32_t*)pnew[rb])[q] = pk;
       // the row sum adds the rounded P that the PV product uses
@@ -466,20 +467,22 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
       lsum[rb] = __builtin_fmaf(lsum[rb], alpha[rb], ls[rb]);
     }
   };
+  auto sm_step = [&](int j) { sm_on(s[j & 1], j & 1, j >> 1); };
   // Keeps the softmax results in the block that computed them (otherwise the
   // compiler sinks the exponentials below the rescale branch).
-  auto pin_softmax = [&]() {
+  auto pin_rb = [&](int rb) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        i32x4 t = __builtin_bit_cast(i32x4, pnew[rb][ks]);
-        asm volatile("" : "+v"(t));
-        pnew[rb][ks] = __builtin_bit_cast(uint4, t);
-      }
-      asm volatile("" : "+v"(lsum[rb]));
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x4 t = __builtin_bit_cast(i32x4, pnew[rb][ks]);
+      asm volatile("" : "+v"(t));
+      pnew[rb][ks] = __builtin_bit_cast(uint4, t);
     }
+    asm volatile("" : "+v"(lsum[rb]));
+  };
+  auto pin_softmax = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) pin_rb(rb);
   };
   auto softmax = [&]() {
 #pragma unroll
