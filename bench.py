@@ -447,8 +447,10 @@ def write_traffic(workload_name, pmc_dir):
 def ceilings(seed=0):
     """Measured chip ceilings beside the published peaks: a pure MFMA loop on
     random and on zero fp16 operands (with the shader clock it ran at), the same
-    loop fed a fresh random A fragment from LDS for every pair of MFMAs, and a
-    streaming read of 4 GiB."""
+    loop fed a fresh random A fragment from LDS for every pair of MFMAs, the
+    same loop with 0-8 fma or exp instructions after every MFMA (shader-clock
+    cycles per MFMA: how much vector work one wave hides behind its own MFMAs),
+    and a streaming read of 4 GiB."""
     import ctypes
     L = ops.lib()
     P, I = ctypes.c_void_p, ctypes.c_int32
@@ -502,6 +504,20 @@ def ceilings(seed=0):
     res["mfma_f16_lds_random_tflops"] = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
     res["mfma_f16_lds_random_clock_ghz"] = float(torch.median(c[:, 0] / c[:, 1]) * 0.1)
     res["mfma_f16_lds_random_cycles_per_mfma"] = float(torch.median(c[:, 0])) / (iters * 4)
+    # vector-ALU work after every MFMA (one wave per SIMD): how much of it the wave hides
+    L.pa_ceiling_mfma_valu.argtypes = [P, P, I, I, I, I, P, P]
+    a = torch.randn(128 * 8, generator=g).half().cuda()
+    coissue = {}
+    for kind, kname in ((0, "fma"), (1, "exp")):
+        for nv in (0, 2, 4, 6, 8):
+            def run_v():
+                st = L.pa_ceiling_mfma_valu(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(sink.data_ptr()), blocks,
+                                            iters // 4, nv, kind, ctypes.c_void_p(clocks.data_ptr()), sp)
+                assert st == 0, st
+            timed(run_v, 1)
+            c = clocks.view(-1, 2).cpu().double()
+            coissue[f"{kname}_{nv}"] = round(float(torch.median(c[:, 0])) / (iters // 4 * 4), 2)
+    res["mfma_cycles_with_valu_per_mfma"] = coissue
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
     rsink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")

@@ -15,6 +15,11 @@
  *   operands[2048..2303] (four register fragments); per iteration 2 LDS reads
  *   and 4 MFMAs (iters is rounded down to even).  sink / clocks / return
  *   codes as pa_ceiling_mfma.
+ * pa_ceiling_mfma_valu: pa_ceiling_mfma's loop with `nvalu` (0, 2, 4, 6 or
+ *   8) independent vector-ALU instructions after every MFMA, v_fma_f32
+ *   (kind 0) or v_exp_f32 (kind 1), on registers the MFMAs do not use; one
+ *   wave per SIMD.  operands[0..127], sink, clocks and return codes as
+ *   pa_ceiling_mfma (-1 also for an unsupported nvalu or kind).
  * pa_ceiling_stream_read: `blocks` x 256 threads read `bytes` (a multiple of
  *   16, 16-byte aligned) of `src` once with 16-byte non-temporal loads, each
  *   block one contiguous range; sink[blocks * 256] receives one float per
@@ -33,6 +38,8 @@ int pa_ceiling_mfma(const void *operands, float *sink, int32_t blocks, int32_t i
                     unsigned long long *clocks, void *stream);
 int pa_ceiling_mfma_lds(const void *operands, float *sink, int32_t blocks, int32_t iters,
                         unsigned long long *clocks, void *stream);
+int pa_ceiling_mfma_valu(const void *operands, float *sink, int32_t blocks, int32_t iters, int32_t nvalu,
+                         int32_t kind, unsigned long long *clocks, void *stream);
 int pa_ceiling_stream_read(const void *src, int64_t bytes, float *sink, int32_t blocks, void *stream);
 
 #ifdef __cplusplus
