@@ -17,7 +17,8 @@ stream the kernels run on.  `roofline` prices the prefill call (its attention
 kernel plus, when the keys are split, the merge of the parts; a split prefill
 runs as pass 1 and the merge with an event between them, so the kernel alone
 is reported beside it) against the MFMA fp16 dense peak; `decode_roofline`
-prices the decode call against the HBM peak.  `cpu_baseline` times the fp64
+prices the decode call, with the caches flushed before each call, against
+the HBM peak (the warm figure beside it).  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on the host cores, and the
 whole oracle on the tiny, decode-batch and varlen workloads on all threads and
 on one.
@@ -778,6 +779,14 @@ def main():
         b = parts["decode"]["bytes"]
         res["decode_cold"] = {"ms_median": ms, "gbs": b / (ms * 1e-3) / 1e9, "reps": len(c.times),
                               "note": "1 GiB scratch read before each repetition"}
+        if "decode_roofline" in res:
+            # the decode roofline is priced on the cache-flushed calls (no K/V
+            # left in the Infinity Cache by the step), the warm figure beside it
+            dr = res["decode_roofline"]
+            dr["achieved_warm"] = dr["achieved"]
+            dr["achieved"] = res["decode_cold"]["gbs"]
+            dr["frac"] = dr["achieved"] / HBM_PEAK_GBS
+            dr["timing"] = "median of the cache-flushed calls"
     pre = [c for c in calls if c.kind == "prefill"]
     if pre:
         res["kv_write"] = kv_write_timing(pre[0].case, pre[0].d, max(5, min(a.steps, 20)))
