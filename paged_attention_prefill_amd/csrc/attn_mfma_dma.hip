@@ -29,7 +29,7 @@ using namespace mf;
 
 // MOD: softcap / ALiBi score modifiers (mod_score) on every visible score.
 template <typename QT, int DPAD, int WAVES, int RB, int NST, bool MOD = false>
-__global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void attn_mfma_dma_kernel(
+__global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
     const AttnParams p) {
   constexpr int WROWS = 32 * RB;                // query rows per wave (RB blocks of 32)
   constexpr int ROWS = WROWS * WAVES;
@@ -37,7 +37,6 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
   constexpr int ROWB = TL::ROWB;                // bytes per key row in LDS
   constexpr int TILE_BYTES = TL::TILE_BYTES;    // one K (or V) tile
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
-  constexpr int LPW = TL::LPW;                  // DMA instructions per wave per tile
   constexpr int NKK = DPAD / 16;
   constexpr int NDB = DPAD / 32;
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
@@ -110,9 +109,23 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
 
   const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
 
-  TileLoader<DPAD, WAVES> tl;
-  tl.init(p, seq, kvh, wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
-  auto issue = [&](int it, int stage) { tl.issue(it, stage); };
+  // Ping-pong (two waves per SIMD): the late wave group runs each tile's PV
+  // one iteration after its softmax, so one group's softmax overlaps the
+  // other group's MFMAs.  The late group carries that PV between the barrier
+  // and its softmax, the early group its own PV after its softmax and then
+  // waits at the next barrier, so the early group alone loads the tiles
+  // (all of a tile's DMA instructions, the page ids of the next tile read
+  // one tile ahead): the load issue and its scalar-load latency leave the
+  // late group's path.
+  constexpr bool PP = (WAVES == 8);
+  constexpr int IW = PP ? WAVES / 2 : WAVES;  // waves that load the tiles
+  const bool late = PP && wave >= WAVES / 2;
+  typedef TileLoader<DPAD, IW> TLI;
+  constexpr int ILPW = TLI::LPW;  // DMA instructions per loading wave per tile
+  TLI tl;
+  // (initialised in every wave, so that it stays in registers; the late
+  // waves never use it)
+  tl.init(p, seq, kvh, late ? wave - IW : wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
 
   // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
   // is an XOR of a lane constant with the loop index on bits that do not
@@ -217,30 +230,48 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 && DPAD <= 128 ? 2 : 1)) void 
     }
   };
 
-  // Ping-pong (two waves per SIMD): the late wave group runs each tile's PV
-  // one iteration after its softmax, so one group's softmax overlaps the
-  // other group's MFMAs.  Tiles are then read up to one iteration after their
-  // barrier, so the loads run DIST = NST - 2 tiles ahead instead of NST - 1.
-  constexpr bool PP = (WAVES == 8);
+  // With ping-pong, tiles are read up to one iteration after their barrier,
+  // so the loads run DIST = NST - 2 tiles ahead instead of NST - 1.
   constexpr int DIST = PP ? NST - 2 : NST - 1;
-  const bool late = PP && wave >= WAVES / 2;
 
   drain_visible_loads();
 
+  // `issued` advances in every wave (the ring's bookkeeping), the loads
+  // only in the loading waves
   int issued = 0;
 #pragma unroll
   for (int i = 0; i < DIST; ++i)
-    if (issued < ntiles) issue(issued, issued), ++issued;
+    if (issued < ntiles) {
+      if (!late) tl.issue(issued, issued);
+      ++issued;
+    }
+  if (!late && issued < ntiles) tl.fetch(issued);
 
   for (int it = 0; it < ntiles; ++it) {
-    wait_tiles<LPW, DIST - 1>(issued - it - 1);  // this tile's own loads have landed
+    // a loading wave waits for its own loads of this tile; the barrier then
+    // covers every wave
+    if (!late) wait_tiles<ILPW, DIST - 1>(issued - it - 1);
     lds_barrier();
-    if (issued < ntiles) issue(issued, issued % NST), ++issued;
+    if (issued < ntiles) {
+      if (!late) {
+        tl.begin(issued % NST);
+        if (tl.fast()) {
+#pragma unroll
+          for (int n = 0; n < ILPW; ++n) tl.template part<true>(n);
+        } else {
+#pragma unroll
+          for (int n = 0; n < ILPW; ++n) tl.template part<false>(n);
+        }
+      }
+      ++issued;
+    }
     const int j0 = kfirst + it * kKT;
     const bool live = wave_active && j0 < wave_kend;
     if (late && it > 0 && wave_active && j0 - kKT < wave_kend) pv((it - 1) % NST);
     if (live) qk_softmax(it % NST, j0);
     if (!late && live) pv(it % NST);
+    // page ids of the next tile to load, read during the next barrier's wait
+    if (!late && issued < ntiles) tl.fetch(issued);
   }
   if (late && ntiles > 0 && wave_active && kfirst + (ntiles - 1) * kKT < wave_kend) pv((ntiles - 1) % NST);
 
