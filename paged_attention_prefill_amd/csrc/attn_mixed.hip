@@ -61,9 +61,9 @@ hipError_t launch_attn_mixed(const AttnParams& pp, const AttnParams& pd, int q_k
   if (q_kind == KV_BF16 && kv_kind == KV_E4M3)
     return launch_mixed<__bf16, KV_E4M3, 8, 2>(pp, pd, prefill_blocks, decode_blocks, stream);
   if (q_kind == KV_F16 && kv_kind == KV_F16)
-    return launch_mixed<_Float16, 0, 5, 1>(pp, pd, prefill_blocks, decode_blocks, stream);
+    return launch_mixed<_Float16, 0, 4, 1>(pp, pd, prefill_blocks, decode_blocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_BF16)
-    return launch_mixed<__bf16, 0, 5, 1>(pp, pd, prefill_blocks, decode_blocks, stream);
+    return launch_mixed<__bf16, 0, 4, 1>(pp, pd, prefill_blocks, decode_blocks, stream);
   return hipErrorInvalidValue;
 }
 

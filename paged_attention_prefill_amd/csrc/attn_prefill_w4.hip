@@ -41,8 +41,8 @@ hipError_t launch_attn_prefill_w4(const AttnParams& p, int q_kind, int kv_kind, 
   if (q_kind == KV_F16 && kv_kind == KV_E4M3) return launch_w4<_Float16, KV_E4M3, 256, 8>(p, nblocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_E5M2) return launch_w4<__bf16, KV_E5M2, 256, 8>(p, nblocks, stream);
   if (q_kind == KV_BF16 && kv_kind == KV_E4M3) return launch_w4<__bf16, KV_E4M3, 256, 8>(p, nblocks, stream);
-  if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, 0, 256, 5>(p, nblocks, stream);
-  if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, 0, 256, 5>(p, nblocks, stream);
+  if (q_kind == KV_F16 && kv_kind == KV_F16) return launch_w4<_Float16, 0, 256, 4>(p, nblocks, stream);
+  if (q_kind == KV_BF16 && kv_kind == KV_BF16) return launch_w4<__bf16, 0, 256, 4>(p, nblocks, stream);
   return hipErrorInvalidValue;
 }
 
@@ -50,7 +50,7 @@ hipError_t prefill_w4_occupancy(int q_kind, int dpad, int* blocks_per_cu) {
   (void)q_kind;
   if (dpad == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 5, 0>, 256, 0);
+                                                        attn_prefill_w4_kernel<_Float16, 0, 256, 4, 0>, 256, 0);
   return hipErrorInvalidValue;
 }
 

@@ -248,7 +248,13 @@ __device__ __forceinline__ uint4 read_vt8(const char* a) {
 // page bases, part<FAST>(n) issues DMA instruction n of this wave.  FAST may
 // be used when fast() holds (one page, every key inside the range).
 // DESC: tiles are fetched in descending key order (a negative stride).
-template <int DPAD, int WAVES, int ES = 2, bool NT = false, bool DESC = false>
+// PIDL: the page ids may come from a table in LDS (set_pid_table) instead of
+// scalar loads of the block table.  A scalar load still in flight makes every
+// later wait for an LDS read a wait for everything (scalar loads return out of
+// order), so a loop that reads page ids from the block table while LDS reads
+// are outstanding pays the scalar load's latency; from LDS it does not.
+// Without a table, a fetch then waits for its own scalar loads.
+template <int DPAD, int WAVES, int ES = 2, bool NT = false, bool DESC = false, bool PIDL = false>
 struct TileLoader {
   static_assert(ES == 2 || (ES == 1 && DPAD == 256), "8-bit KV tiles are laid out for D 256");
   static constexpr int CPK = DPAD * ES / 16;
@@ -273,6 +279,10 @@ struct TileLoader {
   const char* vbase;
   const __attribute__((address_space(4))) int* btc;
   uint32_t lds0;
+  // PIDL: page ids pid_base .. of the group's keys in LDS (when pid_on)
+  const __attribute__((address_space(3))) int* pid_tab;
+  int pid_base;
+  bool pid_on;
 
   __device__ __forceinline__ void init(const AttnParams& p, int seq, int kvh, int wave_, int lane_, int klo_,
                                        int kend_, uint32_t lds0_) {
@@ -313,6 +323,15 @@ struct TileLoader {
   // with DESC; kKT unless set, -kKT with DESC).
   __device__ __forceinline__ void set_stride(int step) { kstep = step; }
 
+  // PIDL: page ids from the table at LDS byte `tab_byte` (entry i = block-table
+  // entry base + i, covering every page a fetch reads) when `on`, else from
+  // the block table.
+  __device__ __forceinline__ void set_pid_table(bool on, uint32_t tab_byte, int base) {
+    pid_on = on;
+    pid_tab = (const __attribute__((address_space(3))) int*)(uintptr_t)tab_byte;
+    pid_base = base;
+  }
+
   // Reads the page ids of the next tile (keys klo + step * it ...); calls come in tile order.
   __device__ __forceinline__ void fetch(int it) {
     (void)it;
@@ -331,12 +350,28 @@ struct TileLoader {
     // is only used when the tile reaches it; otherwise the first is re-read),
     // so nothing waits for these loads before the tile's refill begins
     const int pg2 = (f_first < kKT && (pg + 1) * P < kend) ? pg + 1 : pg;
-    f_pa = btc[pg];
-    f_pb = btc[pg2];
+    if constexpr (PIDL) {
+      if (pid_on) {
+        // LDS reads into vector registers; begin() moves them to scalars
+        f_pa = pid_tab[pg - pid_base];
+        f_pb = pid_tab[pg2 - pid_base];
+      } else {
+        f_pa = btc[pg];
+        f_pb = btc[pg2];
+        asm volatile("" : "+s"(f_pa), "+s"(f_pb));  // the scalar loads complete here
+      }
+    } else {
+      f_pa = btc[pg];
+      f_pb = btc[pg2];
+    }
   }
 
   // Page bases of the fetched tile, to be loaded into `stage`.
   __device__ __forceinline__ void begin(int stage) {
+    if constexpr (PIDL) {
+      f_pa = __builtin_amdgcn_readfirstlane(f_pa);
+      f_pb = __builtin_amdgcn_readfirstlane(f_pb);
+    }
     tA = (int64_t)f_pa * sp_b + (int64_t)f_off * st_b;
     tB = (int64_t)f_pb * sp_b - (int64_t)f_first * st_b;
     tfirst = f_first;

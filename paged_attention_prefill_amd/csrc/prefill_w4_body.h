@@ -35,6 +35,9 @@ namespace pa {
 
 using namespace mf;
 
+// Entries of a work group's page-id table in LDS (32 KB).
+constexpr int kPidMax = 8192;
+
 namespace {
 
 // c = a * b (+ c unless `first`), accumulator in VGPRs.  VALU_A: `a` was just
@@ -105,7 +108,7 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   constexpr bool KV8 = F8 != 0;
   constexpr bool WIN = VAR >= 1, MOD = VAR >= 2, CAP = VAR == 2;
   constexpr int WAVES = 4, RB = 2, WROWS = 64, ROWS = WAVES * WROWS;
-  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2, false, MOD> TL;
+  typedef TileLoader<DPAD, WAVES, KV8 ? 1 : 2, false, MOD, true> TL;
   constexpr int ROWB = TL::ROWB;
   constexpr int TILE_BYTES = TL::TILE_BYTES;
   constexpr int STAGE_BYTES = TL::STAGE_BYTES;
@@ -282,6 +285,22 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   const int kstep = MOD ? -kKT : kKT;
   TL tl;
   tl.init(p, seq, kvh, wave, lane, kstart, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  // The group's page ids (pages kfirst / P .. (kend - 1) / P) are copied to
+  // the table after the ring, so that the tile loop reads them from LDS
+  // instead of the block table; a group with more than kPidMax pages reads
+  // the block table (and waits for it) at every tile.
+  {
+    const int pid_first = kfirst / p.page_size;
+    const int pid_n = (kend - 1) / p.page_size - pid_first + 1;
+    const bool pid_on = pid_n <= kPidMax;
+    if (pid_on) {
+      const int* bt = p.block_tables + (int64_t)seq * p.max_pages + pid_first;
+      int* tab = (int*)(smem + NST * STAGE_BYTES);
+      for (int i = tid; i < pid_n; i += ROWS) tab[i] = bt[i];
+    }
+    tl.set_pid_table(pid_on, (uint32_t)(uintptr_t)(&smem[0]) + NST * STAGE_BYTES, pid_first);
+    __syncthreads();  // the table is complete before any wave fetches
+  }
 
   const uint32_t klane = k_frag_lane(r32, hi);
   const int tg = lane >> 4, tk = lane & 15;
@@ -618,10 +637,10 @@ __device__ __forceinline__ void prefill_w4_body(const AttnParams& p, int bid, ch
   epilogue(std::false_type());
 }
 
-// LDS of the body: NST stages of one K and one V tile.
+// LDS of the body: NST stages of one K and one V tile, then the page-id table.
 template <int F8, int DPAD, int NST>
 constexpr int prefill_w4_lds_bytes() {
-  return NST * TileLoader<DPAD, 4, F8 != 0 ? 1 : 2>::STAGE_BYTES;
+  return NST * TileLoader<DPAD, 4, F8 != 0 ? 1 : 2>::STAGE_BYTES + kPidMax * 4;
 }
 
 }  // namespace pa

@@ -491,6 +491,19 @@ def test_long_chunk_prefill_every_row(long_chunk_ref, splits):
         compare("long chunk decode row", "f16", od.float().cpu().numpy(), rd, ld.cpu().numpy(), rld)
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+def test_prefill_page_ids_past_the_lds_table(splits):
+    """A work group whose keys span more pages than its LDS page-id table holds
+    (8192): 140,000 keys at page 16 are 8750 pages, read from the block table at
+    every tile when unsplit; with 2 parts each group's 4375 pages come from the
+    table.  Every row against the oracle."""
+    case = gen.make_case("page ids past the table", q_lens=[32], seq_lens=[140_000], num_q_heads=4,
+                         num_kv_heads=1, head_dim=256, page_size=16, q_kind="f16", seed=41)
+    ref, rl = run_oracle(case)
+    out, lse = gpu_prefill(case, splits=splits)
+    compare(f"8750 pages, S={splits}", "f16", out, ref, lse, rl)
+
+
 @pytest.mark.parametrize("kv_kind", ["f16", "e5m2"])
 def test_mixed_step_every_row(kv_kind):
     """The mixed step: the verify row (q=5 at 240,000 keys, 64 parts) and every
