@@ -56,7 +56,7 @@ def draw(seed):
                 splits=splits, parts=parts, part_keys=part_keys)
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_configuration(seed):
     c = draw(seed)
     say(f"  case {seed}: {c['qk']}/{c['kvk']} D {c['D']} Hq {c['Hq']} Hkv {c['Hkv']} P {c['P']} q {c['q_lens']} "
