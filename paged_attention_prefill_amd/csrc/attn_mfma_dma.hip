@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
           tmax = fmaxf(tmax, v);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_halves(tmax);  // the other lane half of the row, by v_permlane32_swap (no LDS round trip)
       if (__any(tmax > m[rb] + kTau)) {
         const float mnew = fmaxf(m[rb], tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[rb] - mnew);

@@ -259,7 +259,7 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
       s[r] = v;
       tmax = fmaxf(tmax, v);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_halves(tmax);  // the other lane half of the row, by v_permlane32_swap (no LDS round trip)
     // the running max of a row moves on that row's own scores only (a row
     // that does not need it is multiplied by exactly 1), so a row's bits do
     // not depend on the other rows packed with it: a verify row's token
