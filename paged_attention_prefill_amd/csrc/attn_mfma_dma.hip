@@ -159,35 +159,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float tmax = kNegInf;
+      float tmax;
+      // c: the factor from the scores in `s` to log2 units (the modifier
+      // pass scales them itself; otherwise the softmax scale enters the row
+      // max once and each exponent's FMA)
+      const float c = MOD ? 1.0f : score_scale;
       if constexpr (MOD) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[rb][r] *= score_scale;
         mod_scores16(p, s[rb], slope[rb], L - qlen + tok[rb] - j0 - 4 * hi);
+      }
+      if (MOD || __any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float v = (key < lim[rb] && key >= lo[rb]) ? s[rb][r] : kNegInf;
-          s[rb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      } else if (__any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float v = (key < lim[rb] && key >= lo[rb]) ? s[rb][r] * score_scale : kNegInf;
-          s[rb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = s[rb][r] * score_scale;
-          s[rb][r] = v;
-          tmax = fmaxf(tmax, v);
+          s[rb][r] = (key < lim[rb] && key >= lo[rb]) ? s[rb][r] : kNegInf;
         }
       }
-      tmax = max_halves(tmax);  // the other lane half of the row, by v_permlane32_swap (no LDS round trip)
+      // row max of the 16 scores in two chains of v_max3, then the other lane
+      // half of the row by v_permlane32_swap (no LDS round trip)
+      const float ma = max3f(max3f(max3f(s[rb][0], s[rb][1], s[rb][2]), s[rb][3], s[rb][4]), s[rb][5], s[rb][6]);
+      const float mb = max3f(max3f(max3f(s[rb][7], s[rb][8], s[rb][9]), s[rb][10], s[rb][11]), s[rb][12], s[rb][13]);
+      tmax = max_halves(max3f(ma, mb, max2f(s[rb][14], s[rb][15]))) * c;
       if (__any(tmax > m[rb] + kTau)) {
         const float mnew = fmaxf(m[rb], tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[rb] - mnew);
@@ -196,14 +189,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
         for (int db = 0; db < NDB; ++db) oacc[rb][db] *= alpha;
         m[rb] = mnew;
       }
-      const float mref = m[rb] == kNegInf ? 0.0f : m[rb];
+      const float nref = m[rb] == kNegInf ? 0.0f : -m[rb];
       uint32_t* pw = (uint32_t*)pf[rb];
       float ls = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float e0 = fast_exp2(s[rb][r] - mref), e1 = fast_exp2(s[rb][r + 1] - mref);
-        ls += e0 + e1;
-        pw[r >> 1] = Mf<QT>::pack2(e0, e1);
+        const float e0 = fast_exp2(__builtin_fmaf(s[rb][r], c, nref));
+        const float e1 = fast_exp2(__builtin_fmaf(s[rb][r + 1], c, nref));
+        const uint32_t pk = Mf<QT>::pack2(e0, e1);
+        pw[r >> 1] = pk;
+        // the row sum adds the rounded P that the PV product uses
+        ls = Mf<QT>::sum2(pk, ls);
       }
       lsum[rb] += ls;
     }
