@@ -246,20 +246,31 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
       ++nh;
     }
 
-    float tmax = kNegInf;
+    // c: the factor from the scores in `s` to log2 units (the modifier pass
+    // scales them itself; otherwise the softmax scale enters the row max once
+    // and each exponent's FMA)
+    const float c = MOD ? 1.0f : score_scale;
     if constexpr (MOD) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] *= score_scale;
       mod_scores16(p, s, slope, L - qlen + tok - j0 - 4 * hi);
     }
+    // Only tiles that reach a valid row's last key (or the part's end) or start
+    // before its window need the mask: on the others it is the identity for
+    // every valid row.  Rows past the group's end (lim 0) have zero queries,
+    // so their unmasked scores are finite, and their outputs are never written.
+    if (MOD || __any(valid && (j0 + kKT > lim || j0 < lo))) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float v = (key < lim && key >= lo) ? (MOD ? s[r] : s[r] * score_scale) : kNegInf;
-      s[r] = v;
-      tmax = fmaxf(tmax, v);
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = (key < lim && key >= lo) ? s[r] : kNegInf;
+      }
     }
-    tmax = max_halves(tmax);  // the other lane half of the row, by v_permlane32_swap (no LDS round trip)
+    // row max in two chains of v_max3, then the other lane half of the row by
+    // v_permlane32_swap (no LDS round trip)
+    const float ma = max3f(max3f(max3f(s[0], s[1], s[2]), s[3], s[4]), s[5], s[6]);
+    const float mb = max3f(max3f(max3f(s[7], s[8], s[9]), s[10], s[11]), s[12], s[13]);
+    const float tmax = max_halves(max3f(ma, mb, max2f(s[14], s[15]))) * c;
     // the running max of a row moves on that row's own scores only (a row
     // that does not need it is multiplied by exactly 1), so a row's bits do
     // not depend on the other rows packed with it: a verify row's token
@@ -273,15 +284,18 @@ __device__ __forceinline__ void decode_body(const AttnParams& p, int bid, char* 
       for (int j = 0; j < NDB; ++j) oacc[j] *= alpha;
       m = mnew;
     }
-    const float mref = m == kNegInf ? 0.0f : m;
+    const float nref = m == kNegInf ? 0.0f : -m;
     uint4 pf[2];
     uint32_t* pw = (uint32_t*)pf;
     float ls = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float e0 = fast_exp2(s[r] - mref), e1 = fast_exp2(s[r + 1] - mref);
-      ls += e0 + e1;
-      pw[r >> 1] = Mf<QT>::pack2(e0, e1);
+      const float e0 = fast_exp2(__builtin_fmaf(s[r], c, nref));
+      const float e1 = fast_exp2(__builtin_fmaf(s[r + 1], c, nref));
+      const uint32_t pk = Mf<QT>::pack2(e0, e1);
+      pw[r >> 1] = pk;
+      // the row sum adds the rounded P that the PV product uses
+      ls = Mf<QT>::sum2(pk, ls);
     }
     lsum += ls;
 
