@@ -9,6 +9,7 @@ followed by the split-KV decode of a q=1 row over the same 152,048-token cache
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload long_chunk|mixed_step|mixed_step_fp8|mixed_step_e4m3|decode_batch|varlen]
+    python bench.py --mode copy|traffic|ceilings|crossover|sequences|operands|options
 
 Prints ONE JSON line.  `value` is the step's algorithmic FLOPs (causal-exact:
 4 * D * Hq per attended pair) divided by the step time; the prefill TFLOPS and
@@ -25,6 +26,7 @@ on one.
 """
 
 import argparse
+import copy
 import json
 import os
 import sys
@@ -631,6 +633,43 @@ def operands(reps=20):
     return 0
 
 
+def options(reps=8):
+    """What the score options cost each kernel: the long-chunk prefill (4
+    parts) and q=1 decode row at D 256, the varlen prefill and the decode
+    batch at D 128, each plain, with a logit softcap of 30, with ALiBi and
+    with both, the four calls of one case interleaved in one process.  One
+    JSON line per case with the median call time of each option set (µs)."""
+    stream = torch.cuda.current_stream()
+    lc = gen.long_chunk()
+    cases = [("long chunk prefill, D 256", "prefill", gen.select_seqs(lc, [0]), 4),
+             ("long-chunk decode row q=1, D 256", "decode", gen.select_seqs(lc, [1]), 64),
+             ("varlen prefill, D 128", "prefill", gen.varlen_prefill(kind="bf16"), 1),
+             ("decode batch, 32 rows, D 128", "decode", gen.decode_batch(kind="bf16"), 16)]
+    sets = {"plain": {}, "softcap 30": {"softcap": 30.0}, "ALiBi": {"alibi": True},
+            "both": {"softcap": 30.0, "alibi": True}}
+    for label, kind, case, splits in cases:
+        d = gen.to_device(case)
+        calls = {}
+        for name, o in sets.items():
+            c = copy.copy(case)
+            c.meta = {**case.meta, **o}
+            calls[name] = Call(kind, c, d, splits)
+        for c in calls.values():
+            for _ in range(2):
+                c(stream)
+        torch.cuda.synchronize()
+        for c in calls.values():
+            c.times, c.pass1 = [], []
+        for _ in range(reps):
+            for c in calls.values():
+                c(stream, record=True)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "options", "call": label, "splits": splits,
+                          "median_us": {n: c.ms_median() * 1e3 for n, c in calls.items()}}), flush=True)
+        del d, calls
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -641,12 +680,15 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query tokens in the oracle sample")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover", "sequences", "operands"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "traffic", "ceilings", "crossover", "sequences", "operands",
+                                                      "options"],
                     help="copy: a plain 1 GiB device copy, the reference for the HBM traffic counters; "
                          "traffic: write profiles/traffic.json from the counter runs under --pmc-dir (no GPU); "
                          "ceilings: a pure MFMA loop and a streaming read, measured; "
                          "crossover: one small-q row through the decode and the prefill calls, q = 1..16; "
-                         "sequences: the varlen prefill and its sequences launched alone")
+                         "sequences: the varlen prefill and its sequences launched alone; "
+                         "operands: the long-chunk prefill with Q, K or V zeroed; "
+                         "options: the softcap / ALiBi cost on each kernel")
     ap.add_argument("--pmc-dir", default="pmc",
                     help="--mode traffic: directory holding pmc_<COUNTER>/ and pmccopy_<COUNTER>/ runs")
     a = ap.parse_args()
@@ -668,6 +710,8 @@ def main():
         return operands()
     if a.mode == "sequences":
         return sequences()
+    if a.mode == "options":
+        return options()
     ops.lib()
 
     log(f"building workload {a.workload} ...")
