@@ -108,6 +108,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
   }
 
   const int ntiles = kend > kfirst ? (kend - kfirst + kKT - 1) / kKT : 0;
+  // With score modifiers the tiles run from the highest key down: ALiBi
+  // raises a row's biased maximum with every key, so in ascending order the
+  // running max would grow and the accumulators be rescaled tile after tile.
+  const int kstep = MOD ? -kKT : kKT;
+  const int kstart = MOD && ntiles > 0 ? kfirst + (ntiles - 1) * kKT : kfirst;
 
   // Ping-pong (two waves per SIMD): the late wave group runs each tile's PV
   // one iteration after its softmax, so one group's softmax overlaps the
@@ -120,12 +125,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
   constexpr bool PP = (WAVES == 8);
   constexpr int IW = PP ? WAVES / 2 : WAVES;  // waves that load the tiles
   const bool late = PP && wave >= WAVES / 2;
-  typedef TileLoader<DPAD, IW> TLI;
+  typedef TileLoader<DPAD, IW, 2, false, MOD> TLI;
   constexpr int ILPW = TLI::LPW;  // DMA instructions per loading wave per tile
   TLI tl;
   // (initialised in every wave, so that it stays in registers; the late
   // waves never use it)
-  tl.init(p, seq, kvh, late ? wave - IW : wave, lane, kfirst, kend, (uint32_t)(uintptr_t)(&smem[0]));
+  tl.init(p, seq, kvh, late ? wave - IW : wave, lane, kstart, kend, (uint32_t)(uintptr_t)(&smem[0]));
 
   // ---- per-lane LDS read offsets (loop invariant).  The swizzled chunk index
   // is an XOR of a lane constant with the loop index on bits that do not
@@ -165,11 +170,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
       // max once and each exponent's FMA)
       const float c = MOD ? 1.0f : score_scale;
       if constexpr (MOD) {
+        if (p.softcap_k2 == 0.0f) {
+          // ALiBi alone: the scaled score and its bias -slope (lim - 1 - key)
+          // in two FMAs
+          const float b0 = -slope[rb] * (float)(L - qlen + tok[rb] - j0 - 4 * hi);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[rb][r] *= score_scale;
-        mod_scores16(p, s[rb], slope[rb], L - qlen + tok[rb] - j0 - 4 * hi);
+          for (int r = 0; r < 16; ++r)
+            s[rb][r] = __builtin_fmaf(s[rb][r], score_scale,
+                                      __builtin_fmaf(slope[rb], (float)(8 * (r >> 2) + (r & 3)), b0));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[rb][r] *= score_scale;
+          mod_scores16(p, s[rb], slope[rb], L - qlen + tok[rb] - j0 - 4 * hi);
+        }
       }
-      if (MOD || __any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
+      // the modified scores are finite, so the mask stays an identity on the
+      // tiles that no row's bounds cut
+      if (__any(j0 + kKT > lim[rb] || j0 < lo[rb])) {  // causal diagonal / key-range end / window start
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -261,15 +278,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_mfma_dma_kernel(
       }
       ++issued;
     }
-    const int j0 = kfirst + it * kKT;
+    const int j0 = kstart + it * kstep;
     const bool live = wave_active && j0 < wave_kend;
-    if (late && it > 0 && wave_active && j0 - kKT < wave_kend) pv((it - 1) % NST);
+    if (late && it > 0 && wave_active && j0 - kstep < wave_kend) pv((it - 1) % NST);
     if (live) qk_softmax(it % NST, j0);
     if (!late && live) pv(it % NST);
     // page ids of the next tile to load, read during the next barrier's wait
     if (!late && issued < ntiles) tl.fetch(issued);
   }
-  if (late && ntiles > 0 && wave_active && kfirst + (ntiles - 1) * kKT < wave_kend) pv((ntiles - 1) % NST);
+  if (late && ntiles > 0 && wave_active && kstart + (ntiles - 1) * kstep < wave_kend) pv((ntiles - 1) % NST);
 
   // ---- epilogue
 #pragma unroll
