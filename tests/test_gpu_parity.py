@@ -741,6 +741,9 @@ MOD_CASES = [
     ("f16", "e5m2", 128, 8, 2, 16, 4.0, True, 64, False),
     ("f16", "e4m3", 256, 8, 2, 64, 1.5, True, -1, True),
     ("f16", "e5m2", 256, 8, 2, 64, 10.0, False, 129, False),
+    # softcap alone at D <= 128 (the reciprocal form of the cap), with a window and sinks
+    ("bf16", "bf16", 128, 8, 2, 32, 1.0, False, -1, False),
+    ("f16", "f16", 128, 8, 4, 16, 0.5, False, 100, True),
 ]
 
 
